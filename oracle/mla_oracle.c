@@ -1,0 +1,443 @@
+/*
+ * CPU oracle for MLA latent-cache decode -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the package smoke check and the benchmark's CPU
+ * baseline may load or call this file's library. The GPU library never
+ * does, and shares no code with it.
+ *
+ * Everything is plain, slow, fp64 arithmetic taken from the definitions:
+ *
+ *  - MLA caches one latent vector c_KV per token instead of per-head keys and
+ *    values, and recovers them with up-projections k = W_UK c, v = W_UV c
+ *    ("MLA: Multi-Head Latent Attention -- DeepSeek-AI Explained", section
+ *    Method, the three architecture equations).
+ *  - The up-projections can be folded into the query and output projections,
+ *    so attention runs directly against the latent ("Weight Absorbing
+ *    Trick", nnets.ru article on MLA and FlashAttention, section on the
+ *    essence of MLA; snowgate.dev forum thread 35, last reply: W_UK absorbed
+ *    into the query).
+ *  - Each cached row is the 512-wide latent plus a 64-wide decoupled RoPE key
+ *    shared by all heads, which is kept as a separate slice so the absorption
+ *    still holds (snowgate.dev thread 35, replies on the 512 + 64 row).
+ *  - The kernel is a FlashAttention-style exact attention (FlashMLA page of
+ *    the ik_llama.cpp docs, "What is MLA?"), so the reference is plain
+ *    softmax attention computed directly in two passes.
+ *  - The q8_0 cache type (FlashMLA page, "KV cache with MLA"): blocks of 32
+ *    int8 values sharing one fp16 scale; a value is scale * int.
+ *
+ * Readings where the pages are silent (the paged layout, the causal rule for
+ * several new tokens, empty rows, the split plan) follow the API contract of
+ * the GPU library and are spelled out at each function.
+ *
+ * Parity pins: every function here is pinned by CPU tests against closed
+ * forms, invariants and brute force (absorbed == decompressed on random
+ * W_UK / W_UV; uniform and one-hot softmax cases; exact rows; LSE combine of
+ * a token partition == the unsplit result; IEEE binary16 / bfloat16 decoding
+ * of chosen bit patterns; partition invariants of the plan).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define D_LATENT 512
+#define D_ROPE 64
+#define D_K (D_LATENT + D_ROPE)
+#define BLOCK_TOKENS 64
+#define Q8_GROUP 32
+#define Q8_GROUPS (D_K / Q8_GROUP)
+#define D_HEAD_NOPE 128 /* per-head no-RoPE key width of the decompressed form */
+#define D_HEAD_V 128    /* per-head value width of the decompressed form */
+
+/* ------------------------------------------------------------ decoding */
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. Exact in double. */
+double oracle_bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double oracle_fp16_value(uint16_t bits) {
+  const int s = bits >> 15;
+  const int e = (bits >> 10) & 0x1F;
+  const int m = bits & 0x3FF;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+  return s ? -v : v;
+}
+
+/* q8_0 dequantization of one value: scale * int, exact in double. */
+double oracle_q8_value(int8_t qv, uint16_t scale_bits) {
+  return oracle_fp16_value(scale_bits) * (double)qv;
+}
+
+/* ------------------------------------------------------------ paged cache */
+
+typedef struct {
+  int kind; /* 0: bf16 bits, 1: q8_0 */
+  const void* kv;
+  const uint16_t* scales;
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int32_t max_blocks;
+} cache_view;
+
+/* Token t of a sequence lives in row t % 64 of physical block
+ * block_table[b][t / 64]. Writes its 576 values (exactly) to dst. */
+static void cache_row(const cache_view* c, int32_t b, int64_t t, double* dst) {
+  const int64_t phys = c->block_table[(int64_t)b * c->max_blocks + t / BLOCK_TOKENS];
+  const int64_t row = phys * BLOCK_TOKENS + t % BLOCK_TOKENS;
+  if (c->kind == 0) {
+    const uint16_t* r = (const uint16_t*)c->kv + row * D_K;
+    for (int d = 0; d < D_K; ++d) dst[d] = oracle_bf16_value(r[d]);
+  } else {
+    const int8_t* r = (const int8_t*)c->kv + row * D_K;
+    const uint16_t* s = c->scales + row * Q8_GROUPS;
+    for (int d = 0; d < D_K; ++d) dst[d] = oracle_q8_value(r[d], s[d / Q8_GROUP]);
+  }
+}
+
+/* Tokens of sequence b after clamping its length to the table's capacity;
+ * negative lengths count as empty. */
+static int64_t seq_tokens(const int32_t* seqlens, int32_t b, int32_t max_blocks) {
+  int64_t L = seqlens[b];
+  if (L < 0) L = 0;
+  if (L > (int64_t)max_blocks * BLOCK_TOKENS) L = (int64_t)max_blocks * BLOCK_TOKENS;
+  return L;
+}
+
+/* A sequence is valid when every block it uses has an id in [0, num_blocks).
+ * Invalid sequences produce NaN output and NaN lse for all their rows. */
+static int seq_valid(const cache_view* c, int32_t b, int64_t L) {
+  const int64_t nb = (L + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+  for (int64_t j = 0; j < nb; ++j) {
+    const int32_t id = c->block_table[(int64_t)b * c->max_blocks + j];
+    if (id < 0 || (int64_t)id >= c->num_blocks) return 0;
+  }
+  return 1;
+}
+
+/* Visible tokens of query i among s_q new tokens: the cache length L already
+ * includes the new tokens, and query i sees positions 0 .. L - s_q + i. */
+static int64_t visible_tokens(int64_t L, int32_t s_q, int32_t i) {
+  const int64_t n = L - s_q + 1 + i;
+  return n > 0 ? n : 0;
+}
+
+/* ------------------------------------------------- absorbed latent attention */
+
+/*
+ * One query row against the latent cache, two passes:
+ *   s_t   = scale * sum_{d<576} q[d] * r_t[d]       (t < n)
+ *   m     = max_t s_t,   l = sum_t exp(s_t - m),   lse = m + ln l
+ *   out_e = sum_t exp(s_t - m) * r_t[e] / l        (e < 512: V is the latent)
+ * n == 0 gives out = 0 and lse = -inf.
+ */
+static void absorbed_row(const cache_view* c, int32_t b, int64_t n, const double* q,
+                         double scale, double* out, double* lse, double* s, double* row) {
+  for (int e = 0; e < D_LATENT; ++e) out[e] = 0.0;
+  if (n == 0) {
+    *lse = -INFINITY;
+    return;
+  }
+  double m = -INFINITY;
+  for (int64_t t = 0; t < n; ++t) {
+    cache_row(c, b, t, row);
+    double acc = 0.0;
+    for (int d = 0; d < D_K; ++d) acc += q[d] * row[d];
+    s[t] = scale * acc;
+    if (s[t] > m) m = s[t];
+  }
+  double l = 0.0;
+  for (int64_t t = 0; t < n; ++t) {
+    const double p = exp(s[t] - m);
+    l += p;
+    cache_row(c, b, t, row);
+    for (int e = 0; e < D_LATENT; ++e) out[e] += p * row[e];
+  }
+  for (int e = 0; e < D_LATENT; ++e) out[e] /= l;
+  *lse = m + log(l);
+}
+
+static int decode_absorbed_core(int32_t B, int32_t s_q, int32_t H, const uint16_t* q_bf16,
+                                const double* q_f64, const cache_view* c,
+                                const int32_t* seqlens, double scale, const int64_t* rows,
+                                int64_t n_rows, double* out, double* lse) {
+  const int64_t total = (int64_t)B * s_q * H;
+  if (!rows) n_rows = total;
+  int err = 0;
+#pragma omp parallel
+  {
+    double* row = (double*)malloc(sizeof(double) * D_K);
+    double* qrow = (double*)malloc(sizeof(double) * D_K);
+    double* s = NULL;
+    int64_t s_cap = 0;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t k = 0; k < n_rows; ++k) {
+      const int64_t r = rows ? rows[k] : k;
+      double* o = out + k * D_LATENT;
+      if (r < 0 || r >= total) {
+#pragma omp atomic write
+        err = 1;
+        continue;
+      }
+      const int32_t i = (int32_t)((r / H) % s_q);
+      const int32_t b = (int32_t)(r / ((int64_t)H * s_q));
+      const int64_t L = seq_tokens(seqlens, b, c->max_blocks);
+      if (!seq_valid(c, b, L)) {
+        for (int e = 0; e < D_LATENT; ++e) o[e] = NAN;
+        lse[k] = NAN;
+        continue;
+      }
+      const int64_t n = visible_tokens(L, s_q, i);
+      if (n > s_cap) {
+        free(s);
+        s = (double*)malloc(sizeof(double) * (size_t)n);
+        s_cap = n;
+      }
+      for (int d = 0; d < D_K; ++d)
+        qrow[d] = q_bf16 ? oracle_bf16_value(q_bf16[r * D_K + d]) : q_f64[r * D_K + d];
+      absorbed_row(c, b, n, qrow, scale, o, &lse[k], s, row);
+    }
+    free(row);
+    free(qrow);
+    free(s);
+  }
+  return err ? -1 : 0;
+}
+
+/*
+ * Absorbed-form decode, the contract of the GPU kernel.
+ *   q          bf16 bits [B, s_q, H, 576], row r = (b * s_q + i) * H + h
+ *   kv         bf16 bits or int8 [num_blocks, 64, 576] (kv_kind 0 / 1)
+ *   kv_scales  fp16 bits [num_blocks, 64, 18] for q8_0, else NULL
+ *   block_table int32 [B, max_blocks]; seqlens int32 [B] (new tokens included)
+ *   rows       optional list of row ids to compute (NULL = all, in order)
+ *   out        double [n_rows, 512];  lse double [n_rows] (natural log)
+ * Returns 0, or -1 if a row id is out of range.
+ */
+int oracle_decode_absorbed(int32_t B, int32_t s_q, int32_t H, const uint16_t* q,
+                           int32_t kv_kind, const void* kv, const uint16_t* kv_scales,
+                           int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* seqlens, double softmax_scale, const int64_t* rows,
+                           int64_t n_rows, double* out, double* lse) {
+  cache_view c = {kv_kind, kv, kv_scales, num_blocks, block_table, max_blocks};
+  return decode_absorbed_core(B, s_q, H, q, NULL, &c, seqlens, softmax_scale, rows, n_rows,
+                              out, lse);
+}
+
+/* Same, with an fp64 query [B, s_q, H, 576] (used for the absorption check). */
+int oracle_decode_absorbed_f64q(int32_t B, int32_t s_q, int32_t H, const double* q,
+                                int32_t kv_kind, const void* kv, const uint16_t* kv_scales,
+                                int64_t num_blocks, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* seqlens,
+                                double softmax_scale, double* out, double* lse) {
+  cache_view c = {kv_kind, kv, kv_scales, num_blocks, block_table, max_blocks};
+  return decode_absorbed_core(B, s_q, H, NULL, q, &c, seqlens, softmax_scale, NULL, 0, out,
+                              lse);
+}
+
+/* ------------------------------------------ decompressed (non-absorbed) form */
+
+/*
+ * The definition without absorption: per head h and visible token t,
+ *   k_{t,h} = [ W_UK[h] c_t ; k_rope_t ]   (128 + 64 wide)
+ *   v_{t,h} =   W_UV[h] c_t                (128 wide)
+ * with c_t = r_t[0:512], k_rope_t = r_t[512:576], then standard softmax
+ * attention of q_h = [q_nope_h ; q_rope_h] and the per-head output
+ * o_h = sum_t p_t v_{t,h}.
+ *   q_nope [B, s_q, H, 128], q_rope [B, s_q, H, 64] (fp64)
+ *   w_uk, w_uv [H, 128, 512] (fp64, row j of W is the j-th output dim)
+ *   out [B, s_q, H, 128], lse [B, s_q, H]
+ */
+int oracle_decode_decompressed(int32_t B, int32_t s_q, int32_t H, const double* q_nope,
+                               const double* q_rope, const double* w_uk, const double* w_uv,
+                               const uint16_t* kv, int64_t num_blocks,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* seqlens, double softmax_scale, double* out,
+                               double* lse) {
+  cache_view c = {0, kv, NULL, num_blocks, block_table, max_blocks};
+  const int64_t total = (int64_t)B * s_q * H;
+#pragma omp parallel
+  {
+    double* row = (double*)malloc(sizeof(double) * D_K);
+    double* v = (double*)malloc(sizeof(double) * D_HEAD_V);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < total; ++r) {
+      const int32_t h = (int32_t)(r % H);
+      const int32_t i = (int32_t)((r / H) % s_q);
+      const int32_t b = (int32_t)(r / ((int64_t)H * s_q));
+      const double* qn = q_nope + r * D_HEAD_NOPE;
+      const double* qr = q_rope + r * D_ROPE;
+      const double* wk = w_uk + (int64_t)h * D_HEAD_NOPE * D_LATENT;
+      const double* wv = w_uv + (int64_t)h * D_HEAD_V * D_LATENT;
+      double* o = out + r * D_HEAD_V;
+      const int64_t L = seq_tokens(seqlens, b, max_blocks);
+      for (int j = 0; j < D_HEAD_V; ++j) o[j] = 0.0;
+      if (!seq_valid(&c, b, L)) {
+        for (int j = 0; j < D_HEAD_V; ++j) o[j] = NAN;
+        lse[r] = NAN;
+        continue;
+      }
+      const int64_t n = visible_tokens(L, s_q, i);
+      if (n == 0) {
+        lse[r] = -INFINITY;
+        continue;
+      }
+      double* s = (double*)malloc(sizeof(double) * (size_t)n);
+      double m = -INFINITY;
+      for (int64_t t = 0; t < n; ++t) {
+        cache_row(&c, b, t, row);
+        double acc = 0.0;
+        for (int j = 0; j < D_HEAD_NOPE; ++j) {
+          double k = 0.0;
+          for (int d = 0; d < D_LATENT; ++d) k += wk[j * D_LATENT + d] * row[d];
+          acc += qn[j] * k;
+        }
+        for (int d = 0; d < D_ROPE; ++d) acc += qr[d] * row[D_LATENT + d];
+        s[t] = softmax_scale * acc;
+        if (s[t] > m) m = s[t];
+      }
+      double l = 0.0;
+      for (int64_t t = 0; t < n; ++t) {
+        const double p = exp(s[t] - m);
+        l += p;
+        cache_row(&c, b, t, row);
+        for (int j = 0; j < D_HEAD_V; ++j) {
+          double vj = 0.0;
+          for (int d = 0; d < D_LATENT; ++d) vj += wv[j * D_LATENT + d] * row[d];
+          v[j] = vj;
+        }
+        for (int j = 0; j < D_HEAD_V; ++j) o[j] += p * v[j];
+      }
+      for (int j = 0; j < D_HEAD_V; ++j) o[j] /= l;
+      lse[r] = m + log(l);
+      free(s);
+    }
+    free(row);
+    free(v);
+  }
+  return 0;
+}
+
+/* Absorbed query: q~_h = [ W_UK[h]^T q_nope_h ; q_rope_h ]  -> [rows, 576],
+ * since q_nope . (W_UK c) = (W_UK^T q_nope) . c. */
+void oracle_absorb_query(int64_t rows, int32_t H, const double* q_nope, const double* q_rope,
+                         const double* w_uk, double* q_abs) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const int32_t h = (int32_t)(r % H);
+    const double* wk = w_uk + (int64_t)h * D_HEAD_NOPE * D_LATENT;
+    double* qa = q_abs + r * D_K;
+    for (int d = 0; d < D_LATENT; ++d) {
+      double acc = 0.0;
+      for (int j = 0; j < D_HEAD_NOPE; ++j) acc += wk[j * D_LATENT + d] * q_nope[r * D_HEAD_NOPE + j];
+      qa[d] = acc;
+    }
+    for (int d = 0; d < D_ROPE; ++d) qa[D_LATENT + d] = q_rope[r * D_ROPE + d];
+  }
+}
+
+/* Per-head output from the latent-space output: o_h = W_UV[h] o_lat_h. */
+void oracle_project_output(int64_t rows, int32_t H, const double* o_lat, const double* w_uv,
+                           double* o) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const int32_t h = (int32_t)(r % H);
+    const double* wv = w_uv + (int64_t)h * D_HEAD_V * D_LATENT;
+    for (int j = 0; j < D_HEAD_V; ++j) {
+      double acc = 0.0;
+      for (int d = 0; d < D_LATENT; ++d) acc += wv[j * D_LATENT + d] * o_lat[r * D_LATENT + d];
+      o[r * D_HEAD_V + j] = acc;
+    }
+  }
+}
+
+/* --------------------------------------------------------- LSE combine */
+
+/*
+ * Merge S partial results of the same rows computed over disjoint token
+ * sets:  lse = ln sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * O_s.
+ * A part with lse_s = -inf saw no token and has weight 0; if every part is
+ * empty the row is out = 0, lse = -inf. NaN inputs propagate.
+ *   part_out float [S, R, 512], part_lse float [S, R]
+ *   out double [R, 512], lse double [R]
+ */
+void oracle_combine(int32_t S, int64_t R, const float* part_out, const float* part_lse,
+                    double* out, double* lse) {
+  for (int64_t r = 0; r < R; ++r) {
+    double m = -INFINITY;
+    int any_nan = 0;
+    for (int32_t s = 0; s < S; ++s) {
+      const double v = part_lse[(int64_t)s * R + r];
+      if (isnan(v)) any_nan = 1;
+      if (v > m) m = v;
+    }
+    double* o = out + r * D_LATENT;
+    if (any_nan) {
+      for (int e = 0; e < D_LATENT; ++e) o[e] = NAN;
+      lse[r] = NAN;
+      continue;
+    }
+    for (int e = 0; e < D_LATENT; ++e) o[e] = 0.0;
+    if (m == -INFINITY) {
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double total = 0.0;
+    for (int32_t s = 0; s < S; ++s) total += exp((double)part_lse[(int64_t)s * R + r] - m);
+    const double L = m + log(total);
+    for (int32_t s = 0; s < S; ++s) {
+      const double w = exp((double)part_lse[(int64_t)s * R + r] - L);
+      if (w == 0.0) continue;
+      const float* po = part_out + ((int64_t)s * R + r) * D_LATENT;
+      for (int e = 0; e < D_LATENT; ++e) o[e] += w * (double)po[e];
+    }
+    lse[r] = L;
+  }
+}
+
+/* ---------------------------------------------------------- split plan */
+
+/*
+ * The work partition the GPU library uses (its own rule, stated here from
+ * the library's header): let nb_b = ceil(L_b / 64) with L_b clamped as in
+ * seq_tokens, pre_b = sum_{b'<b} nb_b', T = pre_B. The T blocks, laid end
+ * to end in sequence order, are cut into P parts; part p covers
+ * [floor(p T / P), floor((p+1) T / P)). The part holding block x is
+ * ceil((x+1) P / T) - 1. A non-empty sequence spans parts first..last
+ * (the parts holding its first and its last block); an empty sequence is
+ * owned by the part holding block pre_b, or by part P-1 when pre_b == T.
+ *   seq_prefix [B+1], part_start [P+1], seq_first_part [B], seq_last_part [B]
+ */
+int oracle_plan(int32_t B, const int32_t* seqlens, int32_t max_blocks, int32_t P,
+                int32_t* seq_prefix, int32_t* part_start, int32_t* seq_first_part,
+                int32_t* seq_last_part) {
+  if (P < 1 || B < 0) return -1;
+  int64_t acc = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    seq_prefix[b] = (int32_t)acc;
+    acc += (seq_tokens(seqlens, b, max_blocks) + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+  }
+  seq_prefix[B] = (int32_t)acc;
+  const int64_t T = acc;
+  for (int32_t p = 0; p <= P; ++p) part_start[p] = (int32_t)((int64_t)p * T / P);
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t lo = seq_prefix[b], hi = seq_prefix[b + 1];
+    if (hi > lo) {
+      seq_first_part[b] = (int32_t)(((lo + 1) * P + T - 1) / T - 1);
+      seq_last_part[b] = (int32_t)((hi * P + T - 1) / T - 1);
+    } else {
+      const int32_t owner = lo < T ? (int32_t)(((lo + 1) * P + T - 1) / T - 1) : P - 1;
+      seq_first_part[b] = owner;
+      seq_last_part[b] = owner;
+    }
+  }
+  return 0;
+}
