@@ -1,0 +1,168 @@
+/*
+ * libmla -- Multi-Head Latent Attention decode over a paged latent cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. MLA caches one compressed latent vector c_KV per token
+ * (512 values here) and recovers keys and values through up-projections
+ * k = W_UK c, v = W_UV c ("MLA: Multi-Head Latent Attention -- DeepSeek-AI
+ * Explained", section Method, architecture equations). Folding W_UK into the
+ * query and W_UV into the output projection (the weight-absorbing trick:
+ * nnets.ru article on MLA and FlashAttention, section on the essence of MLA;
+ * snowgate.dev forum thread 35, last reply) lets every head attend directly
+ * to the cached rows, and the RoPE part of the key travels as a separate
+ * 64-wide slice shared by all heads (thread 35, replies on the 512 + 64 row).
+ * So each cached token row is [c_KV (512) | k_rope (64)] = 576 values, each
+ * query row is the absorbed query [W_UK^T q_nope ; q_rope] (576 values), and
+ * for every query row
+ *
+ *     s_t  = softmax_scale * <q, row_t>           over the 576 columns
+ *     out  = sum_t softmax(s)_t * row_t[0:512]    (the latent is V)
+ *     lse  = ln sum_t exp(s_t)
+ *
+ * over the tokens the row may see. The result stays in the 512-wide latent
+ * space; applying W_UV and W_O is the caller's business. No per-head K or V
+ * is ever built. This is exact softmax attention evaluated FlashAttention-
+ * style (FlashMLA page of the ik_llama.cpp docs, "What is MLA?"); the
+ * optional q8_0 cache follows "KV cache with MLA" on the same page.
+ *
+ * Layouts (all row-major and contiguous):
+ *   q            bf16  [B, s_q, H, 576]        query row r = i*H + h of sequence b
+ *   kv_cache     bf16  [num_blocks, 64, 576]   (MLA_KV_BF16)
+ *                int8  [num_blocks, 64, 576]   (MLA_KV_Q8_0) with
+ *   kv_scales    fp16  [num_blocks, 64, 18]    scale g covers columns 32g .. 32g+31;
+ *                                              a cached value is scale * int8
+ *   block_table  int32 [B, max_blocks_per_seq] token t of sequence b is row t % 64
+ *                                              of block block_table[b][t / 64]
+ *   seqlens      int32 [B]                     cached tokens of sequence b,
+ *                                              including its s_q new tokens
+ *   out          bf16  [B, s_q, H, 512]
+ *   lse          fp32  [B, s_q, H]             natural log
+ *
+ * Visibility: query i (0 <= i < s_q) of sequence b sees tokens
+ * 0 .. seqlens[b] - s_q + i (causal among the new tokens). A row that sees no
+ * token gets out = 0 and lse = -inf. seqlens are clamped to
+ * [0, 64 * max_blocks_per_seq]. If any block id a sequence uses lies outside
+ * [0, num_blocks), every out and lse value of that sequence is NaN and no
+ * out-of-range block is read.
+ *
+ * Pointers: every array argument is a device pointer unless marked host. The
+ * caller owns all memory; the library keeps no pointer after a call returns
+ * and allocates nothing. Calls only enqueue work on `stream` (no host
+ * synchronisation); inputs must stay alive until the stream has passed them.
+ * Errors found on the host are returned before anything is enqueued, and
+ * nothing is written then. Results are deterministic for fixed inputs and a
+ * fixed problem descriptor (no floating-point atomics).
+ *
+ * Alignment: q, kv_cache, out and the workspace must be 16-byte aligned;
+ * kv_scales 4-byte (its rows are 36 bytes); lse, block_table, seqlens 4-byte.
+ */
+#ifndef LIBMLA_MLA_H
+#define LIBMLA_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_D_LATENT 512
+#define MLA_D_ROPE 64
+#define MLA_D_K 576
+#define MLA_BLOCK_TOKENS 64
+#define MLA_Q8_GROUP 32
+#define MLA_MAX_BATCH 2048   /* sequences per call */
+#define MLA_MAX_ROWS 4096    /* s_q * H */
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,        /* null pointer, bad size, misaligned pointer */
+  MLA_ERR_UNSUPPORTED = 2,        /* outside the supported limits */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MLA_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+} mla_status;
+
+typedef enum { MLA_KV_BF16 = 0, MLA_KV_Q8_0 = 1 } mla_kv_dtype;
+
+/* Problem descriptor (host struct, read during a call only). */
+typedef struct {
+  int32_t batch;              /* B, 0 .. MLA_MAX_BATCH */
+  int32_t seqlen_q;           /* s_q >= 1: new query tokens per sequence */
+  int32_t num_heads;          /* H >= 1, s_q * H <= MLA_MAX_ROWS */
+  int32_t max_blocks_per_seq; /* block_table row stride, >= 1 */
+  int64_t num_blocks;         /* blocks in the cache pool, >= 0 */
+  int32_t max_seqlen;         /* host-known bound on seqlens used to size the work
+                                 split; 0 means 64 * max_blocks_per_seq. Results do
+                                 not depend on it. */
+  int32_t kv_dtype;           /* mla_kv_dtype */
+  int32_t num_parts;          /* 0: automatic; else P >= 1 KV partitions (see mla_plan) */
+  int32_t m_tile;             /* 0: automatic; else 32 or 64 query rows per
+                                 workgroup */
+} mla_problem;
+
+/* Bytes of device workspace mla_decode needs for *p (written to *bytes, host).
+ * The size depends only on the descriptor and the device's compute-unit count. */
+mla_status mla_workspace_size(const mla_problem* p, size_t* bytes);
+
+/* Number of KV partitions P that mla_decode uses for *p (written to *num_parts, host). */
+mla_status mla_num_parts(const mla_problem* p, int32_t* num_parts);
+
+/*
+ * Decode one step: out and lse for every query row of every sequence, as
+ * defined at the top of this file. Uses split-KV partitions when that fills
+ * the GPU better, with a log-sum-exp merge of the partial results (the same
+ * merge as mla_combine). workspace: device buffer of at least
+ * mla_workspace_size bytes (may be NULL when that size is 0); its contents on
+ * entry do not matter and are overwritten.
+ */
+mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
+                      const void* kv_scales, const int32_t* block_table,
+                      const int32_t* seqlens, float softmax_scale, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Log-sum-exp merge of num_splits partial results of the same rows, each
+ * computed over a disjoint set of tokens:
+ *     lse[r] = ln sum_s exp(partial_lse[s][r])
+ *     out[r] = sum_s exp(partial_lse[s][r] - lse[r]) * partial_out[s][r]
+ * A part with lse = -inf saw no token and has weight 0; rows whose parts are
+ * all empty get out = 0, lse = -inf; NaN in any part gives NaN.
+ *   partial_out fp32 [num_splits, rows, 512], partial_lse fp32 [num_splits, rows]
+ *   out bf16 [rows, 512], lse fp32 [rows]
+ * num_splits >= 1, rows >= 0. This is the merge that makes split-KV decoding
+ * exact (split the tokens, attend to each part, merge), which is how one
+ * long sequence can be spread over many compute units or devices.
+ */
+mla_status mla_combine(int32_t num_splits, int64_t rows, const float* partial_out,
+                       const float* partial_lse, void* out, float* lse, hipStream_t stream);
+
+/*
+ * The work partition mla_decode uses, computed on the device from seqlens.
+ * With nb_b = ceil(L_b / 64) (L_b clamped as above), pre_b = sum_{b'<b} nb_b'
+ * and T = pre_B, the T cache blocks laid end to end in sequence order are cut
+ * into P = mla_num_parts(p) parts; part p covers blocks
+ * [floor(p*T/P), floor((p+1)*T/P)), and block x lies in part
+ * ceil((x+1)*P/T) - 1. A non-empty sequence spans the parts holding its first
+ * and its last block; an empty one is owned by the part holding block pre_b
+ * (part P-1 if pre_b == T). Each part is processed by one workgroup per
+ * query-row tile.
+ * Writes int32 to plan_out (device, capacity plan_capacity int32 values,
+ * at least 3*B + P + 2): seq_prefix [B+1], part_start [P+1],
+ * seq_first_part [B], seq_last_part [B], concatenated in that order.
+ */
+mla_status mla_plan(const mla_problem* p, const int32_t* seqlens, int32_t* plan_out,
+                    int64_t plan_capacity, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* mla_status_str(mla_status s);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMLA_MLA_H */

@@ -1,0 +1,1131 @@
+// libmla: MLA decode in weight-absorbed form over a paged latent cache, for
+// gfx950 (MI355X). The operation and the C ABI are defined in include/mla.h.
+//
+// Design in brief (CDNA4):
+//  * One workgroup = 4 waves on one CU, processing one KV partition of the
+//    cache for a tile of 32*HG query rows. Waves split the rows in groups of
+//    32 (HG groups) and, when HG < 4, split each group's work CG = 4/HG ways:
+//    the 576-wide score contraction by columns (partial scores summed through
+//    LDS) and the 512-wide value product by output columns.
+//  * The cache streams through LDS in 32-token tiles (half a 64-token block,
+//    36 KiB), fetched with global_load_lds_dwordx4 (direct to LDS, no VGPRs)
+//    into a 3-stage ring, so two tiles are in flight while one is consumed.
+//  * Scores are computed transposed, S^T = K q~^T, on v_mfma_f32_32x32x16_bf16
+//    with tokens on the M side and heads on the N side. The accumulator then
+//    holds, per lane, 16 tokens of one head: row max / row sum need only one
+//    cross-lane step, and the probabilities P^T are already laid out as the
+//    B operand of the value product O^T += V^T P^T, so P never leaves
+//    registers. V^T operands come from the same LDS tile through
+//    ds_read_b64_tr_b16 (transposing reads), since V is the latent itself.
+//  * Online softmax in the log2 domain (exp2 on v_exp_f32), fp32 accumulators.
+//  * Split-KV: the blocks of all sequences, laid end to end, are cut into P
+//    equal parts (the plan, recomputed from seqlens inside every kernel, so
+//    the host never synchronises). A sequence that spans parts leaves fp32
+//    partials (normalised O and lse) and a second kernel merges them with a
+//    log-sum-exp combine.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdarg.h>
+#include <stdlib.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "mla.h"
+
+namespace {
+
+constexpr int kDL = MLA_D_LATENT;           // 512: latent width = V width
+constexpr int kDK = MLA_D_K;                // 576: K row width
+constexpr int kBT = MLA_BLOCK_TOKENS;       // 64 tokens per cache block
+constexpr int kTile = 32;                   // tokens per LDS tile
+constexpr int kRowBytes = kDK * 2;          // 1152 bytes per bf16 row
+constexpr int kTileBytes = kTile * kRowBytes;   // 36864
+constexpr int kThreads = 256;
+constexpr int kStages = 3;
+constexpr int kMaxBatch = MLA_MAX_BATCH;
+// q8_0 tiles: 32 rows x 576 int8 plus 32 rows x 18 fp16 scales
+constexpr int kQ8RowBytes = kDK;            // 576
+constexpr int kQ8ScaleRowBytes = 36;
+constexpr int kQ8TileBytes = kTile * kQ8RowBytes;               // 18432
+constexpr int kQ8ScaleTileBytes = kTile * kQ8ScaleRowBytes;     // 1152
+constexpr int kQ8StageBytes = kQ8TileBytes + 2048;              // int8 + scales, padded
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+#define LDS_AS __attribute__((address_space(3)))
+// Read-only for the whole kernel: loads through this address space with a
+// uniform address become scalar loads (s_load, counted by lgkmcnt) instead of
+// vector loads, so they never wait behind the LDS-DMA loads in flight.
+#define CONST_AS __attribute__((address_space(4)))
+
+struct DecodeParams {
+  const uint16_t* q;
+  const uint8_t* kv;
+  const uint8_t* kv_scales;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  uint16_t* out;
+  float* lse;
+  int32_t* ws_prefix;   // [B+1] block prefix, written by workgroup 0
+  float* part_lse;      // [2P, M]
+  float* part_o;        // [2P, M, 512]
+  int64_t num_blocks;
+  int B, s_q, H, M, max_blocks, P, m_tiles;
+  float scale_log2;     // softmax_scale * log2(e)
+};
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ int clamp_len(int L, int max_blocks) {
+  return L < 0 ? 0 : (L > max_blocks * kBT ? max_blocks * kBT : L);
+}
+
+__device__ __forceinline__ int nblocks_of(int L, int max_blocks) {
+  return (clamp_len(L, max_blocks) + kBT - 1) / kBT;
+}
+
+// Part holding flattened block x (T > 0): ceil((x+1) P / T) - 1.
+__device__ __forceinline__ int part_of(int x, int P, int T) {
+  return (int)((((int64_t)x + 1) * P + T - 1) / T - 1);
+}
+
+__device__ __forceinline__ int part_start(int p, int P, int T) {
+  return (int)((int64_t)p * T / P);
+}
+
+// Wait until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS traffic only. __syncthreads() would also wait for
+// every outstanding global load (vmcnt(0)), including the LDS-DMA prefetch of
+// later tiles; callers wait for exactly the loads they need first.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_addr + 16 * l (global_load_lds_dwordx4, M0 = LDS base). Issued as
+// inline asm so that the compiler's wait-count pass, which cannot tell which
+// ring stage a DMA targets, does not serialise every later LDS read behind
+// it; ordering comes from the explicit vmcnt waits and LDS barriers. There is
+// no VGPR destination; the address VGPRs are read at issue.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const LDS_AS uint8_t* p) {
+  return *reinterpret_cast<const LDS_AS bf16x8*>(p);
+}
+
+// V^T operand of the value product for one lane: two transposing 64-bit
+// reads (tokens +0..3 and +8..11 of the fragment). In each 16-lane group,
+// lane 4s+q points at columns 4q..4q+3 of token s, and lane i receives
+// column i of tokens s = 0..3 (ds_read_b64_tr_b16).
+__device__ __forceinline__ bf16x8 vt_fragment(const LDS_AS uint8_t* p0, const LDS_AS uint8_t* p1) {
+  i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0));
+  i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p1));
+  typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// LDS tile layout (bf16, 32 tokens x 576 columns = 36 KiB): chunk-major in
+// 16-byte units (8 columns of one token). Unit 32c + (t ^ 4(c & 3)) holds
+// columns 8c..8c+7 of token t. Reading one chunk row for 32 tokens (the
+// score operand) covers 512 contiguous bytes; the XOR spreads the four
+// chunks a 32-lane half touches in a transposing read (the value operand)
+// over the four 64-byte quarters of the bank window.
+__device__ __forceinline__ int tile_unit(int t, int c) { return 32 * c + (t ^ (4 * (c & 3))); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Block-wide exclusive prefix of cache blocks per sequence: s_pre[0..B].
+// Every thread of the workgroup (NT threads) must call it.
+template <int NT>
+__device__ void plan_prefix(const int32_t* __restrict__ seqlens, int B, int max_blocks,
+                            int* s_pre, int* s_wsum) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int per = (B + NT - 1) / NT;
+  const int lo = min(B, t * per), hi = min(B, lo + per);
+  int local = 0;
+  for (int b = lo; b < hi; ++b) local += nblocks_of(seqlens[b], max_blocks);
+  int x = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_wsum[w] = x;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += s_wsum[i];
+  int run = base + x - local;
+  for (int b = lo; b < hi; ++b) {
+    s_pre[b] = run;
+    run += nblocks_of(seqlens[b], max_blocks);
+  }
+  if (t == NT - 1) s_pre[B] = base + x;
+  __syncthreads();
+}
+
+// ------------------------------------------------------------ decode kernel
+
+// Rescale threshold of the online softmax (log2 units). The reference
+// maximum used for the exponentials only moves when a tile's scores exceed
+// it by more than this, so probabilities stay below 2^8 and the output
+// accumulators are rescaled rarely (in practice on a segment's first tile).
+// The result is the same softmax; only the reference point changes.
+constexpr float kRescaleThreshold = 8.0f;
+
+// LDS-DMA with an SGPR base and a per-lane 32-bit offset (no per-tile
+// address arithmetic); lane l's 16 bytes land at lds_addr + 16 l.
+__device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+template <int HG, int CG, bool Q8>
+__global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParams a) {
+  constexpr int NW = HG * CG;             // waves per workgroup
+  constexpr int NT = 64 * NW;             // threads
+  constexpr int MT = 32 * HG;             // query rows per workgroup
+  constexpr int KS = 36 / CG;             // score k-steps (16 columns) per wave
+  constexpr int NCT = 16 / CG;            // 32-column output tiles per wave
+  constexpr int SL = 16 / CG;             // score registers of this wave's slice
+  constexpr int REC = SL / 2 + 2 <= 4 ? 4 : 8;   // dwords per lane in a slice record
+  constexpr int TILE_LOADS = Q8 ? 20 : 36;  // 1 KiB LDS-DMA loads per tile
+  constexpr int STAGE_BYTES = Q8 ? kQ8StageBytes : kTileBytes;
+  constexpr int MAX_LOADS = (TILE_LOADS + NW - 1) / NW;
+  static_assert(36 % CG == 0 && 16 % CG == 0 && SL % 4 == 0, "bad split");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kStages][STAGE_BYTES];
+  // q8_0: dequantised value tile (columns 0..511, bf16, tile_unit layout)
+  __shared__ __attribute__((aligned(1024))) uint8_t s_deq[Q8 ? kTile * kDL * 2 : 16];
+  // partial scores per wave: bf16 path [4][64] x f32x4 in accumulator order;
+  // q8_0 path as a padded 32 x 33 [head][token] matrix for the transpose
+  __shared__ __attribute__((aligned(16))) float s_sx[(CG > 1 || Q8) ? NW : 1][Q8 ? 32 * 33 : 16 * 64];
+  // per wave and lane: bf16 probabilities of the slice, slice max, slice sum
+  __shared__ __attribute__((aligned(16))) uint32_t s_px[CG > 1 ? NW : 1][64][REC];
+  __shared__ int s_pre[kMaxBatch + 1];
+  __shared__ int s_misc[16];
+  __shared__ int s_raise[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const int hg = wave / CG, cg = wave % CG;
+  const int hi = lane >> 5, l32 = lane & 31;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
+  // that consecutive work items (the row tiles of one part, then neighbouring
+  // parts) land on the same XCD and share its L2.
+  int v = blockIdx.x;
+  const int G = gridDim.x;
+  if ((G & 7) == 0) v = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int part = v / a.m_tiles, mt = v % a.m_tiles;
+
+  plan_prefix<NT>(a.seqlens, a.B, a.max_blocks, s_pre, s_misc);
+  const int T = uniform(s_pre[a.B]);
+  const int P = a.P;
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= a.B; b += NT) a.ws_prefix[b] = s_pre[b];
+  const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
+
+  // Sequences of this part form a contiguous range [b_first, b_last].
+  if (tid == 0) {
+    s_misc[8] = 0x7fffffff;
+    s_misc[9] = -1;
+    s_raise[0] = s_raise[1] = 0;
+  }
+  __syncthreads();
+  for (int b = tid; b < a.B; b += NT) {
+    const int lo = s_pre[b], hi2 = s_pre[b + 1];
+    bool mine;
+    if (hi2 > lo) {
+      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
+    } else {
+      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
+      mine = owner == part;
+    }
+    if (mine) {
+      atomicMin(&s_misc[8], b);
+      atomicMax(&s_misc[9], b);
+    }
+  }
+  __syncthreads();
+  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+
+  const int r = mt * MT + hg * 32 + l32;     // this lane's query row in its sequence
+  const bool row_ok = r < a.M;
+  const int q_i = row_ok ? r / a.H : 0;      // which of the s_q new tokens
+  const int cbase = cg * (kDL / CG);         // first output column of this wave
+
+  // Per-lane constant parts of the LDS operand addresses (tile_unit layout).
+  // Score operand, k-step s: chunk 2s + hi of token l32 at 1024 s + kofs[s & 1].
+  const int kofs0 = 16 * tile_unit(l32, hi);
+  const int kofs1 = 16 * tile_unit(l32, 2 + hi) - 1024;
+  const int kofsA = ((cg * KS) & 1) ? kofs1 : kofs0;   // even ks
+  const int kofsB = ((cg * KS) & 1) ? kofs0 : kofs1;   // odd ks
+  // Value operand, column tile ct, token half kk, read r: lane (g16, i16)
+  // points at token 16 kk + 8 r + 4 h + (i16 >> 2), columns
+  // cbase + 32 ct + 16 (g16 & 1) + 4 (i16 & 3) .. +3, i.e. chunk
+  // cbase/8 + 4 ct + 2 (g16 & 1) + ((i16 & 3) >> 1); the chunk's (c & 3) does
+  // not depend on ct, so the address is vofs[r] + 2048 ct + 256 kk.
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
+  const int vc = cbase / 8 + 2 * (g16 & 1) + (vq >> 1);
+  const int vofs0 = 16 * tile_unit(4 * vh + vs, vc) + 8 * (vq & 1);
+  const int vofs1 = 16 * tile_unit(8 + 4 * vh + vs, vc) + 8 * (vq & 1);
+
+  // Per-lane source offsets of this wave's LDS-DMA loads within a tile.
+  // bf16: load k fills units 64k .. 64k+63 = chunks 2k (lanes 0..31) and
+  // 2k+1 (lanes 32..63); lane position l32 of chunk c holds token
+  // l32 ^ 4(c & 3). q8_0: loads 0..17 fill the int8 rows chunk-major in
+  // 16-column units (unit 32c' + t), loads 18..19 the 1152 bytes of scales.
+  uint32_t doff[MAX_LOADS];
+#pragma unroll
+  for (int j = 0; j < MAX_LOADS; ++j) {
+    const int k = wave + NW * j;
+    const int c = 2 * k + hi;
+    if constexpr (!Q8) {
+      doff[j] = (uint32_t)((l32 ^ (4 * (c & 3))) * kRowBytes + c * 16);
+    } else {
+      const int off = (k - 18) * 1024 + lane * 16;
+      doff[j] = k < 18 ? (uint32_t)(l32 * kQ8RowBytes + c * 16)
+                       : (uint32_t)(off < kQ8ScaleTileBytes ? off : 0);
+    }
+  }
+
+  for (int b = b_first; b <= b_last; ++b) {
+    const int pre_b = uniform(s_pre[b]), pre_e = uniform(s_pre[b + 1]);
+    const int L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
+    const int seg_lo = max(p_lo, pre_b) - pre_b, seg_hi = min(p_hi, pre_e) - pre_b;
+    bool split = false;
+    int slot = 0;
+    if (pre_e > pre_b) {
+      const int fp = part_of(pre_b, P, T), lp = part_of(pre_e - 1, P, T);
+      split = lp > fp;
+      slot = 2 * part + ((part == fp && pre_b > p_lo) ? 1 : 0);
+    }
+    const int t_begin = 2 * seg_lo;
+    const int t_end = min(2 * seg_hi, (L + kTile - 1) / kTile);
+    const int n_tiles = max(0, t_end - t_begin);
+    const CONST_AS int32_t* bt =
+        (const CONST_AS int32_t*)a.block_table + (int64_t)b * a.max_blocks;
+
+    // every block id this segment reads must be in range
+    int bad_local = 0;
+    for (int j = seg_lo + tid; j < seg_hi; j += NT) {
+      const int id = bt[j];
+      if (id < 0 || (int64_t)id >= a.num_blocks) bad_local = 1;
+    }
+    const bool bad = __syncthreads_or(bad_local) != 0;
+    const int n_run = bad ? 0 : n_tiles;
+
+    // absorbed query rows: operand of the score MFMA (k-steps cg*KS ..)
+    bf16x8 qf[KS];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)b * a.M + (row_ok ? r : 0)) * kDK;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int s = cg * KS + ks;
+        bf16x8 z = {};
+        qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hi) : z;
+      }
+    }
+    // visible tokens of this row; padding rows see everything (never stored)
+    const int n_vis = row_ok ? L - a.s_q + 1 + q_i : 0x7fffffff;
+
+    f32x16 o[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[ct][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    auto issue = [&](int idx) {
+      const uint32_t dst = lds_addr_of(s_stage[idx % kStages]);
+      const int tt = t_begin + idx;
+      const int64_t phys = bt[tt >> 1];
+      if constexpr (!Q8) {
+        const uint8_t* src = a.kv + (phys * kBT + (tt & 1) * kTile) * kRowBytes;
+#pragma unroll
+        for (int j = 0; j < MAX_LOADS; ++j) {
+          const int k = wave + NW * j;
+          if (k < TILE_LOADS) dma16_sbase(src, doff[j], dst + k * 1024);
+        }
+      } else {
+        const uint8_t* src = a.kv + (phys * kBT + (tt & 1) * kTile) * kQ8RowBytes;
+        const uint8_t* ssrc =
+            a.kv_scales + (phys * kBT + (tt & 1) * kTile) * kQ8ScaleRowBytes;
+#pragma unroll
+        for (int j = 0; j < MAX_LOADS; ++j) {
+          const int k = wave + NW * j;
+          if (k < 18)
+            dma16_sbase(src, doff[j], dst + k * 1024);
+          else if (k < TILE_LOADS)
+            dma16_sbase(ssrc, doff[j], dst + kQ8TileBytes + (k - 18) * 1024);
+        }
+      }
+    };
+
+    // wait for this wave's loads of the tile about to be consumed; at most
+    // one later tile (ahead) may still be in flight
+    auto wait_tile = [&](bool one_ahead) {
+      if (!one_ahead) {
+        wait_vmcnt<0>();
+      } else if constexpr (TILE_LOADS % NW == 0) {
+        wait_vmcnt<TILE_LOADS / NW>();
+      } else {
+        if (wave < TILE_LOADS % NW)
+          wait_vmcnt<TILE_LOADS / NW + 1>();
+        else
+          wait_vmcnt<TILE_LOADS / NW>();
+      }
+    };
+
+    // The last tile of a sequence may hold rows past its end: clear them so
+    // that whatever the unused cache slots contain cannot reach the result
+    // (a zero probability times a NaN would still be NaN).
+    auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
+      if constexpr (!Q8) {
+        for (int u = tid; u < kTile * 72; u += NT) {
+          const int c = u >> 5, pos = u & 31;
+          if ((pos ^ (4 * (c & 3))) >= valid)
+            *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      } else {
+        for (int u = tid; u < kTile * 36; u += NT) {
+          if ((u & 31) >= valid)
+            *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int t = valid + tid; t < kTile; t += NT) {
+          LDS_AS uint32_t* srow =
+              reinterpret_cast<LDS_AS uint32_t*>(st + kQ8TileBytes + t * kQ8ScaleRowBytes);
+#pragma unroll
+          for (int e = 0; e < kQ8ScaleRowBytes / 4; ++e) srow[e] = 0u;
+        }
+      }
+    };
+
+    auto compute = [&](int it, const LDS_AS uint8_t* st) {
+      const int t0 = (t_begin + it) * kTile;   // first token of the tile
+      // ---- (A) this wave's slice of the scores S^T (tokens x heads):
+      // registers i in [SL cg, SL cg + SL), token t0 + 8(i>>2) + 4hi + (i&3)
+      float tot[SL];
+      if constexpr (Q8) {
+        // Value tile: bf16(scale * int8) for columns 0..511.
+        LDS_AS uint8_t* dq = (LDS_AS uint8_t*)s_deq;
+        for (int u = tid; u < kTile * (kDL / 8); u += NT) {
+          const int c = u >> 5, t = u & 31;        // 8-column chunk, token
+          const uint64_t raw = *reinterpret_cast<const LDS_AS uint64_t*>(
+              st + (32 * (c >> 1) + t) * 16 + 8 * (c & 1));
+          const uint16_t sbits = *reinterpret_cast<const LDS_AS uint16_t*>(
+              st + kQ8TileBytes + t * kQ8ScaleRowBytes + (c >> 2) * 2);
+          const float sc = (float)__builtin_bit_cast(_Float16, sbits);
+          bf16x8 vals;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vals[e] = (__bf16)(sc * (float)(int8_t)(raw >> (8 * e)));
+          *reinterpret_cast<LDS_AS bf16x8*>(dq + 16 * tile_unit(t, c)) = vals;
+        }
+        // Exact scores: S (heads x tokens, one token per lane) on the int8
+        // values themselves (exact in bf16), each 32-column group's partial
+        // sum times that token's fp16 scale in fp32.
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 snt, accg;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) snt[i] = accg[i] = 0.f;
+        const LDS_AS uint8_t* srow = st + kQ8TileBytes + l32 * kQ8ScaleRowBytes;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int s = cg * KS + ks;              // columns 16s .. 16s+15
+          const uint64_t raw = *reinterpret_cast<const LDS_AS uint64_t*>(
+              st + (32 * s + l32) * 16 + 8 * hi);
+          bf16x8 kf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kf[e] = (__bf16)(float)(int8_t)(raw >> (8 * e));
+          accg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, accg, 0, 0, 0);
+          if ((s & 1) || ks == KS - 1) {           // group s/2 done for this wave
+            const uint16_t sbits =
+                *reinterpret_cast<const LDS_AS uint16_t*>(srow + (s >> 1) * 2);
+            const float d = (float)__builtin_bit_cast(_Float16, sbits);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              snt[i] += d * accg[i];
+              accg[i] = 0.f;
+            }
+          }
+        }
+        // transpose through LDS, summing the CG partials for this slice
+        float* mine = s_sx[wave];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mine[(8 * (i >> 2) + 4 * hi + (i & 3)) * 33 + l32] = snt[i];
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < SL; ++j) {
+          const int i = SL * cg + j;
+          float x = 0.f;
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+            x += s_sx[hg * CG + c][l32 * 33 + 8 * (i >> 2) + 4 * hi + (i & 3)];
+          tot[j] = x;
+        }
+        st = (const LDS_AS uint8_t*)s_deq;
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 sacc, sodd;   // two independent chains (even / odd k-steps)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = sodd[i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int s = cg * KS + ks;
+          const bf16x8 kf = lds_read_b128(st + 1024 * s + ((ks & 1) ? kofsB : kofsA));
+          if (ks & 1)
+            sodd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sodd, 0, 0, 0);
+          else
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] += sodd[i];
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (CG > 1) {
+          // reduce-scatter: every wave stores its partial scores, then sums
+          // (in a fixed order) the partials of its own slice only
+          f32x4* mine = reinterpret_cast<f32x4*>(s_sx[wave]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            mine[q * 64 + lane] = f32x4{sacc[4 * q], sacc[4 * q + 1], sacc[4 * q + 2], sacc[4 * q + 3]};
+          lds_barrier();
+#pragma unroll
+          for (int j = 0; j < SL; ++j) tot[j] = 0.f;
+#pragma unroll
+          for (int c = 0; c < CG; ++c) {
+            const f32x4* other = reinterpret_cast<const f32x4*>(s_sx[hg * CG + c]);
+#pragma unroll
+            for (int qq = 0; qq < SL / 4; ++qq) {
+              const f32x4 x = other[(SL / 4 * cg + qq) * 64 + lane];
+              tot[4 * qq] += x[0]; tot[4 * qq + 1] += x[1];
+              tot[4 * qq + 2] += x[2]; tot[4 * qq + 3] += x[3];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < SL; ++j) tot[j] = sacc[j];
+        }
+      }
+
+      // ---- (B) softmax on the slice, against the shared reference m_run
+      __builtin_amdgcn_sched_barrier(0);
+      const bool interior = __all(t0 + kTile <= n_vis);
+      float vv[SL];
+      float smax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < SL; ++j) {
+        const int i = SL * cg + j;
+        const int tok = t0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        vv[j] = (interior || tok < n_vis) ? tot[j] * a.scale_log2 : -INFINITY;
+        smax = fmaxf(smax, vv[j]);
+      }
+      smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+      float pv[SL];
+      float psum = 0.f;
+      auto exps = [&]() {
+        psum = 0.f;
+        if (m_run != -INFINITY) {
+#pragma unroll
+          for (int j = 0; j < SL; ++j) {
+            pv[j] = __builtin_amdgcn_exp2f(vv[j] - m_run);
+            psum += pv[j];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < SL; ++j) pv[j] = 0.f;
+        }
+        psum += __shfl_xor(psum, 32, 64);
+      };
+      exps();
+      const bool raise_lane =
+          smax > m_run + kRescaleThreshold || (m_run == -INFINITY && smax > -INFINITY);
+      uint32_t pw[8];     // all 16 probabilities of the lane, packed bf16 pairs
+      float tmax, tsum;
+      if constexpr (CG > 1) {
+        // all-gather the slices of the row group through LDS
+        auto publish = [&]() {
+          uint32_t* rec = s_px[wave][lane];
+          uint32_t w[REC];
+#pragma unroll
+          for (int j = 0; j < SL / 2; ++j) w[j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+          w[SL / 2] = __builtin_bit_cast(uint32_t, smax);
+          w[SL / 2 + 1] = __builtin_bit_cast(uint32_t, psum);
+#pragma unroll
+          for (int j = SL / 2 + 2; j < REC; ++j) w[j] = 0u;
+#pragma unroll
+          for (int q = 0; q < REC / 4; ++q)
+            reinterpret_cast<u32x4*>(rec)[q] = u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+        };
+        auto gather = [&]() {
+          tmax = -INFINITY;
+          tsum = 0.f;
+#pragma unroll
+          for (int c = 0; c < CG; ++c) {
+            const u32x4* rec = reinterpret_cast<const u32x4*>(s_px[hg * CG + c][lane]);
+            uint32_t w[REC];
+#pragma unroll
+            for (int q = 0; q < REC / 4; ++q) {
+              const u32x4 x = rec[q];
+              w[4 * q] = x[0]; w[4 * q + 1] = x[1]; w[4 * q + 2] = x[2]; w[4 * q + 3] = x[3];
+            }
+#pragma unroll
+            for (int j = 0; j < SL / 2; ++j) pw[(SL / 2) * c + j] = w[j];
+            tmax = fmaxf(tmax, __builtin_bit_cast(float, w[SL / 2]));
+            tsum += __builtin_bit_cast(float, w[SL / 2 + 1]);
+          }
+        };
+        publish();
+        if (__any(raise_lane) && lane == 0) atomicOr(&s_raise[it & 1], 1);
+        lds_barrier();
+        const bool rare = s_raise[it & 1] != 0;   // same value in every wave
+        if (tid == 0) s_raise[(it + 1) & 1] = 0;
+        gather();
+        if (rare) {
+          // a new reference maximum for the rows that need one; every wave
+          // takes this path together (one more barrier)
+          const bool raise = tmax > m_run + kRescaleThreshold ||
+                             (m_run == -INFINITY && tmax > -INFINITY);
+          if (__any(raise)) {
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.f;
+            if (raise) m_run = tmax;
+            l_run *= alpha;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) o[ct][i] *= alpha;
+          }
+          exps();
+          lds_barrier();       // everyone has read the old records
+          publish();
+          lds_barrier();
+          gather();
+        }
+      } else {
+        tmax = smax;
+        if (__builtin_expect(__any(raise_lane), 0)) {
+          const bool raise = raise_lane;
+          const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.f;
+          if (raise) m_run = tmax;
+          l_run *= alpha;
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[ct][i] *= alpha;
+          exps();
+        }
+        tsum = psum;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pw[j] = pack_bf16x2(pv[2 * j], pv[2 * j + 1]);
+      }
+      l_run += tsum;
+      const bf16x8 pb0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      const bf16x8 pb1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+
+      // ---- (C) value product O^T (columns x heads) += V^T P^T
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const bf16x8 v0 = vt_fragment(st + vofs0 + 2048 * ct, st + vofs1 + 2048 * ct);
+        o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, o[ct], 0, 0, 0);
+        const bf16x8 v1 =
+            vt_fragment(st + vofs0 + 2048 * ct + 256, st + vofs1 + 2048 * ct + 256);
+        o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, o[ct], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // 3-stage ring: tiles it+1 and it+2 load while tile it is consumed.
+    // Everything the compiler itself loaded (the query rows) is drained first,
+    // so its own wait counts stay exact while DMAs are in flight.
+    wait_vmcnt<0>();
+    if (n_run > 0) issue(0);
+    if (n_run > 1) issue(1);
+    for (int it = 0; it < n_run; ++it) {
+      wait_tile(it + 1 < n_run);
+      lds_barrier();
+      if (it + 2 < n_run) issue(it + 2);
+      LDS_AS uint8_t* st = (LDS_AS uint8_t*)s_stage[it % kStages];
+      const int valid = L - (t_begin + it) * kTile;
+      if (valid < kTile) {           // last tile of the sequence
+        clear_tail(st, valid);
+        lds_barrier();
+      }
+      compute(it, st);
+    }
+
+    // ---- epilogue: final rows, or fp32 partials of a split sequence
+    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+    float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+    if (bad) lse_v = __builtin_nanf("");
+    if (row_ok) {
+      const int64_t row = (int64_t)b * a.M + r;
+      if (!split) {
+        uint16_t* orow = a.out + row * kDL;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = cbase + 32 * ct + 8 * g + 4 * hi;
+            uint16_t hbits[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              hbits[e] = bad ? (uint16_t)0x7FC0 : f32_to_bf16_bits(o[ct][4 * g + e] * inv_l);
+            const uint64_t packed = (uint64_t)hbits[0] | ((uint64_t)hbits[1] << 16) |
+                                    ((uint64_t)hbits[2] << 32) | ((uint64_t)hbits[3] << 48);
+            *reinterpret_cast<uint64_t*>(orow + col) = packed;
+          }
+        if (hi == 0 && cg == 0) a.lse[row] = lse_v;
+      } else {
+        float* prow = a.part_o + ((int64_t)slot * a.M + r) * kDL;
+        const float nanv = __builtin_nanf("");
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = cbase + 32 * ct + 8 * g + 4 * hi;
+            float4 f;
+            f.x = bad ? nanv : o[ct][4 * g + 0] * inv_l;
+            f.y = bad ? nanv : o[ct][4 * g + 1] * inv_l;
+            f.z = bad ? nanv : o[ct][4 * g + 2] * inv_l;
+            f.w = bad ? nanv : o[ct][4 * g + 3] * inv_l;
+            *reinterpret_cast<float4*>(prow + col) = f;
+          }
+        if (hi == 0 && cg == 0) a.part_lse[(int64_t)slot * a.M + r] = lse_v;
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();   // the ring is reused by the next sequence
+  }
+}
+
+// ------------------------------------------------------------ combine
+
+// Merge n (lse, O) parts of one row; one wave, 8 columns per lane.
+template <typename PartPtr>
+__device__ __forceinline__ void merge_row(int n, PartPtr part, uint16_t* out_row, float* lse_out) {
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;
+  bool has_nan = false;
+  for (int s = 0; s < n; ++s) {
+    const float l = *part.lse(s);
+    has_nan |= isnan(l);
+    m = fmaxf(m, l);
+  }
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float L;
+  if (has_nan) {
+    L = __builtin_nanf("");
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = __builtin_nanf("");
+  } else if (m == -INFINITY) {
+    L = -INFINITY;
+  } else {
+    float tot = 0.f;
+    for (int s = 0; s < n; ++s) tot += expf(*part.lse(s) - m);
+    L = m + logf(tot);
+    for (int s = 0; s < n; ++s) {
+      const float w = expf(*part.lse(s) - L);
+      if (w == 0.f) continue;
+      const float4* src = reinterpret_cast<const float4*>(part.o(s) + 8 * lane);
+      const float4 x0 = src[0], x1 = src[1];
+      acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
+      acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+    }
+  }
+  uint16_t hb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hb[e] = f32_to_bf16_bits(acc[e]);
+  uint4 pk;
+  pk.x = hb[0] | ((uint32_t)hb[1] << 16);
+  pk.y = hb[2] | ((uint32_t)hb[3] << 16);
+  pk.z = hb[4] | ((uint32_t)hb[5] << 16);
+  pk.w = hb[6] | ((uint32_t)hb[7] << 16);
+  *reinterpret_cast<uint4*>(out_row + 8 * lane) = pk;
+  if (lane == 0) *lse_out = L;
+}
+
+struct SplitParts {   // parts of a split sequence inside the decode workspace
+  const float* part_o;
+  const float* part_lse;
+  int M, r, first, pre_b, P, T;
+  __device__ int slot(int s) const {
+    const int p = first + s;
+    return 2 * p + ((s == 0 && pre_b > part_start(p, P, T)) ? 1 : 0);
+  }
+  __device__ const float* lse(int s) const { return part_lse + (int64_t)slot(s) * M + r; }
+  __device__ const float* o(int s) const { return part_o + ((int64_t)slot(s) * M + r) * kDL; }
+};
+
+__global__ __launch_bounds__(kThreads) void mla_split_combine_kernel(DecodeParams a) {
+  const int b = blockIdx.x;
+  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (r >= a.M) return;
+  const int pre_b = a.ws_prefix[b], pre_e = a.ws_prefix[b + 1], T = a.ws_prefix[a.B];
+  if (pre_e <= pre_b) return;
+  const int fp = part_of(pre_b, a.P, T), lp = part_of(pre_e - 1, a.P, T);
+  if (lp == fp) return;
+  SplitParts parts{a.part_o, a.part_lse, a.M, r, fp, pre_b, a.P, T};
+  const int64_t row = (int64_t)b * a.M + r;
+  merge_row(lp - fp + 1, parts, a.out + row * kDL, a.lse + row);
+}
+
+struct DenseParts {   // caller-provided partials [S, R, 512] / [S, R]
+  const float* part_o;
+  const float* part_lse;
+  int64_t R, r;
+  __device__ const float* lse(int s) const { return part_lse + (int64_t)s * R + r; }
+  __device__ const float* o(int s) const { return part_o + ((int64_t)s * R + r) * kDL; }
+};
+
+__global__ __launch_bounds__(kThreads) void mla_combine_kernel(int S, int64_t R,
+                                                               const float* part_o,
+                                                               const float* part_lse,
+                                                               uint16_t* out, float* lse) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  DenseParts parts{part_o, part_lse, R, r};
+  merge_row(S, parts, out + r * kDL, lse + r);
+}
+
+// ------------------------------------------------------------ plan export
+
+__global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seqlens, int B,
+                                                            int max_blocks, int P,
+                                                            int32_t* plan) {
+  __shared__ int pre[kMaxBatch + 1];
+  __shared__ int wsum[8];
+  plan_prefix<kThreads>(seqlens, B, max_blocks, pre, wsum);
+  const int T = pre[B];
+  int32_t* o_pre = plan;
+  int32_t* o_ps = o_pre + B + 1;
+  int32_t* o_fp = o_ps + P + 1;
+  int32_t* o_lp = o_fp + B;
+  for (int b = threadIdx.x; b <= B; b += kThreads) o_pre[b] = pre[b];
+  for (int p = threadIdx.x; p <= P; p += kThreads) o_ps[p] = part_start(p, P, T);
+  for (int b = threadIdx.x; b < B; b += kThreads) {
+    const int lo = pre[b], hi = pre[b + 1];
+    if (hi > lo) {
+      o_fp[b] = part_of(lo, P, T);
+      o_lp[b] = part_of(hi - 1, P, T);
+    } else {
+      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
+      o_fp[b] = owner;
+      o_lp[b] = owner;
+    }
+  }
+}
+
+// ================================================================== host
+
+thread_local std::string g_last_error;
+
+mla_status fail(mla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mla_status fail(mla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+mla_status ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return -1;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+struct Plan {
+  int HG, CG, MT, m_tiles, P, M;
+  size_t off_prefix, off_lse, off_o, bytes;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+mla_status validate_problem(const mla_problem* p) {
+  if (!p) return fail(MLA_ERR_INVALID_ARG, "problem descriptor is NULL");
+  if (p->batch < 0) return fail(MLA_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", p->batch);
+  if (p->batch > MLA_MAX_BATCH)
+    return fail(MLA_ERR_UNSUPPORTED, "batch %d exceeds %d", p->batch, MLA_MAX_BATCH);
+  if (p->seqlen_q < 1) return fail(MLA_ERR_INVALID_ARG, "seqlen_q must be >= 1");
+  if (p->num_heads < 1) return fail(MLA_ERR_INVALID_ARG, "num_heads must be >= 1");
+  if ((int64_t)p->seqlen_q * p->num_heads > MLA_MAX_ROWS)
+    return fail(MLA_ERR_UNSUPPORTED, "seqlen_q * num_heads exceeds %d", MLA_MAX_ROWS);
+  if (p->max_blocks_per_seq < 1) return fail(MLA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+  if ((int64_t)p->max_blocks_per_seq * MLA_BLOCK_TOKENS > INT32_MAX ||
+      (int64_t)p->batch * p->max_blocks_per_seq > INT32_MAX / 2)
+    return fail(MLA_ERR_UNSUPPORTED, "block table too large");
+  if (p->num_blocks < 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks must be >= 0");
+  if (p->max_seqlen < 0) return fail(MLA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_Q8_0)
+    return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);
+  if (p->num_parts < 0) return fail(MLA_ERR_INVALID_ARG, "num_parts must be >= 0");
+  if (p->m_tile != 0 && p->m_tile != 32 && p->m_tile != 64)
+    return fail(MLA_ERR_INVALID_ARG, "m_tile must be 0, 32 or 64 (got %d)", p->m_tile);
+  return MLA_OK;
+}
+
+// Work split: HG row groups per workgroup from the rows per sequence, and P
+// partitions so that P * m_tiles workgroups about fill the compute units.
+mla_status make_plan(const mla_problem* p, Plan* pl) {
+  mla_status s = validate_problem(p);
+  if (s != MLA_OK) return s;
+  const int M = p->seqlen_q * p->num_heads;
+  pl->M = M;
+  // row tile: 32 rows (one 32-row group) or 64 rows (two groups); each
+  // group's work is split over CG waves. More rows than one tile holds take
+  // several row tiles per KV part; they are placed on the same XCD so the
+  // second read of each cache tile hits L2.
+  pl->HG = p->m_tile ? p->m_tile / 32 : (M <= 32 ? 1 : 2);
+  pl->CG = 4;
+  if (const char* e = getenv("MLA_SPLIT_WAYS")) {   // tuning hook: waves per 32-row group
+    const int cg = atoi(e);
+    if (cg == 2 || cg == 4) pl->CG = cg;
+  }
+  pl->MT = 32 * pl->HG;
+  pl->m_tiles = (M + pl->MT - 1) / pl->MT;
+  int P = p->num_parts;
+  if (P == 0) {
+    const int cus = device_cus();
+    if (cus <= 0) return fail(MLA_ERR_HIP, "cannot query the device's compute-unit count");
+    const int64_t cap_tokens =
+        (int64_t)p->max_blocks_per_seq * MLA_BLOCK_TOKENS;
+    const int64_t ms = p->max_seqlen > 0 ? (p->max_seqlen < cap_tokens ? p->max_seqlen : cap_tokens)
+                                         : cap_tokens;
+    const int64_t t_max = (int64_t)p->batch * ((ms + MLA_BLOCK_TOKENS - 1) / MLA_BLOCK_TOKENS);
+    int64_t want = cus / pl->m_tiles;
+    const int64_t min_blocks_per_part = 4;
+    const int64_t cap = (t_max + min_blocks_per_part - 1) / min_blocks_per_part;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    P = (int)want;
+  }
+  if ((int64_t)P * pl->m_tiles > INT32_MAX / 2) return fail(MLA_ERR_UNSUPPORTED, "too many parts");
+  pl->P = P;
+  size_t off = 0;
+  pl->off_prefix = off;
+  off = align_up(off + 4 * ((size_t)p->batch + 1), 256);
+  pl->off_lse = off;
+  if (P > 1) {
+    off = align_up(off + (size_t)2 * P * M * 4, 256);
+    pl->off_o = off;
+    off += (size_t)2 * P * M * kDL * 4;
+  } else {
+    pl->off_o = off;
+  }
+  pl->bytes = off;
+  return MLA_OK;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+template <int HG, int CG, bool Q8>
+hipError_t launch_decode(const DecodeParams& dp, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_decode_kernel<HG, CG, Q8>), dim3(grid), dim3(64 * HG * CG), 0, stream,
+                     dp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "unknown mla_status";
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+mla_status mla_workspace_size(const mla_problem* p, size_t* bytes) {
+  if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
+  Plan pl;
+  mla_status s = make_plan(p, &pl);
+  if (s != MLA_OK) return s;
+  *bytes = pl.bytes;
+  return ok();
+}
+
+mla_status mla_num_parts(const mla_problem* p, int32_t* num_parts) {
+  if (!num_parts) return fail(MLA_ERR_INVALID_ARG, "num_parts is NULL");
+  Plan pl;
+  mla_status s = make_plan(p, &pl);
+  if (s != MLA_OK) return s;
+  *num_parts = pl.P;
+  return ok();
+}
+
+mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
+                      const void* kv_scales, const int32_t* block_table,
+                      const int32_t* seqlens, float softmax_scale, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // everything checkable on the host, before any HIP call
+  mla_status s = validate_problem(p);
+  if (s != MLA_OK) return s;
+  if (p->batch == 0) return ok();
+  if (!q || !kv_cache || !block_table || !seqlens || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "null array argument");
+  if (p->kv_dtype == MLA_KV_Q8_0 && !kv_scales)
+    return fail(MLA_ERR_INVALID_ARG, "kv_scales is required for MLA_KV_Q8_0");
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
+    return fail(MLA_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seqlens, 4))
+    return fail(MLA_ERR_INVALID_ARG, "lse, block_table and seqlens must be 4-byte aligned");
+  if (p->kv_dtype == MLA_KV_Q8_0 && !aligned(kv_scales, 16))
+    return fail(MLA_ERR_INVALID_ARG, "kv_scales must be 16-byte aligned");
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (workspace && !aligned(workspace, 16))
+    return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  Plan pl;
+  s = make_plan(p, &pl);
+  if (s != MLA_OK) return s;
+  if (workspace_bytes < pl.bytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.bytes,
+                workspace_bytes);
+  if (!workspace) return fail(MLA_ERR_INVALID_ARG, "workspace is NULL");
+
+  DecodeParams dp;
+  dp.q = (const uint16_t*)q;
+  dp.kv = (const uint8_t*)kv_cache;
+  dp.kv_scales = (const uint8_t*)kv_scales;
+  dp.block_table = block_table;
+  dp.seqlens = seqlens;
+  dp.out = (uint16_t*)out;
+  dp.lse = lse;
+  uint8_t* ws = (uint8_t*)workspace;
+  dp.ws_prefix = (int32_t*)(ws + pl.off_prefix);
+  dp.part_lse = (float*)(ws + pl.off_lse);
+  dp.part_o = (float*)(ws + pl.off_o);
+  dp.num_blocks = p->num_blocks;
+  dp.B = p->batch;
+  dp.s_q = p->seqlen_q;
+  dp.H = p->num_heads;
+  dp.M = pl.M;
+  dp.max_blocks = p->max_blocks_per_seq;
+  dp.P = pl.P;
+  dp.m_tiles = pl.m_tiles;
+  dp.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+
+  const int grid = pl.P * pl.m_tiles;
+  hipError_t e;
+  const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
+  switch (pl.HG * 20 + pl.CG * 2 + (q8 ? 1 : 0)) {
+    case 28: e = launch_decode<1, 4, false>(dp, grid, stream); break;
+    case 29: e = launch_decode<1, 4, true>(dp, grid, stream); break;
+    case 24: e = launch_decode<1, 2, false>(dp, grid, stream); break;
+    case 25: e = launch_decode<1, 2, true>(dp, grid, stream); break;
+    case 48: e = launch_decode<2, 4, false>(dp, grid, stream); break;
+    case 49: e = launch_decode<2, 4, true>(dp, grid, stream); break;
+    case 44: e = launch_decode<2, 2, false>(dp, grid, stream); break;
+    case 45: e = launch_decode<2, 2, true>(dp, grid, stream); break;
+    default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
+  }
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  if (pl.P > 1) {
+    hipLaunchKernelGGL(mla_split_combine_kernel, dim3(p->batch, (pl.M + 3) / 4), dim3(kThreads), 0,
+                       stream, dp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+mla_status mla_combine(int32_t num_splits, int64_t rows, const float* partial_out,
+                       const float* partial_lse, void* out, float* lse, hipStream_t stream) {
+  if (num_splits < 1) return fail(MLA_ERR_INVALID_ARG, "num_splits must be >= 1");
+  if (rows < 0) return fail(MLA_ERR_INVALID_ARG, "rows must be >= 0");
+  if (rows == 0) return ok();
+  if (!partial_out || !partial_lse || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "null array argument");
+  if (!aligned(partial_out, 16) || !aligned(out, 16) || !aligned(partial_lse, 4) ||
+      !aligned(lse, 4))
+    return fail(MLA_ERR_INVALID_ARG, "partial_out and out must be 16-byte aligned, lse arrays 4");
+  if (rows > (int64_t)INT32_MAX * 4) return fail(MLA_ERR_UNSUPPORTED, "too many rows");
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(kThreads), 0,
+                     stream, num_splits, rows, partial_out, partial_lse, (uint16_t*)out, lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mla_status mla_plan(const mla_problem* p, const int32_t* seqlens, int32_t* plan_out,
+                    int64_t plan_capacity, hipStream_t stream) {
+  Plan pl;
+  mla_status s = make_plan(p, &pl);
+  if (s != MLA_OK) return s;
+  const int64_t need = 3 * (int64_t)p->batch + pl.P + 2;
+  if (!plan_out || (!seqlens && p->batch > 0))
+    return fail(MLA_ERR_INVALID_ARG, "null array argument");
+  if (plan_capacity < need)
+    return fail(MLA_ERR_INVALID_ARG, "plan_out needs %lld int32 values",
+                (long long)need);
+  if (!aligned(plan_out, 4) || !aligned(seqlens, 4))
+    return fail(MLA_ERR_INVALID_ARG, "plan_out and seqlens must be 4-byte aligned");
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kThreads), 0, stream, seqlens, p->batch,
+                     p->max_blocks_per_seq, pl.P, plan_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

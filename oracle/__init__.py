@@ -50,6 +50,9 @@ def _load():
         lib.oracle_decode_absorbed.argtypes = [i32, i32, i32, vp, i32, vp, vp, i64, vp, i32, vp,
                                                dbl, vp, i64, vp, vp]
         lib.oracle_decode_absorbed.restype = ctypes.c_int
+        lib.oracle_decode_absorbed_abs.argtypes = [i32, i32, i32, vp, i32, vp, vp, i64, vp, i32,
+                                                   vp, dbl, vp, i64, vp, vp, vp]
+        lib.oracle_decode_absorbed_abs.restype = ctypes.c_int
         lib.oracle_decode_absorbed_f64q.argtypes = [i32, i32, i32, vp, i32, vp, vp, i64, vp, i32,
                                                     vp, dbl, vp, vp]
         lib.oracle_decode_absorbed_f64q.restype = ctypes.c_int
@@ -88,12 +91,14 @@ def q8_value(q: int, scale_bits: int) -> float:
     return _load().oracle_q8_value(q, scale_bits)
 
 
-def decode_absorbed(q, kv, block_table, seqlens, softmax_scale, *, kv_scales=None, rows=None):
+def decode_absorbed(q, kv, block_table, seqlens, softmax_scale, *, kv_scales=None, rows=None,
+                    with_abs=False):
     """Absorbed-form decode (fp64). q: uint16 [B, s_q, H, 576] bf16 bits.
 
     kv: uint16 bf16 bits or int8 (with kv_scales uint16 fp16 bits [nb, 64, 18]).
     rows: optional int64 row ids r = (b * s_q + i) * H + h.
     Returns (out float64 [n, 512], lse float64 [n]); all rows -> shaped [B, s_q, H, ...].
+    with_abs: also return out_abs = sum_t p_t |row_t| (same shape as out).
     """
     q = _c(q, np.uint16)
     B, s_q, H, dk = q.shape
@@ -107,14 +112,24 @@ def decode_absorbed(q, kv, block_table, seqlens, softmax_scale, *, kv_scales=Non
     n = B * s_q * H if rr is None else rr.size
     out = np.empty((n, D_LATENT), np.float64)
     lse = np.empty(n, np.float64)
-    rc = _load().oracle_decode_absorbed(B, s_q, H, _p(q), kind, _p(kv), _p(sc), kv.shape[0],
-                                        _p(bt), bt.shape[1], _p(sl), float(softmax_scale),
-                                        _p(rr), n, _p(out), _p(lse))
+    if with_abs:
+        oabs = np.empty((n, D_LATENT), np.float64)
+        rc = _load().oracle_decode_absorbed_abs(B, s_q, H, _p(q), kind, _p(kv), _p(sc),
+                                                kv.shape[0], _p(bt), bt.shape[1], _p(sl),
+                                                float(softmax_scale), _p(rr), n, _p(out),
+                                                _p(lse), _p(oabs))
+    else:
+        rc = _load().oracle_decode_absorbed(B, s_q, H, _p(q), kind, _p(kv), _p(sc), kv.shape[0],
+                                            _p(bt), bt.shape[1], _p(sl), float(softmax_scale),
+                                            _p(rr), n, _p(out), _p(lse))
     if rc != 0:
         raise ValueError("row id out of range")
     if rr is None:
-        return out.reshape(B, s_q, H, D_LATENT), lse.reshape(B, s_q, H)
-    return out, lse
+        res = (out.reshape(B, s_q, H, D_LATENT), lse.reshape(B, s_q, H))
+        if with_abs:
+            res = res + (oabs.reshape(B, s_q, H, D_LATENT),)
+        return res
+    return (out, lse, oabs) if with_abs else (out, lse)
 
 
 def decode_absorbed_f64q(q, kv, block_table, seqlens, softmax_scale):

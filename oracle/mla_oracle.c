@@ -142,8 +142,11 @@ static int64_t visible_tokens(int64_t L, int32_t s_q, int32_t i) {
  * n == 0 gives out = 0 and lse = -inf.
  */
 static void absorbed_row(const cache_view* c, int32_t b, int64_t n, const double* q,
-                         double scale, double* out, double* lse, double* s, double* row) {
+                         double scale, double* out, double* lse, double* s, double* row,
+                         double* out_abs) {
   for (int e = 0; e < D_LATENT; ++e) out[e] = 0.0;
+  if (out_abs)
+    for (int e = 0; e < D_LATENT; ++e) out_abs[e] = 0.0;
   if (n == 0) {
     *lse = -INFINITY;
     return;
@@ -162,15 +165,19 @@ static void absorbed_row(const cache_view* c, int32_t b, int64_t n, const double
     l += p;
     cache_row(c, b, t, row);
     for (int e = 0; e < D_LATENT; ++e) out[e] += p * row[e];
+    if (out_abs)
+      for (int e = 0; e < D_LATENT; ++e) out_abs[e] += p * fabs(row[e]);
   }
   for (int e = 0; e < D_LATENT; ++e) out[e] /= l;
+  if (out_abs)
+    for (int e = 0; e < D_LATENT; ++e) out_abs[e] /= l;
   *lse = m + log(l);
 }
 
 static int decode_absorbed_core(int32_t B, int32_t s_q, int32_t H, const uint16_t* q_bf16,
                                 const double* q_f64, const cache_view* c,
                                 const int32_t* seqlens, double scale, const int64_t* rows,
-                                int64_t n_rows, double* out, double* lse) {
+                                int64_t n_rows, double* out, double* lse, double* out_abs) {
   const int64_t total = (int64_t)B * s_q * H;
   if (!rows) n_rows = total;
   int err = 0;
@@ -192,8 +199,11 @@ static int decode_absorbed_core(int32_t B, int32_t s_q, int32_t H, const uint16_
       const int32_t i = (int32_t)((r / H) % s_q);
       const int32_t b = (int32_t)(r / ((int64_t)H * s_q));
       const int64_t L = seq_tokens(seqlens, b, c->max_blocks);
+      double* oa = out_abs ? out_abs + k * D_LATENT : NULL;
       if (!seq_valid(c, b, L)) {
         for (int e = 0; e < D_LATENT; ++e) o[e] = NAN;
+        if (oa)
+          for (int e = 0; e < D_LATENT; ++e) oa[e] = NAN;
         lse[k] = NAN;
         continue;
       }
@@ -205,7 +215,7 @@ static int decode_absorbed_core(int32_t B, int32_t s_q, int32_t H, const uint16_
       }
       for (int d = 0; d < D_K; ++d)
         qrow[d] = q_bf16 ? oracle_bf16_value(q_bf16[r * D_K + d]) : q_f64[r * D_K + d];
-      absorbed_row(c, b, n, qrow, scale, o, &lse[k], s, row);
+      absorbed_row(c, b, n, qrow, scale, o, &lse[k], s, row, oa);
     }
     free(row);
     free(qrow);
@@ -231,7 +241,23 @@ int oracle_decode_absorbed(int32_t B, int32_t s_q, int32_t H, const uint16_t* q,
                            int64_t n_rows, double* out, double* lse) {
   cache_view c = {kv_kind, kv, kv_scales, num_blocks, block_table, max_blocks};
   return decode_absorbed_core(B, s_q, H, q, NULL, &c, seqlens, softmax_scale, rows, n_rows,
-                              out, lse);
+                              out, lse, NULL);
+}
+
+/* Same, plus out_abs [n_rows, 512] = sum_t p_t |r_t[e]|: the magnitude of the
+ * terms behind each output value. Rounding the probabilities (or the output)
+ * to a format with relative precision u perturbs out[e] by at most about
+ * u * out_abs[e], which is what an error bound for such arithmetic scales
+ * with; out_abs >= |out| always, with equality when all terms share a sign. */
+int oracle_decode_absorbed_abs(int32_t B, int32_t s_q, int32_t H, const uint16_t* q,
+                               int32_t kv_kind, const void* kv, const uint16_t* kv_scales,
+                               int64_t num_blocks, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seqlens, double softmax_scale,
+                               const int64_t* rows, int64_t n_rows, double* out, double* lse,
+                               double* out_abs) {
+  cache_view c = {kv_kind, kv, kv_scales, num_blocks, block_table, max_blocks};
+  return decode_absorbed_core(B, s_q, H, q, NULL, &c, seqlens, softmax_scale, rows, n_rows,
+                              out, lse, out_abs);
 }
 
 /* Same, with an fp64 query [B, s_q, H, 576] (used for the absorption check). */
@@ -242,7 +268,7 @@ int oracle_decode_absorbed_f64q(int32_t B, int32_t s_q, int32_t H, const double*
                                 double softmax_scale, double* out, double* lse) {
   cache_view c = {kv_kind, kv, kv_scales, num_blocks, block_table, max_blocks};
   return decode_absorbed_core(B, s_q, H, NULL, q, &c, seqlens, softmax_scale, NULL, 0, out,
-                              lse);
+                              lse, NULL);
 }
 
 /* ------------------------------------------ decompressed (non-absorbed) form */

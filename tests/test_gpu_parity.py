@@ -1,0 +1,227 @@
+"""GPU parity of libmla against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (ctypes binding). Small cases compare all
+rows; the five decode workloads at full size compare a seeded sample of rows
+in the launch configuration the benchmark uses. Integer / index work (the
+plan, block-table paging) must be bit-exact."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_10_amd as mla
+import oracle
+import workload as wl
+from gpu_helpers import (compare, device_inputs, log, oracle_rows, require_library, run_gpu,
+                         sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    require_library()
+    assert torch.cuda.is_available()
+
+
+SMALL = [
+    # name, B, s_q, H, seqlens, table, kv_dtype, m_tile
+    ("h16_ragged", 3, 1, 16, [1, 100, 1037], "permuted", "bf16", 0),
+    ("h128_ragged", 3, 1, 128, [70, 640, 1500], "permuted", "bf16", 0),
+    ("h128_pair", 2, 2, 128, [33, 900], "sequential", "bf16", 0),
+    ("h40_pad", 2, 1, 40, [500, 77], "permuted", "bf16", 0),
+    ("h16_triple", 2, 3, 16, [5, 300], "permuted", "bf16", 0),
+    ("h128_q8", 2, 1, 128, [700, 129], "permuted", "q8_0", 0),
+    ("h16_q8", 3, 1, 16, [64, 1, 999], "permuted", "q8_0", 0),
+    ("h128_mt32", 2, 1, 128, [300, 1000], "permuted", "bf16", 32),
+    ("h128_mt64", 2, 1, 128, [300, 1000], "permuted", "bf16", 64),
+    ("h64_mt64_q8", 2, 1, 64, [513, 64], "sequential", "q8_0", 64),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("parts", [0, 1, 7])
+def test_small_all_rows(case, parts):
+    name, B, s_q, H, seqlens, table, kvd, mt = case
+    log(f"case {name} parts={parts}")
+    w = wl.make_workload(name, B, s_q, H, seqlens, seed=77, table=table, kv_dtype=kvd)
+    out, lse, _ = run_gpu(w, num_parts=parts, m_tile=mt)
+    compare(out, lse, *oracle_rows(w), what=f"{name}/P={parts}")
+
+
+def test_tiny_config_all_rows():
+    w = wl.config_workload(1)
+    log("config 1 (tiny)")
+    out, lse, _ = run_gpu(w)
+    compare(out, lse, *oracle_rows(w), what="tiny")
+
+
+@pytest.mark.parametrize("cfg,n_rows", [(2, 384), (3, 384), (4, 24), (5, 160)])
+def test_full_size_config_sampled_rows(cfg, n_rows):
+    w = wl.config_workload(cfg)
+    log(f"config {cfg} ({w.name}): generated, rows={w.rows}")
+    out, lse, _ = run_gpu(w)
+    rows = sample_rows(w, n_rows, seed=cfg)
+    compare(out.reshape(-1, 512)[rows], lse.reshape(-1)[rows], *oracle_rows(w, rows),
+            what=w.name)
+
+
+def test_forced_part_counts_agree():
+    w = wl.make_workload("parts", 4, 1, 128, [2000, 1, 4096, 777], seed=5, table="permuted")
+    ref_out, ref_lse, ref_abs = oracle_rows(w)
+    t = device_inputs(w)
+    T = int(((np.maximum(w.seqlens, 0) + 63) // 64).sum())
+    results = []
+    for P in (1, 2, 7, 64, T, T + 13):
+        log(f"parts {P}")
+        out, lse, _ = run_gpu(w, t, num_parts=P)
+        compare(out, lse, ref_out, ref_lse, ref_abs, what=f"P={P}")
+        results.append((out, lse))
+    for out, lse in results[1:]:
+        assert np.abs(out - results[0][0]).max() <= 2e-2
+        assert np.abs(lse - results[0][1]).max() <= 1e-3
+
+
+def test_block_permutation_is_bit_identical():
+    w = wl.make_workload("perm", 3, 1, 128, [900, 64, 2049], seed=6)
+    out1, lse1, bits1 = run_gpu(w, num_parts=5)
+    perm = wl.permutation(w.num_blocks, 7, 1)
+    kv2 = np.empty_like(w.kv)
+    kv2[perm] = w.kv
+    w2 = wl.Workload(**{**w.__dict__, "kv": kv2,
+                        "block_table": np.where(w.block_table >= 0,
+                                                perm[np.maximum(w.block_table, 0)], -1)
+                        .astype(np.int32)})
+    out2, lse2, bits2 = run_gpu(w2, num_parts=5)
+    assert np.array_equal(bits1, bits2)
+    assert np.array_equal(lse1, lse2)
+
+
+def _one_hot(B, H, seqlens, targets, seed, s_q=1, d_probe=11):
+    w = wl.make_workload("probe", B, s_q, H, seqlens, seed=seed, table="permuted")
+    w.kv[:, :, 512:] = 0
+    w.q[:] = 0
+    one = int(wl.f32_to_bf16_bits(np.float32([64.0]))[0])
+    w.q[..., 512 + d_probe] = one
+    for b, t in targets:
+        w.kv[w.block_table[b, t // 64], t % 64, 512 + d_probe] = one
+    w.softmax_scale = 1.0
+    return w
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_one_hot_probe_returns_the_exact_row(H):
+    seqlens = [300, 64, 129, 4096]
+    targets = [(0, 299), (1, 0), (2, 128), (3, 2047)]
+    w = _one_hot(4, H, seqlens, targets, seed=8)
+    for parts in (1, 0, 9):
+        out, lse, bits = run_gpu(w, num_parts=parts)
+        for b, t in targets:
+            row = w.kv[w.block_table[b, t // 64], t % 64, :512]
+            for h in range(H):
+                assert np.array_equal(bits[b, 0, h], row), (b, t, h, parts)
+            assert np.abs(lse[b, 0] - 4096.0).max() <= 1e-3
+
+
+def test_empty_rows_and_causal_visibility():
+    w = wl.make_workload("deg", 4, 2, 16, [0, 1, 2, 130], seed=9, table="permuted")
+    for parts in (1, 3):
+        out, lse, _ = run_gpu(w, num_parts=parts)
+        compare(out, lse, *oracle_rows(w), what=f"degenerate P={parts}")
+        assert np.all(np.isneginf(lse[0])) and np.all(out[0] == 0)
+        assert np.all(np.isneginf(lse[1, 0])) and np.all(np.isfinite(lse[1, 1]))
+
+
+def test_invalid_block_ids_poison_only_their_sequence():
+    w = wl.make_workload("bad", 3, 1, 128, [300, 300, 300], seed=10)
+    w.block_table[1, 2] = w.num_blocks + 5
+    for parts in (1, 4):
+        out, lse, _ = run_gpu(w, num_parts=parts)
+        compare(out, lse, *oracle_rows(w), what=f"invalid ids P={parts}")
+        assert np.all(np.isnan(lse[1])) and np.all(np.isnan(out[1]))
+    w.block_table[1, 2] = -1
+    out, lse, _ = run_gpu(w, num_parts=2)
+    assert np.all(np.isnan(lse[1])) and np.all(np.isfinite(lse[[0, 2]]))
+
+
+def test_combine_entry_point_matches_the_oracle():
+    S, R = 5, 300
+    po = wl.normal_f32(S * R * 512, 3, 1).reshape(S, R, 512)
+    pl = (wl.normal_f32(S * R, 3, 2) * 4).reshape(S, R)
+    pl[1, :50] = -np.inf
+    pl[:, 60] = -np.inf
+    pl[2, 70] = np.nan
+    out, lse = mla.mla_combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda())
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.combine(po, pl)
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, what="combine")
+
+
+@pytest.mark.parametrize("B,P,seed", [(1, 1, 1), (64, 256, 2), (128, 256, 3), (7, 40, 4),
+                                      (300, 17, 5), (2048, 256, 6)])
+def test_plan_entry_point_is_bit_exact(B, P, seed):
+    sl = wl.uniform_int(B, seed, 7, 0, 3000)
+    sl[::5] = 0
+    sl[1::7] = -3
+    max_blocks = 40
+    got = mla.mla_plan(torch.from_numpy(sl).cuda(), batch=B, seqlen_q=1, num_heads=16,
+                       max_blocks_per_seq=max_blocks, num_blocks=1, num_parts=P)
+    torch.cuda.synchronize()
+    ref = oracle.plan(sl, max_blocks, P)
+    for k in ("seq_prefix", "part_start", "seq_first_part", "seq_last_part"):
+        assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
+
+
+def test_q8_block_permutation_is_bit_identical():
+    w = wl.make_workload("q8perm", 3, 1, 128, [1000, 65, 333], seed=12, kv_dtype="q8_0")
+    perm = wl.permutation(w.num_blocks, 9, 1)
+    kv2 = np.empty_like(w.kv)
+    kv2[perm] = w.kv
+    sc2 = np.empty_like(w.kv_scales)
+    sc2[perm] = w.kv_scales
+    bt2 = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    w2 = wl.Workload(**{**w.__dict__, "kv": kv2, "kv_scales": sc2, "block_table": bt2})
+    for parts in (1, 6):
+        _, lse1, bits1 = run_gpu(w, num_parts=parts)
+        _, lse2, bits2 = run_gpu(w2, num_parts=parts)
+        assert np.array_equal(bits1, bits2) and np.array_equal(lse1, lse2)
+
+
+def test_causal_pair_first_query_matches_single_token_decode():
+    w = wl.make_workload("pair", 3, 2, 128, [100, 4000, 65], seed=13)
+    out2, lse2, _ = run_gpu(w)
+    w1 = wl.Workload(**{**w.__dict__, "s_q": 1, "q": np.ascontiguousarray(w.q[:, :1]),
+                        "seqlens": w.seqlens - 1})
+    out1, lse1, _ = run_gpu(w1)
+    assert np.abs(out2[:, 0] - out1[:, 0]).max() <= 2e-2
+    assert np.abs(lse2[:, 0] - lse1[:, 0]).max() <= 1e-3
+
+
+def test_repeat_runs_are_bit_identical():
+    w = wl.config_workload(3, B=32)
+    t = device_inputs(w)
+    _, lse1, bits1 = run_gpu(w, t)
+    _, lse2, bits2 = run_gpu(w, t)
+    assert np.array_equal(bits1, bits2) and np.array_equal(lse1, lse2)
+
+
+def test_absorbed_query_end_to_end():
+    """Feed bf16(q~) built from random W_UK to the GPU; W_UV applied to its
+    latent output must match the decompressed per-head definition."""
+    w = wl.config_workload(1)
+    H, seed = w.H, 1001
+    w_uk = wl.normal_f64(H * 128 * 512, seed, wl.S_WUK, stddev=1 / math.sqrt(512)).reshape(H, 128, 512)
+    w_uv = wl.normal_f64(H * 128 * 512, seed, wl.S_WUV, stddev=1 / math.sqrt(512)).reshape(H, 128, 512)
+    q_nope = wl.normal_f64(H * 128, seed, wl.S_QNOPE).reshape(1, 1, H, 128)
+    q_rope = wl.normal_f64(H * 64, seed, wl.S_QROPE).reshape(1, 1, H, 64)
+    q_abs = oracle.absorb_query(q_nope, q_rope, w_uk)
+    w.q = wl.f32_to_bf16_bits(q_abs.astype(np.float32)).reshape(1, 1, H, 576)
+    out, lse, _ = run_gpu(w)
+    compare(out, lse, *oracle_rows(w), what="absorbed q")
+    o_ref, lse_ref = oracle.decode_decompressed(q_nope, q_rope, w_uk, w_uv, w.kv, w.block_table,
+                                                w.seqlens, w.softmax_scale)
+    o_gpu = oracle.project_output(out, w_uv)
+    # bf16 rounding of q~ and of out bounds the gap
+    assert np.abs(o_gpu - o_ref).max() <= 5e-2 * max(1.0, np.abs(o_ref).max())
+    assert np.abs(lse - lse_ref).max() <= 5e-2

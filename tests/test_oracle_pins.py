@@ -147,6 +147,22 @@ def test_single_token_returns_the_latent_row_exactly():
             assert abs(lse[b, 0, h] - s0) < 1e-12
 
 
+def test_term_magnitude_closed_forms():
+    # one token: out_abs = |row|; zero query: out_abs = mean |row|; always >= |out|
+    w = wl.make_workload("t", 2, 1, 3, [1, 150], seed=35, table="permuted")
+    out, lse, oabs = oracle.decode_absorbed(w.q, w.kv, w.block_table, w.seqlens,
+                                            w.softmax_scale, with_abs=True)
+    assert np.array_equal(oabs[0, 0, 1], np.abs(_seq_rows(w, 0)[0, :512]))
+    assert np.all(oabs >= np.abs(out) - 1e-15)
+    w.q[:] = 0
+    out, lse, oabs = oracle.decode_absorbed(w.q, w.kv, w.block_table, w.seqlens,
+                                            w.softmax_scale, with_abs=True)
+    np.testing.assert_allclose(oabs[1, 0, 2], np.abs(_seq_rows(w, 1)[:, :512]).mean(axis=0),
+                               atol=1e-13)
+    o2, l2 = oracle.decode_absorbed(w.q, w.kv, w.block_table, w.seqlens, w.softmax_scale)
+    assert np.array_equal(o2, out) and np.array_equal(l2, lse)
+
+
 def test_two_tokens_is_a_logistic_mix():
     w = wl.make_workload("t", 1, 1, 5, [2], seed=24)
     out, lse = oracle.decode_absorbed(w.q, w.kv, w.block_table, w.seqlens, w.softmax_scale)
