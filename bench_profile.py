@@ -1,0 +1,104 @@
+"""Turn rocprofv3 output of bench.py runs into the summaries kept under profiles/.
+
+  python bench_profile.py trace  <kernel-trace dir> <out.md> "<command that made it>"
+  python bench_profile.py traffic <fetch dir> <write dir> <copy-fetch dir> <copy-write dir> \
+                          <out.json> "<commands>"
+
+trace: per-kernel calls / average / total duration from a
+  `rocprofv3 --kernel-trace --stats --output-format csv` run.
+traffic: HBM bytes per decode step from two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
+  runs (KiB per dispatch), each scaled by the factor the same counter shows for
+  a plain 1 GiB device copy (`bench.py --copy-calibration`): factor = copied
+  bytes / (counter KiB * 1024). One step = every library kernel launched by one
+  mla_decode call. The JSON carries the source hash bench.py checks, so a
+  stale measurement is never reported for a changed kernel.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import json
+import os
+import sys
+from collections import defaultdict
+
+import bench
+
+LIB_KERNELS = ("mla_decode", "mla_split_combine", "mla_combine")
+COPY_BYTES = 1 << 30
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def _short(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    return name.split("(")[0].replace("void ", "")
+
+
+def trace(kt_dir: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(_find(kt_dir, "kernel_stats.csv"))))
+    lines = [f"# Kernel trace: {os.path.basename(out_md)[:-3]}", "", "Command:", "",
+             "```", command, "```", "",
+             "| kernel | calls | average (us) | total (us) | share |",
+             "|---|---|---|---|---|"]
+    for r in rows:
+        avg_ns = float(r["AverageNs"])
+        tot_ns = float(r["TotalDurationNs"])
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {avg_ns / 1e3:.2f} | "
+                     f"{tot_ns / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _per_kernel(d: str, counter: str):
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        if r["Counter_Name"] == counter:
+            vals[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return vals
+
+
+def _copy_factor(d: str, counter: str) -> float:
+    v = _per_kernel(d, counter)
+    copies = [x for k, xs in v.items() if "copyBuffer" in k for x in xs]
+    if not copies:
+        raise RuntimeError(f"no copy kernel in {d}")
+    kib = sorted(copies)[len(copies) // 2]
+    return COPY_BYTES / (kib * 1024.0)
+
+
+def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, command) -> None:
+    ff = _copy_factor(cfetch_dir, "FETCH_SIZE")
+    wf = _copy_factor(cwrite_dir, "WRITE_SIZE")
+    fetch = _per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _per_kernel(write_dir, "WRITE_SIZE")
+    per = {}
+    for k in sorted(set(fetch) | set(write)):
+        if not any(t in k for t in LIB_KERNELS):
+            continue
+        f = fetch.get(k, [0.0])
+        w = write.get(k, [0.0])
+        per[k] = {"fetch_bytes": sum(f) / len(f) * 1024 * ff,
+                  "write_bytes": sum(w) / len(w) * 1024 * wf, "launches_seen": len(f)}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())
+    rec = {"source_hash": bench.source_hash(), "command": command,
+           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+           "per_kernel": per, "bytes_per_launch": int(total)}
+    if len(sys.argv) > 8:
+        rec.update(json.loads(sys.argv[8]))
+    json.dump(rec, open(out_json, "w"), indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "trace":
+        trace(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "traffic":
+        traffic(*sys.argv[2:8])
+    else:
+        raise SystemExit(__doc__)

@@ -53,8 +53,8 @@
  * nothing is written then. Results are deterministic for fixed inputs and a
  * fixed problem descriptor (no floating-point atomics).
  *
- * Alignment: q, kv_cache, out and the workspace must be 16-byte aligned;
- * kv_scales 4-byte (its rows are 36 bytes); lse, block_table, seqlens 4-byte.
+ * Alignment: q, kv_cache, kv_scales, out and the workspace must be 16-byte
+ * aligned; lse, block_table and seqlens 4-byte.
  */
 #ifndef LIBMLA_MLA_H
 #define LIBMLA_MLA_H
@@ -98,8 +98,8 @@ typedef struct {
                                  not depend on it. */
   int32_t kv_dtype;           /* mla_kv_dtype */
   int32_t num_parts;          /* 0: automatic; else P >= 1 KV partitions (see mla_plan) */
-  int32_t m_tile;             /* 0: automatic; else 32 or 64 query rows per
-                                 workgroup */
+  int32_t m_tile;             /* 0: automatic; else 32, 64 or 128 query rows
+                                 per workgroup (128: bf16 cache only) */
 } mla_problem;
 
 /* Bytes of device workspace mla_decode needs for *p (written to *bytes, host).

@@ -33,6 +33,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 #include <string>
 
 #include "mla.h"
@@ -81,6 +82,9 @@ struct DecodeParams {
   int64_t num_blocks;
   int B, s_q, H, M, max_blocks, P, m_tiles;
   float scale_log2;     // softmax_scale * log2(e)
+  float scale_mag_log2; // |softmax_scale| * log2(e)
+  uint32_t q_sign2;     // 0x80008000 when softmax_scale < 0: the query is negated
+                        // instead, so the scale applied in the kernel is >= 0
 };
 
 // ------------------------------------------------------------------ helpers
@@ -210,8 +214,13 @@ __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, ui
                : "memory", "m0");
 }
 
+// Two floats to a bf16 pair (round to nearest even), lo in bits 0..15: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  const f32x2v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
 template <int HG, int CG, bool Q8>
@@ -733,6 +742,395 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
   }
 }
 
+
+// acc *= alpha in place on the accumulation registers (rare path of the
+// online softmax). Done in asm so that the accumulators of the value product
+// keep a single home in AGPRs; compiler-generated VALU scaling would make the
+// allocator stage every accumulator through VGPRs on each loop iteration.
+// The leading nops cover the MFMA-write -> accvgpr-read latency.
+__device__ __forceinline__ void acc_scale(f32x16& acc, float alpha) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = acc[i];
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(x), "=&v"(t)
+        : "v"(alpha));
+    acc[i] = x;
+  }
+}
+
+// ------------------------------------------------- bf16 decode kernel (rows)
+
+// One workgroup = 4 waves (one per SIMD) on one KV partition for a tile of
+// 32*HG query rows. Every wave owns whole query rows: wave (hg, cg) computes
+// the complete 576-column scores of its 32-row group hg, so no partial score
+// ever crosses waves, and the value product of those rows for output columns
+// [cg*512/CG, (cg+1)*512/CG), CG = 4/HG. With HG = 4 nothing is computed
+// twice; with fewer row groups (short rows per sequence) the CG waves of a
+// group repeat the same score product, which costs MFMA time these
+// bandwidth-bound shapes have to spare.
+//
+// Per 32-token tile the only workgroup synchronisation is one barrier: a
+// 4-stage LDS ring holds the tile whose value product runs, the tile whose
+// scores run, and two tiles in flight. The score product of tile i+1 is
+// issued before the softmax of tile i, so the exponentials overlap MFMA work
+// of the same wave.
+template <int HG>
+__global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a) {
+  constexpr int NW = 4;
+  constexpr int NT = 64 * NW;
+  constexpr int CG = NW / HG;             // waves per row group
+  constexpr int MT = 32 * HG;             // query rows per workgroup
+  constexpr int NCT = 16 / CG;            // 32-column output blocks per wave
+  constexpr int NST = 4;                  // ring stages
+  constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
+  constexpr int KPF = HG == 4 ? 2 : 3;    // score operands in flight
+  constexpr int VPF = HG == 4 ? 2 : 3;    // value operands in flight
+  static_assert(HG == 1 || HG == 2 || HG == 4, "row groups");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NST][kTileBytes];
+  __shared__ int s_pre[kMaxBatch + 1];
+  __shared__ int s_misc[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const int hg = wave / CG, cg = wave % CG;
+  const int hi = lane >> 5, l32 = lane & 31;
+
+  int v = blockIdx.x;
+  const int G = gridDim.x;
+  if ((G & 7) == 0) v = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int part = v / a.m_tiles, mt = v % a.m_tiles;
+
+  plan_prefix<NT>(a.seqlens, a.B, a.max_blocks, s_pre, s_misc);
+  const int T = uniform(s_pre[a.B]);
+  const int P = a.P;
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= a.B; b += NT) a.ws_prefix[b] = s_pre[b];
+  const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
+
+  if (tid == 0) {
+    s_misc[8] = 0x7fffffff;
+    s_misc[9] = -1;
+  }
+  __syncthreads();
+  for (int b = tid; b < a.B; b += NT) {
+    const int lo = s_pre[b], hi2 = s_pre[b + 1];
+    bool mine;
+    if (hi2 > lo) {
+      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
+    } else {
+      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
+      mine = owner == part;
+    }
+    if (mine) {
+      atomicMin(&s_misc[8], b);
+      atomicMax(&s_misc[9], b);
+    }
+  }
+  __syncthreads();
+  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+
+  const int r = mt * MT + hg * 32 + l32;     // this lane's query row in its sequence
+  const bool row_ok = r < a.M;
+  const int q_i = row_ok ? r / a.H : 0;
+  const int cbase = cg * (kDL / CG);         // first output column of this wave
+
+  // Score operand of k-step s: chunk 2s + hi of token l32, at
+  // 1024 s + kofs[s & 1] (tile_unit layout).
+  const int kofs0 = 16 * tile_unit(l32, hi);
+  const int kofs1 = 16 * tile_unit(l32, 2 + hi) - 1024;
+  // Value operand: lane (g16, i16) of column block ct, token half kk points
+  // at token 16 kk + 4 (g16 >> 1) + (i16 >> 2) (+8 for the second read),
+  // columns cbase + 32 ct + 16 (g16 & 1) + 4 (i16 & 3) .. +3.
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
+  const int vc = cbase / 8 + 2 * (g16 & 1) + (vq >> 1);
+  const int vofs0 = 16 * tile_unit(4 * vh + vs, vc) + 8 * (vq & 1);
+  const int vofs1 = 16 * tile_unit(8 + 4 * vh + vs, vc) + 8 * (vq & 1);
+  // LDS-DMA: load j of this wave fills units 64k .. 64k+63, k = wave + 4j,
+  // i.e. chunk c = 2k + hi for token position l32, which holds token
+  // l32 ^ 4(c & 3). (c & 3) does not depend on j, so the source offset is
+  // doff + 128 j and the destination 1024 k.
+  const int dchunk = 2 * wave + hi;
+  const uint32_t doff = (uint32_t)((l32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
+
+  for (int b = b_first; b <= b_last; ++b) {
+    const int pre_b = uniform(s_pre[b]), pre_e = uniform(s_pre[b + 1]);
+    const int L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
+    const int seg_lo = max(p_lo, pre_b) - pre_b, seg_hi = min(p_hi, pre_e) - pre_b;
+    bool split = false;
+    int slot = 0;
+    if (pre_e > pre_b) {
+      const int fp = part_of(pre_b, P, T), lp = part_of(pre_e - 1, P, T);
+      split = lp > fp;
+      slot = 2 * part + ((part == fp && pre_b > p_lo) ? 1 : 0);
+    }
+    const int t_begin = 2 * seg_lo;
+    const int t_end = min(2 * seg_hi, (L + kTile - 1) / kTile);
+    const int n_tiles = max(0, t_end - t_begin);
+    const CONST_AS int32_t* bt =
+        (const CONST_AS int32_t*)a.block_table + (int64_t)b * a.max_blocks;
+
+    int bad_local = 0;
+    for (int j = seg_lo + tid; j < seg_hi; j += NT) {
+      const int id = bt[j];
+      if (id < 0 || (int64_t)id >= a.num_blocks) bad_local = 1;
+    }
+    const bool bad = __syncthreads_or(bad_local) != 0;
+    const int n_run = bad ? 0 : n_tiles;
+
+    bf16x8 qf[36];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)b * a.M + (row_ok ? r : 0)) * kDK;
+      const uint32_t sg = a.q_sign2;
+#pragma unroll
+      for (int s = 0; s < 36; ++s) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if (row_ok) z = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hi) ^ sg;
+        qf[s] = __builtin_bit_cast(bf16x8, z);
+      }
+    }
+    const int n_vis = row_ok ? L - a.s_q + 1 + q_i : 0x7fffffff;
+
+    f32x16 o[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[ct][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // Block id of a tile, read one issue ahead (a scalar load whose latency
+    // then hides behind a whole iteration); indices past the segment reuse
+    // its last tile.
+    auto block_of = [&](int idx) {
+      return bt[(t_begin + min(idx, n_run - 1)) >> 1];
+    };
+    int next_phys = 0;
+    auto issue = [&](int idx) {
+      const uint32_t dst = lds_addr_of(s_stage[idx % NST]) + 1024 * wave;
+      const int tt = t_begin + idx;
+      const int64_t phys = next_phys;
+      next_phys = block_of(idx + 1);
+      const uint8_t* src = a.kv + (phys * kBT + (tt & 1) * kTile) * kRowBytes;
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) dma16_sbase(src + 128 * j, doff, dst + 4096 * j);
+    };
+
+    // Rows past the end of the sequence in its last tile are cleared, so that
+    // whatever unused cache slots hold cannot reach the result.
+    auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
+      for (int u = tid; u < kTile * 72; u += NT) {
+        const int c = u >> 5, pos = u & 31;
+        if ((pos ^ (4 * (c & 3))) >= valid)
+          *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+
+    // S^T (tokens x rows) of one tile: register i is token 8(i>>2) + 4hi + (i&3)
+    auto scores = [&](const LDS_AS uint8_t* st) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 36; ++s) {
+        const bf16x8 kf = lds_read_b128(st + 1024 * s + ((s & 1) ? kofs1 : kofs0));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
+      }
+      return acc;
+    };
+
+    auto prepare = [&](int idx) {   // tile idx has landed in every wave's share
+      const int valid = L - (t_begin + idx) * kTile;
+      if (valid < kTile) {
+        clear_tail((LDS_AS uint8_t*)s_stage[idx % NST], valid);
+        lds_barrier();
+      }
+    };
+
+    f32x16 s_cur;
+    wait_vmcnt<0>();
+    if (n_run > 0) next_phys = block_of(0);
+    if (n_run > 0) issue(0);
+    if (n_run > 1) issue(1);
+    if (n_run > 2) issue(2);
+    if (n_run > 0) {
+      if (n_run > 2) wait_vmcnt<2 * LPW>();
+      else if (n_run > 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      prepare(0);
+      s_cur = scores((const LDS_AS uint8_t*)s_stage[0]);
+    }
+    for (int it = 0; it < n_run; ++it) {
+      if (it + 1 < n_run) {
+        if (it + 2 < n_run) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (it + 3 < n_run) issue(it + 3);
+        prepare(it + 1);
+      }
+      // One straight-line block, software-pipelined by hand: the score product
+      // of tile it+1 (on the last tile a dummy pass over a resident stage,
+      // result unused), with three LDS operand reads in flight, and between
+      // its MFMAs the softmax of tile it, assuming its reference maximum holds.
+      // Interior tiles (every token visible to every row) skip the mask.
+      const LDS_AS uint8_t* sn = (const LDS_AS uint8_t*)s_stage[(it + 1) % NST];
+      const int t0 = (t_begin + it) * kTile;
+      const float c = a.scale_mag_log2;
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      float x[16];
+      float lmax, psum;
+      uint32_t pw[8];
+      f32x16 s_next;
+      auto kread = [&](int s) {
+        return lds_read_b128(sn + 1024 * s + ((s & 1) ? kofs1 : kofs0));
+      };
+      // x[i]: the raw score (interior tiles) or the scaled, masked score;
+      // kept so that the rare path can redo the probabilities
+      auto fused = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        // visible tokens of this lane's row within the tile, minus the lane's
+        // token offset 4 hi (masked tiles only)
+        const int lim = n_vis - t0 - 4 * hi;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_next[i] = 0.f;
+        float mx[4];
+        float p_prev = 0.f;
+        psum = 0.f;
+        bf16x8 kb[KPF];
+#pragma unroll
+        for (int j = 0; j < KPF; ++j) kb[j] = kread(j);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 36; ++s) {
+          s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[s % KPF], qf[s], s_next, 0, 0, 0);
+          if (s + KPF < 36) kb[s % KPF] = kread(s + KPF);
+          if (s < 16) {
+            // masked tiles scale first and then select, so that a masked
+            // token is -inf whatever the scale (even 0)
+            const int i = s;
+            x[i] = MASKED ? ((8 * (i >> 2) + (i & 3) < lim) ? s_cur[i] * c : -INFINITY) : s_cur[i];
+            if ((i & 3) == 3)
+              mx[i >> 2] = fmaxf(fmaxf(x[i - 3], x[i - 2]), fmaxf(x[i - 1], x[i]));
+          } else if (s < 32) {
+            const int i = s - 16;
+            const float pi = __builtin_amdgcn_exp2f(MASKED ? x[i] + neg_m : __builtin_fmaf(x[i], c, neg_m));
+            psum += pi;
+            if (i & 1) pw[i >> 1] = pack_bf16x2(p_prev, pi);
+            p_prev = pi;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        lmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+        if (!MASKED) lmax *= c;
+      };
+      const bool masked = !__all(t0 + kTile <= n_vis);
+      if (!masked)
+        fused(std::integral_constant<bool, false>{});
+      else
+        fused(std::integral_constant<bool, true>{});
+
+      if (__builtin_expect(__any(lmax > m_run + kRescaleThreshold), 0)) {
+        // a new reference maximum: the two lanes holding a row's tokens agree
+        // on it, the accumulators are rescaled, the probabilities redone
+        const float rmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
+        const bool raise = rmax > m_run + kRescaleThreshold;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - rmax) : 1.f;
+        if (__any(raise && m_run != -INFINITY)) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) acc_scale(o[ct], alpha);
+        }
+        l_run *= alpha;
+        if (raise) m_run = rmax;
+        const float neg_m2 = m_run == -INFINITY ? 0.f : -m_run;
+        psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(masked ? x[2 * j] + neg_m2
+                                                         : __builtin_fmaf(x[2 * j], c, neg_m2));
+          const float p1 = __builtin_amdgcn_exp2f(masked ? x[2 * j + 1] + neg_m2
+                                                         : __builtin_fmaf(x[2 * j + 1], c, neg_m2));
+          psum += p0 + p1;
+          pw[j] = pack_bf16x2(p0, p1);
+        }
+      }
+      l_run += psum;
+      const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]}),
+                            __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]})};
+
+      // ---- value product O^T (columns x rows) += V^T P^T of tile it, token
+      // half major so consecutive MFMAs are independent; operands of two
+      // steps ahead in flight
+      const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage[it % NST];
+      auto vread = [&](int q) {
+        const int ct = q % NCT, kk = q / NCT;
+        return vt_fragment(st + vofs0 + 2048 * ct + 256 * kk, st + vofs1 + 2048 * ct + 256 * kk);
+      };
+      constexpr int NQ = 2 * NCT;
+      bf16x8 va[VPF];
+#pragma unroll
+      for (int j = 0; j < VPF; ++j) va[j] = vread(j);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        o[q % NCT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[q % VPF], pb[q / NCT], o[q % NCT], 0, 0, 0);
+        if (q + VPF < NQ) va[q % VPF] = vread(q + VPF);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s_cur = s_next;
+    }
+
+    // ---- epilogue: final rows, or fp32 partials of a split sequence
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    if (bad) lse_v = __builtin_nanf("");
+    if (row_ok) {
+      const int64_t row = (int64_t)b * a.M + r;
+      if (!split) {
+        uint16_t* orow = a.out + row * kDL;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = cbase + 32 * ct + 8 * g + 4 * hi;
+            uint16_t hbits[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              hbits[e] = bad ? (uint16_t)0x7FC0 : f32_to_bf16_bits(o[ct][4 * g + e] * inv_l);
+            const uint64_t packed = (uint64_t)hbits[0] | ((uint64_t)hbits[1] << 16) |
+                                    ((uint64_t)hbits[2] << 32) | ((uint64_t)hbits[3] << 48);
+            *reinterpret_cast<uint64_t*>(orow + col) = packed;
+          }
+        if (hi == 0 && cg == 0) a.lse[row] = lse_v;
+      } else {
+        float* prow = a.part_o + ((int64_t)slot * a.M + r) * kDL;
+        const float nanv = __builtin_nanf("");
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = cbase + 32 * ct + 8 * g + 4 * hi;
+            float4 f;
+            f.x = bad ? nanv : o[ct][4 * g + 0] * inv_l;
+            f.y = bad ? nanv : o[ct][4 * g + 1] * inv_l;
+            f.z = bad ? nanv : o[ct][4 * g + 2] * inv_l;
+            f.w = bad ? nanv : o[ct][4 * g + 3] * inv_l;
+            *reinterpret_cast<float4*>(prow + col) = f;
+          }
+        if (hi == 0 && cg == 0) a.part_lse[(int64_t)slot * a.M + r] = lse_v;
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();   // the ring is reused by the next sequence
+  }
+}
+
 // ------------------------------------------------------------ combine
 
 // Merge n (lse, O) parts of one row; one wave, 8 columns per lane.
@@ -913,8 +1311,8 @@ mla_status validate_problem(const mla_problem* p) {
   if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_Q8_0)
     return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);
   if (p->num_parts < 0) return fail(MLA_ERR_INVALID_ARG, "num_parts must be >= 0");
-  if (p->m_tile != 0 && p->m_tile != 32 && p->m_tile != 64)
-    return fail(MLA_ERR_INVALID_ARG, "m_tile must be 0, 32 or 64 (got %d)", p->m_tile);
+  if (p->m_tile != 0 && p->m_tile != 32 && p->m_tile != 64 && p->m_tile != 128)
+    return fail(MLA_ERR_INVALID_ARG, "m_tile must be 0, 32, 64 or 128 (got %d)", p->m_tile);
   return MLA_OK;
 }
 
@@ -925,16 +1323,28 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   if (s != MLA_OK) return s;
   const int M = p->seqlen_q * p->num_heads;
   pl->M = M;
-  // row tile: 32 rows (one 32-row group) or 64 rows (two groups); each
-  // group's work is split over CG waves. More rows than one tile holds take
-  // several row tiles per KV part; they are placed on the same XCD so the
-  // second read of each cache tile hits L2.
-  pl->HG = p->m_tile ? p->m_tile / 32 : (M <= 32 ? 1 : 2);
-  pl->CG = 4;
-  if (const char* e = getenv("MLA_SPLIT_WAYS")) {   // tuning hook: waves per 32-row group
-    const int cg = atoi(e);
-    if (cg == 2 || cg == 4) pl->CG = cg;
+  // Row tile. bf16 cache: 32, 64 or 128 rows per workgroup (1, 2 or 4 row
+  // groups of 32, each wave owning whole rows); the smallest tile that holds
+  // all rows of a sequence, so the cache is streamed once per part. q8_0
+  // cache: 32 or 64 rows, each row group's work split over CG waves. More rows
+  // than one tile holds take several row tiles per KV part, placed on the
+  // same XCD so the second read of each cache tile hits L2.
+  const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
+  if (q8 && p->m_tile == 128)
+    return fail(MLA_ERR_UNSUPPORTED, "m_tile 128 is not available for the q8_0 cache");
+  if (p->m_tile) {
+    pl->HG = p->m_tile / 32;
+  } else if (q8) {
+    pl->HG = M <= 32 ? 1 : 2;
+  } else {
+    pl->HG = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   }
+  pl->CG = 4;
+  if (const char* e = getenv("MLA_SPLIT_WAYS")) {   // tuning hook (q8_0): waves per row group
+    const int cg = atoi(e);
+    if (q8 && (cg == 2 || cg == 4)) pl->CG = cg;
+  }
+  if (!q8) pl->CG = 4 / pl->HG;
   pl->MT = 32 * pl->HG;
   pl->m_tiles = (M + pl->MT - 1) / pl->MT;
   int P = p->num_parts;
@@ -976,6 +1386,12 @@ template <int HG, int CG, bool Q8>
 hipError_t launch_decode(const DecodeParams& dp, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((mla_decode_kernel<HG, CG, Q8>), dim3(grid), dim3(64 * HG * CG), 0, stream,
                      dp);
+  return hipGetLastError();
+}
+
+template <int HG>
+hipError_t launch_rows(const DecodeParams& dp, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_decode_rows_kernel<HG>), dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -1065,20 +1481,27 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
   dp.P = pl.P;
   dp.m_tiles = pl.m_tiles;
   dp.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  dp.scale_mag_log2 = fabsf(dp.scale_log2);
+  dp.q_sign2 = softmax_scale < 0.f ? 0x80008000u : 0u;
 
   const int grid = pl.P * pl.m_tiles;
   hipError_t e;
   const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
-  switch (pl.HG * 20 + pl.CG * 2 + (q8 ? 1 : 0)) {
-    case 28: e = launch_decode<1, 4, false>(dp, grid, stream); break;
-    case 29: e = launch_decode<1, 4, true>(dp, grid, stream); break;
-    case 24: e = launch_decode<1, 2, false>(dp, grid, stream); break;
-    case 25: e = launch_decode<1, 2, true>(dp, grid, stream); break;
-    case 48: e = launch_decode<2, 4, false>(dp, grid, stream); break;
-    case 49: e = launch_decode<2, 4, true>(dp, grid, stream); break;
-    case 44: e = launch_decode<2, 2, false>(dp, grid, stream); break;
-    case 45: e = launch_decode<2, 2, true>(dp, grid, stream); break;
-    default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
+  if (!q8) {
+    switch (pl.HG) {
+      case 1: e = launch_rows<1>(dp, grid, stream); break;
+      case 2: e = launch_rows<2>(dp, grid, stream); break;
+      case 4: e = launch_rows<4>(dp, grid, stream); break;
+      default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
+    }
+  } else {
+    switch (pl.HG * 10 + pl.CG) {
+      case 14: e = launch_decode<1, 4, true>(dp, grid, stream); break;
+      case 12: e = launch_decode<1, 2, true>(dp, grid, stream); break;
+      case 24: e = launch_decode<2, 4, true>(dp, grid, stream); break;
+      case 22: e = launch_decode<2, 2, true>(dp, grid, stream); break;
+      default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
+    }
   }
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   if (pl.P > 1) {
