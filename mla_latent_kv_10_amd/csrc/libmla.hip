@@ -789,6 +789,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
   constexpr int NCT = 16 / CG;            // 32-column output blocks per wave
   constexpr int NST = 4;                  // ring stages
   constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
+  // HG = 4: 128 rows per CU leave no registers for a second score tile, so
+  // the score product of a tile is not overlapped with the previous softmax
+  constexpr bool PIPE = HG != 4;
   constexpr int KPF = HG == 4 ? 2 : 3;    // score operands in flight
   constexpr int VPF = HG == 4 ? 2 : 3;    // value operands in flight
   static_assert(HG == 1 || HG == 2 || HG == 4, "row groups");
@@ -936,10 +939,17 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      auto rd = [&](int s) { return lds_read_b128(st + 1024 * s + ((s & 1) ? kofs1 : kofs0)); };
+      constexpr int D = 4;
+      bf16x8 kf[D];
+#pragma unroll
+      for (int j = 0; j < D; ++j) kf[j] = rd(j);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 36; ++s) {
-        const bf16x8 kf = lds_read_b128(st + 1024 * s + ((s & 1) ? kofs1 : kofs0));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % D], qf[s], acc, 0, 0, 0);
+        if (s + D < 36) kf[s % D] = rd(s + D);
+        __builtin_amdgcn_sched_barrier(0);
       }
       return acc;
     };
@@ -958,7 +968,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
     if (n_run > 0) issue(0);
     if (n_run > 1) issue(1);
     if (n_run > 2) issue(2);
-    if (n_run > 0) {
+    if (PIPE && n_run > 0) {
       if (n_run > 2) wait_vmcnt<2 * LPW>();
       else if (n_run > 1) wait_vmcnt<LPW>();
       else wait_vmcnt<0>();
@@ -967,12 +977,23 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
       s_cur = scores((const LDS_AS uint8_t*)s_stage[0]);
     }
     for (int it = 0; it < n_run; ++it) {
-      if (it + 1 < n_run) {
-        if (it + 2 < n_run) wait_vmcnt<LPW>();
+      if (PIPE) {
+        if (it + 1 < n_run) {
+          if (it + 2 < n_run) wait_vmcnt<LPW>();
+          else wait_vmcnt<0>();
+          lds_barrier();
+          if (it + 3 < n_run) issue(it + 3);
+          prepare(it + 1);
+        }
+      } else {
+        // tile it landed; tiles it+1, it+2 may still be in flight
+        if (it + 2 < n_run) wait_vmcnt<2 * LPW>();
+        else if (it + 1 < n_run) wait_vmcnt<LPW>();
         else wait_vmcnt<0>();
         lds_barrier();
         if (it + 3 < n_run) issue(it + 3);
-        prepare(it + 1);
+        prepare(it);
+        s_cur = scores((const LDS_AS uint8_t*)s_stage[it % NST]);
       }
       // One straight-line block, software-pipelined by hand: the score product
       // of tile it+1 (on the last tile a dummy pass over a resident stage,
@@ -1003,13 +1024,17 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
         float p_prev = 0.f;
         psum = 0.f;
         bf16x8 kb[KPF];
+        if (PIPE) {
 #pragma unroll
-        for (int j = 0; j < KPF; ++j) kb[j] = kread(j);
+          for (int j = 0; j < KPF; ++j) kb[j] = kread(j);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 36; ++s) {
-          s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[s % KPF], qf[s], s_next, 0, 0, 0);
-          if (s + KPF < 36) kb[s % KPF] = kread(s + KPF);
+          if (PIPE) {
+            s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[s % KPF], qf[s], s_next, 0, 0, 0);
+            if (s + KPF < 36) kb[s % KPF] = kread(s + KPF);
+          }
           if (s < 16) {
             // masked tiles scale first and then select, so that a masked
             // token is -inf whatever the scale (even 0)
@@ -1082,7 +1107,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
         if (q + VPF < NQ) va[q % VPF] = vread(q + VPF);
         __builtin_amdgcn_sched_barrier(0);
       }
-      s_cur = s_next;
+      if (PIPE) s_cur = s_next;
     }
 
     // ---- epilogue: final rows, or fp32 partials of a split sequence
@@ -1128,6 +1153,355 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
     }
     wait_vmcnt<0>();
     __syncthreads();   // the ring is reused by the next sequence
+  }
+}
+
+// ------------------------------------------ bf16 decode kernel (128-row tile)
+
+// 128 query rows per workgroup, so every cache tile is streamed into exactly
+// one CU (the LDS-DMA fill rate per CU is the scarce resource). Wave w:
+//  * computes the full 576-column scores and the softmax of rows 32w..32w+31
+//    (its query fragments stay in registers);
+//  * publishes those rows' probabilities (bf16, already in the value
+//    product's B-operand layout) through LDS;
+//  * accumulates the value product of all 128 rows for output columns
+//    128w..128w+127, so each V^T operand read from LDS feeds four MFMAs.
+// Two barriers per 32-token tile: one for the tile (3-stage LDS-DMA ring,
+// two tiles in flight), one for the probabilities. The reference maximum of
+// the online softmax moves rarely; when a row's does, its owner publishes the
+// factor and every wave rescales that row's accumulators.
+__global__ __launch_bounds__(256, 1) void mla_decode_quad_kernel(DecodeParams a) {
+  constexpr int NW = 4;
+  constexpr int NT = 64 * NW;
+  constexpr int MT = 128;
+  constexpr int NST = 3;                  // ring stages
+  constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
+  constexpr int KPF = 3;                  // score operands in flight
+
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NST][kTileBytes];
+  // probabilities: [row group][token half][lane] x 16 bytes (B-operand layout)
+  __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];
+  __shared__ float s_alpha[MT];           // rescale factor per row (rare path)
+  __shared__ float s_lsum[MT];            // softmax denominators (epilogue)
+  __shared__ int s_flag[NW];
+  __shared__ int s_pre[kMaxBatch + 1];
+  __shared__ int s_misc[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const int hi = lane >> 5, l32 = lane & 31;
+
+  int v = blockIdx.x;
+  const int G = gridDim.x;
+  if ((G & 7) == 0) v = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int part = v / a.m_tiles, mt = v % a.m_tiles;
+
+  plan_prefix<NT>(a.seqlens, a.B, a.max_blocks, s_pre, s_misc);
+  const int T = uniform(s_pre[a.B]);
+  const int P = a.P;
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= a.B; b += NT) a.ws_prefix[b] = s_pre[b];
+  const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
+
+  if (tid == 0) {
+    s_misc[8] = 0x7fffffff;
+    s_misc[9] = -1;
+  }
+  __syncthreads();
+  for (int b = tid; b < a.B; b += NT) {
+    const int lo = s_pre[b], hi2 = s_pre[b + 1];
+    bool mine;
+    if (hi2 > lo) {
+      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
+    } else {
+      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
+      mine = owner == part;
+    }
+    if (mine) {
+      atomicMin(&s_misc[8], b);
+      atomicMax(&s_misc[9], b);
+    }
+  }
+  __syncthreads();
+  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+
+  const int r = mt * MT + 32 * wave + l32;   // row whose scores this lane computes
+  const bool row_ok = r < a.M;
+  const int q_i = row_ok ? r / a.H : 0;
+  const int cbase = 128 * wave;              // first output column of this wave
+
+  const int kofs0 = 16 * tile_unit(l32, hi);
+  const int kofs1 = 16 * tile_unit(l32, 2 + hi) - 1024;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
+  const int vc = cbase / 8 + 2 * (g16 & 1) + (vq >> 1);
+  const int vofs0 = 16 * tile_unit(4 * vh + vs, vc) + 8 * (vq & 1);
+  const int vofs1 = 16 * tile_unit(8 + 4 * vh + vs, vc) + 8 * (vq & 1);
+  const int dchunk = 2 * wave + hi;
+  const uint32_t doff = (uint32_t)((l32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
+
+  for (int b = b_first; b <= b_last; ++b) {
+    const int pre_b = uniform(s_pre[b]), pre_e = uniform(s_pre[b + 1]);
+    const int L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
+    const int seg_lo = max(p_lo, pre_b) - pre_b, seg_hi = min(p_hi, pre_e) - pre_b;
+    bool split = false;
+    int slot = 0;
+    if (pre_e > pre_b) {
+      const int fp = part_of(pre_b, P, T), lp = part_of(pre_e - 1, P, T);
+      split = lp > fp;
+      slot = 2 * part + ((part == fp && pre_b > p_lo) ? 1 : 0);
+    }
+    const int t_begin = 2 * seg_lo;
+    const int t_end = min(2 * seg_hi, (L + kTile - 1) / kTile);
+    const int n_tiles = max(0, t_end - t_begin);
+    const CONST_AS int32_t* bt =
+        (const CONST_AS int32_t*)a.block_table + (int64_t)b * a.max_blocks;
+
+    int bad_local = 0;
+    for (int j = seg_lo + tid; j < seg_hi; j += NT) {
+      const int id = bt[j];
+      if (id < 0 || (int64_t)id >= a.num_blocks) bad_local = 1;
+    }
+    const bool bad = __syncthreads_or(bad_local) != 0;
+    const int n_run = bad ? 0 : n_tiles;
+
+    const int n_vis = row_ok ? L - a.s_q + 1 + q_i : 0x7fffffff;
+
+    // o[4 rb + cb]: rows 32 rb .. +31 of the tile, columns cbase + 32 cb .. +31
+    f32x16 o[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[j][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // Block ids of the segment, 64 at a time, one per lane: a tile's id is a
+    // v_readlane away, with no memory access on the tile loop's path.
+    const int seg_len = max(0, seg_hi - seg_lo);
+    int bt_base = 0;
+    int bt_lane = 0;
+    auto load_ids = [&]() {
+      const int j = bt_base + min(lane, max(0, seg_len - bt_base - 1));
+      bt_lane = seg_len > 0 ? ((const int32_t*)a.block_table)[(int64_t)b * a.max_blocks + seg_lo + j] : 0;
+    };
+    // Source of tile idx (segment-relative; past the segment: its last tile,
+    // reloaded as a harmless dummy so that every iteration issues one tile).
+    auto tile_src = [&](int idx) {
+      idx = min(idx, n_run - 1);
+      int rel = (idx >> 1) - bt_base;
+      if (rel >= 64) {            // next 64 ids (segments longer than 64 blocks)
+        bt_base += 64;
+        rel -= 64;
+        load_ids();
+        wait_vmcnt<0>();
+      }
+      const int64_t phys = uniform(__builtin_amdgcn_readlane(bt_lane, rel));
+      return a.kv + (phys * kBT + ((t_begin + idx) & 1) * kTile) * kRowBytes;
+    };
+    auto issue = [&](int idx) {
+      const uint32_t dst = lds_addr_of(s_stage[idx % NST]) + 1024 * wave;
+      const uint8_t* src = tile_src(idx);
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) dma16_sbase(src + 128 * j, doff, dst + 4096 * j);
+    };
+    auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
+      for (int u = tid; u < kTile * 72; u += NT) {
+        const int c = u >> 5, pos = u & 31;
+        if ((pos ^ (4 * (c & 3))) >= valid)
+          *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+
+    wait_vmcnt<0>();
+    load_ids();
+    wait_vmcnt<0>();
+    if (n_run > 0) {
+      issue(0);
+      issue(1);
+    }
+    // the query rows load while the first tiles stream in (the compiler's
+    // waits for these loads also cover the earlier LDS-DMA loads)
+    bf16x8 qf[36];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)b * a.M + (row_ok ? r : 0)) * kDK;
+      const uint32_t sg = a.q_sign2;
+#pragma unroll
+      for (int s = 0; s < 36; ++s) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if (row_ok) z = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hi) ^ sg;
+        qf[s] = __builtin_bit_cast(bf16x8, z);
+      }
+    }
+    for (int it = 0; it < n_run; ++it) {
+      // ---- tile it has landed (tile it+1 may still be in flight); the stage
+      // of tile it-1 is free for tile it+2
+      wait_vmcnt<LPW>();
+      lds_barrier();
+      const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage[it % NST];
+      // tile it+2 streams into the free stage, one load every four score
+      // MFMAs: a burst of loads would stall this wave on a full memory queue
+      const uint8_t* nsrc = tile_src(it + 2);
+      const uint32_t ndst = lds_addr_of(s_stage[(it + 2) % NST]) + 1024 * wave;
+      const int t0 = (t_begin + it) * kTile;
+      {
+        const int valid = L - t0;
+        if (valid < kTile) {
+          clear_tail((LDS_AS uint8_t*)s_stage[it % NST], valid);
+          lds_barrier();
+        }
+      }
+
+      // ---- scores S^T (tokens x own rows): register i is token
+      // 8(i>>2) + 4hi + (i&3)
+      f32x16 s;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = 0.f;
+      {
+        auto rd = [&](int k) { return lds_read_b128(st + 1024 * k + ((k & 1) ? kofs1 : kofs0)); };
+        bf16x8 kf[KPF];
+#pragma unroll
+        for (int j = 0; j < KPF; ++j) kf[j] = rd(j);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 36; ++k) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k % KPF], qf[k], s, 0, 0, 0);
+          if (k + KPF < 36) kf[k % KPF] = rd(k + KPF);
+          if ((k & 3) == 1) dma16_sbase(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+
+      // ---- online softmax of the own rows (log2 domain)
+      const float c = a.scale_mag_log2;
+      const bool masked = !__all(t0 + kTile <= n_vis);
+      const int lim = n_vis - t0 - 4 * hi;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        x[i] = masked ? ((8 * (i >> 2) + (i & 3) < lim) ? s[i] * c : -INFINITY) : s[i] * c;
+      float lmax = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, x[i]);
+      float alpha = 1.f;
+      const bool want = lmax > m_run + kRescaleThreshold;
+      const bool raise_any = __any(want);
+      if (__builtin_expect(raise_any, 0)) {
+        const float rmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
+        const bool raise = rmax > m_run + kRescaleThreshold;
+        alpha = raise ? __builtin_amdgcn_exp2f(m_run - rmax) : 1.f;
+        l_run *= alpha;
+        if (raise) m_run = rmax;
+      }
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      float psum = 0.f;
+      uint32_t pw[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
+        const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
+        psum += p0 + p1;
+        pw[j] = pack_bf16x2(p0, p1);
+      }
+      l_run += psum;
+      s_p[wave][0][lane] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+      s_p[wave][1][lane] = u32x4{pw[4], pw[5], pw[6], pw[7]};
+      if (raise_any && hi == 0) s_alpha[32 * wave + l32] = alpha;
+      if (lane == 0) s_flag[wave] = raise_any ? 1 : 0;
+      lds_barrier();
+
+      // ---- a row's reference maximum moved: rescale its accumulators in
+      // every wave (on a segment's first tile they are still zero)
+      {
+        const int f = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
+        if (__builtin_expect(f != 0 && it > 0, 0)) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            const float al = s_flag[rb] ? s_alpha[32 * rb + l32] : 1.f;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) acc_scale(o[4 * rb + cb], al);
+          }
+        }
+      }
+
+      // ---- value product of all 128 rows, own 128 columns:
+      // O^T(columns x rows) += V^T P^T, each V^T operand shared by 4 row blocks
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 pf[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) pf[rb] = __builtin_bit_cast(bf16x8, s_p[rb][kk][lane]);
+        auto vread = [&](int cb) {
+          return vt_fragment(st + vofs0 + 2048 * cb + 256 * kk, st + vofs1 + 2048 * cb + 256 * kk);
+        };
+        bf16x8 va[2] = {vread(0), vread(1)};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb & 1], pf[rb], o[4 * rb + cb], 0, 0, 0);
+          if (cb + 2 < 4) va[cb & 1] = vread(cb + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+
+    // ---- epilogue: every wave needs the denominators of all 128 rows
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    if (bad) lse_v = __builtin_nanf("");
+    if (hi == 0) s_lsum[32 * wave + l32] = l_tot;
+    lds_barrier();
+    const float nanv = __builtin_nanf("");
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int rr = mt * MT + 32 * rb + l32;
+      if (rr >= a.M) continue;
+      const float lt = s_lsum[32 * rb + l32];
+      const float inv_l = lt > 0.f ? 1.f / lt : 0.f;
+      const int64_t row = (int64_t)b * a.M + rr;
+      if (!split) {
+        uint16_t* orow = a.out + row * kDL;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = cbase + 32 * cb + 8 * g + 4 * hi;
+            const f32x16& acc = o[4 * rb + cb];
+            uint32_t w0, w1;
+            if (bad) {
+              w0 = w1 = 0x7FC07FC0u;
+            } else {
+              w0 = pack_bf16x2(acc[4 * g + 0] * inv_l, acc[4 * g + 1] * inv_l);
+              w1 = pack_bf16x2(acc[4 * g + 2] * inv_l, acc[4 * g + 3] * inv_l);
+            }
+            *reinterpret_cast<uint64_t*>(orow + col) = (uint64_t)w0 | ((uint64_t)w1 << 32);
+          }
+      } else {
+        float* prow = a.part_o + ((int64_t)slot * a.M + rr) * kDL;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = cbase + 32 * cb + 8 * g + 4 * hi;
+            const f32x16& acc = o[4 * rb + cb];
+            float4 f;
+            f.x = bad ? nanv : acc[4 * g + 0] * inv_l;
+            f.y = bad ? nanv : acc[4 * g + 1] * inv_l;
+            f.z = bad ? nanv : acc[4 * g + 2] * inv_l;
+            f.w = bad ? nanv : acc[4 * g + 3] * inv_l;
+            *reinterpret_cast<float4*>(prow + col) = f;
+          }
+      }
+    }
+    if (row_ok && hi == 0) {
+      const int64_t row = (int64_t)b * a.M + r;
+      if (!split)
+        a.lse[row] = lse_v;
+      else
+        a.part_lse[(int64_t)slot * a.M + r] = lse_v;
+    }
+    wait_vmcnt<0>();     // no LDS-DMA may outlive the ring's use
+    if (b < b_last) __syncthreads();   // the ring and the exchange buffers are reused
   }
 }
 
@@ -1389,6 +1763,11 @@ hipError_t launch_decode(const DecodeParams& dp, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_quad(const DecodeParams& dp, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_decode_quad_kernel, dim3(grid), dim3(256), 0, stream, dp);
+  return hipGetLastError();
+}
+
 template <int HG>
 hipError_t launch_rows(const DecodeParams& dp, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((mla_decode_rows_kernel<HG>), dim3(grid), dim3(256), 0, stream, dp);
@@ -1491,7 +1870,8 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
     switch (pl.HG) {
       case 1: e = launch_rows<1>(dp, grid, stream); break;
       case 2: e = launch_rows<2>(dp, grid, stream); break;
-      case 4: e = launch_rows<4>(dp, grid, stream); break;
+      case 4: e = getenv("MLA_ROWS128") ? launch_rows<4>(dp, grid, stream)
+                                        : launch_quad(dp, grid, stream); break;
       default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
     }
   } else {
