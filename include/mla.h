@@ -113,7 +113,8 @@ mla_status mla_num_parts(const mla_problem* p, int32_t* num_parts);
  * Decode one step: out and lse for every query row of every sequence, as
  * defined at the top of this file. Uses split-KV partitions when that fills
  * the GPU better, with a log-sum-exp merge of the partial results (the same
- * merge as mla_combine). workspace: device buffer of at least
+ * merge as mla_combine; inside the workspace a partial result is held as
+ * bf16 of the part's normalised output, plus its fp32 lse). workspace: device buffer of at least
  * mla_workspace_size bytes (may be NULL when that size is 0); its contents on
  * entry do not matter and are overwritten.
  */

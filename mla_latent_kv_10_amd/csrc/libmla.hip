@@ -78,7 +78,7 @@ struct DecodeParams {
   float* lse;
   int32_t* ws_prefix;   // [B+1] block prefix, written by workgroup 0
   float* part_lse;      // [2P, M]
-  float* part_o;        // [2P, M, 512]
+  uint16_t* part_o;     // [2P, M, 512] bf16: partial results of split sequences
   int64_t num_blocks;
   int B, s_q, H, M, max_blocks, P, m_tiles;
   float scale_log2;     // softmax_scale * log2(e)
@@ -720,19 +720,20 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
           }
         if (hi == 0 && cg == 0) a.lse[row] = lse_v;
       } else {
-        float* prow = a.part_o + ((int64_t)slot * a.M + r) * kDL;
-        const float nanv = __builtin_nanf("");
+        uint16_t* prow = a.part_o + ((int64_t)slot * a.M + r) * kDL;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int col = cbase + 32 * ct + 8 * g + 4 * hi;
-            float4 f;
-            f.x = bad ? nanv : o[ct][4 * g + 0] * inv_l;
-            f.y = bad ? nanv : o[ct][4 * g + 1] * inv_l;
-            f.z = bad ? nanv : o[ct][4 * g + 2] * inv_l;
-            f.w = bad ? nanv : o[ct][4 * g + 3] * inv_l;
-            *reinterpret_cast<float4*>(prow + col) = f;
+            uint32_t w0, w1;
+            if (bad) {
+              w0 = w1 = 0x7FC07FC0u;
+            } else {
+              w0 = pack_bf16x2(o[ct][4 * g + 0] * inv_l, o[ct][4 * g + 1] * inv_l);
+              w1 = pack_bf16x2(o[ct][4 * g + 2] * inv_l, o[ct][4 * g + 3] * inv_l);
+            }
+            *reinterpret_cast<uint64_t*>(prow + col) = (uint64_t)w0 | ((uint64_t)w1 << 32);
           }
         if (hi == 0 && cg == 0) a.part_lse[(int64_t)slot * a.M + r] = lse_v;
       }
@@ -1134,19 +1135,20 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
           }
         if (hi == 0 && cg == 0) a.lse[row] = lse_v;
       } else {
-        float* prow = a.part_o + ((int64_t)slot * a.M + r) * kDL;
-        const float nanv = __builtin_nanf("");
+        uint16_t* prow = a.part_o + ((int64_t)slot * a.M + r) * kDL;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int col = cbase + 32 * ct + 8 * g + 4 * hi;
-            float4 f;
-            f.x = bad ? nanv : o[ct][4 * g + 0] * inv_l;
-            f.y = bad ? nanv : o[ct][4 * g + 1] * inv_l;
-            f.z = bad ? nanv : o[ct][4 * g + 2] * inv_l;
-            f.w = bad ? nanv : o[ct][4 * g + 3] * inv_l;
-            *reinterpret_cast<float4*>(prow + col) = f;
+            uint32_t w0, w1;
+            if (bad) {
+              w0 = w1 = 0x7FC07FC0u;
+            } else {
+              w0 = pack_bf16x2(o[ct][4 * g + 0] * inv_l, o[ct][4 * g + 1] * inv_l);
+              w1 = pack_bf16x2(o[ct][4 * g + 2] * inv_l, o[ct][4 * g + 3] * inv_l);
+            }
+            *reinterpret_cast<uint64_t*>(prow + col) = (uint64_t)w0 | ((uint64_t)w1 << 32);
           }
         if (hi == 0 && cg == 0) a.part_lse[(int64_t)slot * a.M + r] = lse_v;
       }
@@ -1445,53 +1447,63 @@ __global__ __launch_bounds__(256, 1) void mla_decode_quad_kernel(DecodeParams a)
       }
     }
 
-    // ---- epilogue: every wave needs the denominators of all 128 rows
+    // ---- epilogue: every wave needs the denominators of all 128 rows. The
+    // normalised bf16 rows go through LDS (the ring is idle now) so that the
+    // global stores are whole 256-byte row segments, 16 bytes per lane.
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     if (bad) lse_v = __builtin_nanf("");
+    wait_vmcnt<0>();                   // ring loads (including dummies) have landed
     if (hi == 0) s_lsum[32 * wave + l32] = l_tot;
     lds_barrier();
-    const float nanv = __builtin_nanf("");
+    constexpr int kStageRow = 272;     // bytes per staged row: 256 + 16 of padding
+    uint16_t* dst_base = split ? a.part_o + ((int64_t)slot * a.M) * kDL
+                               : a.out + ((int64_t)b * a.M) * kDL;
+    LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_stage[0] + wave * (64 * kStageRow);
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int rr = mt * MT + 32 * rb + l32;
-      if (rr >= a.M) continue;
-      const float lt = s_lsum[32 * rb + l32];
-      const float inv_l = lt > 0.f ? 1.f / lt : 0.f;
-      const int64_t row = (int64_t)b * a.M + rr;
-      if (!split) {
-        uint16_t* orow = a.out + row * kDL;
+    for (int half = 0; half < 2; ++half) {
+      // rows 64 half .. 64 half + 63 of the tile, this wave's 128 columns
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = cbase + 32 * cb + 8 * g + 4 * hi;
-            const f32x16& acc = o[4 * rb + cb];
-            uint32_t w0, w1;
-            if (bad) {
-              w0 = w1 = 0x7FC07FC0u;
-            } else {
-              w0 = pack_bf16x2(acc[4 * g + 0] * inv_l, acc[4 * g + 1] * inv_l);
-              w1 = pack_bf16x2(acc[4 * g + 2] * inv_l, acc[4 * g + 3] * inv_l);
-            }
-            *reinterpret_cast<uint64_t*>(orow + col) = (uint64_t)w0 | ((uint64_t)w1 << 32);
-          }
-      } else {
-        float* prow = a.part_o + ((int64_t)slot * a.M + rr) * kDL;
+      for (int q = 0; q < 2; ++q) {
+        const int rb = 2 * half + q;
+        const float lt = s_lsum[32 * rb + l32];
+        // an invalid block id makes the whole sequence NaN
+        const float inv_l = bad ? __builtin_nanf("") : (lt > 0.f ? 1.f / lt : 0.f);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = cbase + 32 * cb + 8 * g + 4 * hi;
             const f32x16& acc = o[4 * rb + cb];
-            float4 f;
-            f.x = bad ? nanv : acc[4 * g + 0] * inv_l;
-            f.y = bad ? nanv : acc[4 * g + 1] * inv_l;
-            f.z = bad ? nanv : acc[4 * g + 2] * inv_l;
-            f.w = bad ? nanv : acc[4 * g + 3] * inv_l;
-            *reinterpret_cast<float4*>(prow + col) = f;
+            const uint32_t w0 = pack_bf16x2(acc[4 * g + 0] * inv_l, acc[4 * g + 1] * inv_l);
+            const uint32_t w1 = pack_bf16x2(acc[4 * g + 2] * inv_l, acc[4 * g + 3] * inv_l);
+            const int col = 32 * cb + 8 * g + 4 * hi;
+            *reinterpret_cast<LDS_AS uint64_t*>(stg + (32 * q + l32) * kStageRow + 2 * col) =
+                (uint64_t)w0 | ((uint64_t)w1 << 32);
           }
       }
+      lds_barrier();
+      // 64 rows x 256 bytes: lane = 16 bytes, 4 rows per store instruction.
+      // The lane index is made opaque here so that the compiler cannot hoist
+      // (and spill) the sixteen store addresses out of the sequence loop.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int rl0 = ln >> 4, cl = 8 * (ln & 15);
+      const int row0 = mt * MT + 64 * half;
+      uint16_t* gdst = dst_base + (int64_t)(row0 + rl0) * kDL + cbase + cl;
+      const LDS_AS uint8_t* lsrc = stg + rl0 * kStageRow + 2 * cl;
+      if (row0 + 64 <= a.M) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          *reinterpret_cast<u32x4*>(gdst + 4 * i * kDL) =
+              *reinterpret_cast<const LDS_AS u32x4*>(lsrc + 4 * i * kStageRow);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (row0 + rl0 + 4 * i < a.M)
+            *reinterpret_cast<u32x4*>(gdst + 4 * i * kDL) =
+                *reinterpret_cast<const LDS_AS u32x4*>(lsrc + 4 * i * kStageRow);
+      }
+      lds_barrier();
     }
     if (row_ok && hi == 0) {
       const int64_t row = (int64_t)b * a.M + r;
@@ -1535,10 +1547,10 @@ __device__ __forceinline__ void merge_row(int n, PartPtr part, uint16_t* out_row
     for (int s = 0; s < n; ++s) {
       const float w = expf(*part.lse(s) - L);
       if (w == 0.f) continue;
-      const float4* src = reinterpret_cast<const float4*>(part.o(s) + 8 * lane);
-      const float4 x0 = src[0], x1 = src[1];
-      acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
-      acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+      float x[8];
+      part.o8(s, lane, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += w * x[e];
     }
   }
   uint16_t hb[8];
@@ -1553,8 +1565,8 @@ __device__ __forceinline__ void merge_row(int n, PartPtr part, uint16_t* out_row
   if (lane == 0) *lse_out = L;
 }
 
-struct SplitParts {   // parts of a split sequence inside the decode workspace
-  const float* part_o;
+struct SplitParts {   // parts of a split sequence inside the decode workspace (bf16)
+  const uint16_t* part_o;
   const float* part_lse;
   int M, r, first, pre_b, P, T;
   __device__ int slot(int s) const {
@@ -1562,7 +1574,15 @@ struct SplitParts {   // parts of a split sequence inside the decode workspace
     return 2 * p + ((s == 0 && pre_b > part_start(p, P, T)) ? 1 : 0);
   }
   __device__ const float* lse(int s) const { return part_lse + (int64_t)slot(s) * M + r; }
-  __device__ const float* o(int s) const { return part_o + ((int64_t)slot(s) * M + r) * kDL; }
+  __device__ void o8(int s, int lane, float x[8]) const {
+    const uint4 v = *reinterpret_cast<const uint4*>(part_o + ((int64_t)slot(s) * M + r) * kDL + 8 * lane);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __builtin_bit_cast(float, w[e] << 16);
+      x[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xffff0000u);
+    }
+  }
 };
 
 __global__ __launch_bounds__(kThreads) void mla_split_combine_kernel(DecodeParams a) {
@@ -1583,7 +1603,12 @@ struct DenseParts {   // caller-provided partials [S, R, 512] / [S, R]
   const float* part_lse;
   int64_t R, r;
   __device__ const float* lse(int s) const { return part_lse + (int64_t)s * R + r; }
-  __device__ const float* o(int s) const { return part_o + ((int64_t)s * R + r) * kDL; }
+  __device__ void o8(int s, int lane, float x[8]) const {
+    const float4* src = reinterpret_cast<const float4*>(part_o + ((int64_t)s * R + r) * kDL + 8 * lane);
+    const float4 x0 = src[0], x1 = src[1];
+    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+  }
 };
 
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(int S, int64_t R,
@@ -1746,7 +1771,7 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   if (P > 1) {
     off = align_up(off + (size_t)2 * P * M * 4, 256);
     pl->off_o = off;
-    off += (size_t)2 * P * M * kDL * 4;
+    off += (size_t)2 * P * M * kDL * 2;   // bf16 partials
   } else {
     pl->off_o = off;
   }
@@ -1850,7 +1875,7 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
   uint8_t* ws = (uint8_t*)workspace;
   dp.ws_prefix = (int32_t*)(ws + pl.off_prefix);
   dp.part_lse = (float*)(ws + pl.off_lse);
-  dp.part_o = (float*)(ws + pl.off_o);
+  dp.part_o = (uint16_t*)(ws + pl.off_o);
   dp.num_blocks = p->num_blocks;
   dp.B = p->batch;
   dp.s_q = p->seqlen_q;

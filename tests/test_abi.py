@@ -93,13 +93,13 @@ def _ws(L, prob):
 
 
 def test_workspace_size_formula(L):
-    # one part: only the block prefix; P parts: + 2P slots of lse and fp32 rows
+    # one part: only the block prefix; P parts: + 2P slots of lse and bf16 rows
     assert _ws(L, _prob(num_parts=1)) == 256
     B, M, P = 2, 16, 5
     pre = 256
     lse = (2 * P * M * 4 + 255) // 256 * 256
-    assert _ws(L, _prob(num_parts=P)) == pre + lse + 2 * P * M * 512 * 4
-    assert _ws(L, _prob(num_parts=3, seqlen_q=2, num_heads=128)) == 256 + 2 * 3 * 256 * 4 + 2 * 3 * 256 * 512 * 4
+    assert _ws(L, _prob(num_parts=P)) == pre + lse + 2 * P * M * 512 * 2
+    assert _ws(L, _prob(num_parts=3, seqlen_q=2, num_heads=128)) == 256 + 2 * 3 * 256 * 4 + 2 * 3 * 256 * 512 * 2
 
 
 def test_workspace_too_small(L):
