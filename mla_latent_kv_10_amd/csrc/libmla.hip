@@ -1517,6 +1517,374 @@ __global__ __launch_bounds__(256, 1) void mla_decode_quad_kernel(DecodeParams a)
   }
 }
 
+
+// Score-chain MFMA with its accumulator in VGPRs. With 256 AGPRs holding the
+// value-product accumulators there is no AGPR room for the score tile, so it
+// is pinned to VGPRs here (C/D of an MFMA may live in either file). `first`
+// starts the chain from zero (literal srcC); the chain's own back-to-back
+// SrcC dependency needs no wait states. mfma_vgpr_drain() must follow the
+// last one before VALU code reads the result.
+__device__ __forceinline__ void mfma_score(f32x16& acc, const bf16x8& a, const bf16x8& b, bool first) {
+  if (first)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
+  // XDL write -> VALU read of the same VGPRs: more than 18 wait states
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+
+// --------------------------- bf16 decode kernel (128-row tile, pipelined)
+
+// Same division of work as the 128-row kernel above (each wave: scores and
+// softmax of 32 rows, value product of all 128 rows for 128 columns), but the
+// value product of tile i-1 is interleaved with the score product of tile i:
+// the independent value MFMAs fill the latency of the dependent score chain,
+// and the transposing V reads mix with the score operand reads. A 4-stage
+// ring keeps tile i-1 resident while tile i is scored and tiles i+1, i+2
+// stream in. The plan prefix and the epilogue's scratch live in ring space
+// that is idle at those times, which keeps LDS under 160 KiB.
+__global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a) {
+  constexpr int NW = 4;
+  constexpr int NT = 64 * NW;
+  constexpr int MT = 128;
+  constexpr int NST = 4;                  // ring stages
+  constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
+  constexpr int KPF = 3;                  // score operands in flight
+
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NST][kTileBytes];
+  __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];   // P, B-operand layout
+  __shared__ float s_alpha[MT];
+  __shared__ int s_flag[NW];
+  // aliases inside ring stage 3, which is idle before the first tile and
+  // after the last one
+  int* s_pre = reinterpret_cast<int*>(s_stage[3]);                  // [B+1]
+  int* s_misc = reinterpret_cast<int*>(s_stage[3] + 4 * (kMaxBatch + 8));
+  float* s_lsum = reinterpret_cast<float*>(s_stage[3]);            // epilogue
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const int hi = lane >> 5, l32 = lane & 31;
+
+  int v = blockIdx.x;
+  const int G = gridDim.x;
+  if ((G & 7) == 0) v = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int part = v / a.m_tiles, mt = v % a.m_tiles;
+
+  plan_prefix<NT>(a.seqlens, a.B, a.max_blocks, s_pre, s_misc);
+  const int T = uniform(s_pre[a.B]);
+  const int P = a.P;
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= a.B; b += NT) a.ws_prefix[b] = s_pre[b];
+  const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
+
+  if (tid == 0) {
+    s_misc[8] = 0x7fffffff;
+    s_misc[9] = -1;
+  }
+  __syncthreads();
+  for (int b = tid; b < a.B; b += NT) {
+    const int lo = s_pre[b], hi2 = s_pre[b + 1];
+    bool mine;
+    if (hi2 > lo) {
+      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
+    } else {
+      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
+      mine = owner == part;
+    }
+    if (mine) {
+      atomicMin(&s_misc[8], b);
+      atomicMax(&s_misc[9], b);
+    }
+  }
+  __syncthreads();
+  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+  int pre_b = b_first <= b_last ? uniform(s_pre[b_first]) : 0;
+  __syncthreads();   // ring stage 3 is free from here on
+
+  const int r = mt * MT + 32 * wave + l32;   // row whose scores this lane computes
+  const bool row_ok = r < a.M;
+  const int q_i = row_ok ? r / a.H : 0;
+  const int cbase = 128 * wave;              // first output column of this wave
+
+  const int kofs0 = 16 * tile_unit(l32, hi);
+  const int kofs1 = 16 * tile_unit(l32, 2 + hi) - 1024;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
+  const int vc = cbase / 8 + 2 * (g16 & 1) + (vq >> 1);
+  const int vofs0 = 16 * tile_unit(4 * vh + vs, vc) + 8 * (vq & 1);
+  const int vofs1 = 16 * tile_unit(8 + 4 * vh + vs, vc) + 8 * (vq & 1);
+  const int dchunk = 2 * wave + hi;
+  const uint32_t doff = (uint32_t)((l32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
+
+  for (int b = b_first; b <= b_last; ++b) {
+    const int L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
+    const int pre_e = pre_b + (L + kBT - 1) / kBT;
+    const int seg_lo = max(p_lo, pre_b) - pre_b, seg_hi = min(p_hi, pre_e) - pre_b;
+    bool split = false;
+    int slot = 0;
+    if (pre_e > pre_b) {
+      const int fp = part_of(pre_b, P, T), lp = part_of(pre_e - 1, P, T);
+      split = lp > fp;
+      slot = 2 * part + ((part == fp && pre_b > p_lo) ? 1 : 0);
+    }
+    const int t_begin = 2 * seg_lo;
+    const int t_end = min(2 * seg_hi, (L + kTile - 1) / kTile);
+    const int n_tiles = max(0, t_end - t_begin);
+    const CONST_AS int32_t* bt =
+        (const CONST_AS int32_t*)a.block_table + (int64_t)b * a.max_blocks;
+
+    int bad_local = 0;
+    for (int j = seg_lo + tid; j < seg_hi; j += NT) {
+      const int id = bt[j];
+      if (id < 0 || (int64_t)id >= a.num_blocks) bad_local = 1;
+    }
+    const bool bad = __syncthreads_or(bad_local) != 0;
+    const int n_run = bad ? 0 : n_tiles;
+    const int n_vis = row_ok ? L - a.s_q + 1 + q_i : 0x7fffffff;
+
+    f32x16 o[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[j][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int seg_len = max(0, seg_hi - seg_lo);
+    int bt_base = 0;
+    int bt_lane = 0;
+    auto load_ids = [&]() {
+      const int j = bt_base + min(lane, max(0, seg_len - bt_base - 1));
+      bt_lane = seg_len > 0 ? ((const int32_t*)a.block_table)[(int64_t)b * a.max_blocks + seg_lo + j] : 0;
+    };
+    auto tile_src = [&](int idx) {
+      idx = min(idx, n_run - 1);
+      int rel = (idx >> 1) - bt_base;
+      if (rel >= 64) {
+        bt_base += 64;
+        rel -= 64;
+        load_ids();
+        wait_vmcnt<0>();
+      }
+      const int64_t phys = uniform(__builtin_amdgcn_readlane(bt_lane, rel));
+      return a.kv + (phys * kBT + ((t_begin + idx) & 1) * kTile) * kRowBytes;
+    };
+    auto issue = [&](int idx) {
+      const uint32_t dst = lds_addr_of(s_stage[idx % NST]) + 1024 * wave;
+      const uint8_t* src = tile_src(idx);
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) dma16_sbase(src + 128 * j, doff, dst + 4096 * j);
+    };
+    auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
+      for (int u = tid; u < kTile * 72; u += NT) {
+        const int c = u >> 5, pos = u & 31;
+        if ((pos ^ (4 * (c & 3))) >= valid)
+          *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+
+    wait_vmcnt<0>();
+    load_ids();
+    wait_vmcnt<0>();
+    if (n_run > 0) {
+      // "tile -1" (value product before the first tile) reads stage 3 with
+      // P = 0: both are zero-filled so that it adds exact zeros
+      for (int u = tid; u < kTileBytes / 16; u += NT)
+        *reinterpret_cast<LDS_AS f32x4*>((LDS_AS uint8_t*)s_stage[3] + 16 * u) =
+            f32x4{0.f, 0.f, 0.f, 0.f};
+      s_p[wave][0][lane] = u32x4{0u, 0u, 0u, 0u};
+      s_p[wave][1][lane] = u32x4{0u, 0u, 0u, 0u};
+      issue(0);
+      issue(1);
+    }
+    bf16x8 qf[36];
+    {
+      const uint16_t* qrow = a.q + ((int64_t)b * a.M + (row_ok ? r : 0)) * kDK;
+      const uint32_t sg = a.q_sign2;
+#pragma unroll
+      for (int s = 0; s < 36; ++s) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if (row_ok) z = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hi) ^ sg;
+        qf[s] = __builtin_bit_cast(bf16x8, z);
+      }
+    }
+
+    // iteration it: scores + softmax of tile it (it < n_run), value product
+    // of tile it-1 (it >= 1; "tile -1" adds zeros), tile it+2 streams in
+    for (int it = 0; n_run > 0 && it <= n_run; ++it) {
+      wait_vmcnt<LPW>();          // tile it landed; tile it+1 may be in flight
+      lds_barrier();              // ... and P(it-1), alpha, flags are visible
+      const bool has_s = it < n_run;
+      const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage[it % NST];
+      const LDS_AS uint8_t* sp = (const LDS_AS uint8_t*)s_stage[(it + NST - 1) % NST];
+      const int t0 = (t_begin + it) * kTile;
+      if (has_s && L - t0 < kTile) {     // last tile: zero rows past the end
+        clear_tail((LDS_AS uint8_t*)s_stage[it % NST], L - t0);
+        lds_barrier();
+      }
+      // a row's reference maximum moved at tile it-1: rescale its
+      // accumulators (which then hold tiles up to it-2) in every wave
+      {
+        const int f = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
+        if (__builtin_expect(f != 0 && it >= 2, 0)) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            const float al = s_flag[rb] ? s_alpha[32 * rb + l32] : 1.f;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) acc_scale(o[4 * rb + cb], al);
+          }
+        }
+      }
+      const uint8_t* nsrc = tile_src(it + 2);
+      const uint32_t ndst = lds_addr_of(s_stage[(it + 2) % NST]) + 1024 * wave;
+
+      // ---- interleave: score MFMA k (k < 36) and value MFMA q = k (q < 32);
+      // value step q = (kk, cb, rb) with kk = q / 16, cb = (q / 4) % 4, rb = q % 4
+      f32x16 s;
+      auto rd = [&](int k) { return lds_read_b128(st + 1024 * k + ((k & 1) ? kofs1 : kofs0)); };
+      auto vread = [&](int kk, int cb) {
+        return vt_fragment(sp + vofs0 + 2048 * cb + 256 * kk, sp + vofs1 + 2048 * cb + 256 * kk);
+      };
+      bf16x8 kf[KPF];
+#pragma unroll
+      for (int j = 0; j < KPF; ++j) kf[j] = rd(j);
+      bf16x8 pf[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) pf[rb] = __builtin_bit_cast(bf16x8, s_p[rb][0][lane]);
+      bf16x8 va[2] = {vread(0, 0), vread(0, 1)};
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 36; ++k) {
+        mfma_score(s, kf[k % KPF], qf[k], k == 0);
+        if (k + KPF < 36) kf[k % KPF] = rd(k + KPF);
+        if (k < 32) {
+          const int q = k, kk = q >> 4, cb = (q >> 2) & 3, rb = q & 3;
+          o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb & 1], pf[rb], o[4 * rb + cb], 0, 0, 0);
+          if (rb == 3) {
+            // next V^T operand two column blocks ahead (token half changes at 16)
+            const int nq = q + 5, nkk = nq >> 4, ncb = (nq >> 2) & 3;
+            if (nq < 32) va[cb & 1] = vread(nkk, ncb);
+          }
+          if (q == 15) {
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) pf[r2] = __builtin_bit_cast(bf16x8, s_p[r2][1][lane]);
+          }
+        }
+        if ((k & 3) == 1) dma16_sbase(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      mfma_vgpr_drain(s);
+
+      // ---- online softmax of tile it (own rows)
+      uint32_t pw[8];
+      float alpha = 1.f;
+      bool raise_any = false;
+      if (has_s) {
+        const float c = a.scale_mag_log2;
+        const bool masked = !__all(t0 + kTile <= n_vis);
+        const int lim = n_vis - t0 - 4 * hi;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          x[i] = masked ? ((8 * (i >> 2) + (i & 3) < lim) ? s[i] * c : -INFINITY) : s[i] * c;
+        float lmax = x[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, x[i]);
+        raise_any = __any(lmax > m_run + kRescaleThreshold);
+        if (__builtin_expect(raise_any, 0)) {
+          const float rmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
+          const bool raise = rmax > m_run + kRescaleThreshold;
+          alpha = raise ? __builtin_amdgcn_exp2f(m_run - rmax) : 1.f;
+          l_run *= alpha;
+          if (raise) m_run = rmax;
+        }
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
+          const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
+          psum += p0 + p1;
+          pw[j] = pack_bf16x2(p0, p1);
+        }
+        l_run += psum;
+      }
+      lds_barrier();              // every wave has read P(it-1) and tile it-1
+      if (has_s) {
+        s_p[wave][0][lane] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+        s_p[wave][1][lane] = u32x4{pw[4], pw[5], pw[6], pw[7]};
+        if (raise_any && hi == 0) s_alpha[32 * wave + l32] = alpha;
+      }
+      if (lane == 0) s_flag[wave] = raise_any ? 1 : 0;
+    }
+
+    // ---- epilogue (as in the 128-row kernel): rows staged through the idle
+    // ring so that global stores are whole 256-byte row segments
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    if (bad) lse_v = __builtin_nanf("");
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (hi == 0) s_lsum[32 * wave + l32] = l_tot;
+    lds_barrier();
+    constexpr int kStageRow = 272;
+    uint16_t* dst_base = split ? a.part_o + ((int64_t)slot * a.M) * kDL
+                               : a.out + ((int64_t)b * a.M) * kDL;
+    LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_stage[0] + wave * (64 * kStageRow);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rb = 2 * half + q;
+        const float lt = s_lsum[32 * rb + l32];
+        const float inv_l = bad ? __builtin_nanf("") : (lt > 0.f ? 1.f / lt : 0.f);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& acc = o[4 * rb + cb];
+            const uint32_t w0 = pack_bf16x2(acc[4 * g + 0] * inv_l, acc[4 * g + 1] * inv_l);
+            const uint32_t w1 = pack_bf16x2(acc[4 * g + 2] * inv_l, acc[4 * g + 3] * inv_l);
+            const int col = 32 * cb + 8 * g + 4 * hi;
+            *reinterpret_cast<LDS_AS uint64_t*>(stg + (32 * q + l32) * kStageRow + 2 * col) =
+                (uint64_t)w0 | ((uint64_t)w1 << 32);
+          }
+      }
+      lds_barrier();
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int rl0 = ln >> 4, cl = 8 * (ln & 15);
+      const int row0 = mt * MT + 64 * half;
+      uint16_t* gdst = dst_base + (int64_t)(row0 + rl0) * kDL + cbase + cl;
+      const LDS_AS uint8_t* lsrc = stg + rl0 * kStageRow + 2 * cl;
+      if (row0 + 64 <= a.M) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          *reinterpret_cast<u32x4*>(gdst + 4 * i * kDL) =
+              *reinterpret_cast<const LDS_AS u32x4*>(lsrc + 4 * i * kStageRow);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (row0 + rl0 + 4 * i < a.M)
+            *reinterpret_cast<u32x4*>(gdst + 4 * i * kDL) =
+                *reinterpret_cast<const LDS_AS u32x4*>(lsrc + 4 * i * kStageRow);
+      }
+      lds_barrier();
+    }
+    if (row_ok && hi == 0) {
+      const int64_t row = (int64_t)b * a.M + r;
+      if (!split)
+        a.lse[row] = lse_v;
+      else
+        a.part_lse[(int64_t)slot * a.M + r] = lse_v;
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    pre_b = pre_e;
+  }
+}
+
 // ------------------------------------------------------------ combine
 
 // Merge n (lse, O) parts of one row; one wave, 8 columns per lane.
@@ -1788,6 +2156,11 @@ hipError_t launch_decode(const DecodeParams& dp, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_pipe(const DecodeParams& dp, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_decode_pipe_kernel, dim3(grid), dim3(256), 0, stream, dp);
+  return hipGetLastError();
+}
+
 hipError_t launch_quad(const DecodeParams& dp, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(mla_decode_quad_kernel, dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
@@ -1896,7 +2269,8 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
       case 1: e = launch_rows<1>(dp, grid, stream); break;
       case 2: e = launch_rows<2>(dp, grid, stream); break;
       case 4: e = getenv("MLA_ROWS128") ? launch_rows<4>(dp, grid, stream)
-                                        : launch_quad(dp, grid, stream); break;
+                  : getenv("MLA_QUAD") ? launch_quad(dp, grid, stream)
+                                        : launch_pipe(dp, grid, stream); break;
       default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
     }
   } else {
