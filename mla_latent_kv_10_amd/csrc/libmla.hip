@@ -34,6 +34,7 @@
 
 #include <mutex>
 #include <type_traits>
+#include <utility>
 #include <string>
 
 #include "mla.h"
@@ -211,6 +212,28 @@ __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, ui
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, fully unrolled.
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// As dma16_sbase with constant offsets added to the lane offset (VADD) and
+// to the LDS address (MADD) inside the asm, so that a run of copies shares
+// two base registers instead of one hoisted (and spilled) value per copy.
+template <int VADD, int MADD>
+__device__ __forceinline__ void dma16_sbase_off(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t t;
+  asm volatile("v_add_u32 %0, %5, %1\n\ts_add_u32 m0, %3, %4\n\tglobal_load_lds_dwordx4 %0, %2"
+               : "=&v"(t)
+               : "v"(voff), "s"(sbase), "s"(lds_base), "n"(MADD), "n"(VADD)
                : "memory", "m0");
 }
 
@@ -1530,6 +1553,13 @@ __device__ __forceinline__ void mfma_score(f32x16& acc, const bf16x8& a, const b
   else
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+// max of three floats in one v_max3_f32; the asm also pins the result where
+// it stands (no sinking into later conditional code).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
   // XDL write -> VALU read of the same VGPRs: more than 18 wait states
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
@@ -1552,6 +1582,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   constexpr int NST = 4;                  // ring stages
   constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
   constexpr int KPF = 3;                  // score operands in flight
+  constexpr int NA = 0;                   // value steps interleaved with the score chain
 
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NST][kTileBytes];
   __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];   // P, B-operand layout
@@ -1631,16 +1662,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     const int t_begin = 2 * seg_lo;
     const int t_end = min(2 * seg_hi, (L + kTile - 1) / kTile);
     const int n_tiles = max(0, t_end - t_begin);
-    const CONST_AS int32_t* bt =
-        (const CONST_AS int32_t*)a.block_table + (int64_t)b * a.max_blocks;
-
-    int bad_local = 0;
-    for (int j = seg_lo + tid; j < seg_hi; j += NT) {
-      const int id = bt[j];
-      if (id < 0 || (int64_t)id >= a.num_blocks) bad_local = 1;
-    }
-    const bool bad = __syncthreads_or(bad_local) != 0;
-    const int n_run = bad ? 0 : n_tiles;
+    const int n_run = n_tiles;
     const int n_vis = row_ok ? L - a.s_q + 1 + q_i : 0x7fffffff;
 
     f32x16 o[16];
@@ -1650,12 +1672,22 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       for (int i = 0; i < 16; ++i) o[j][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
+    // Block ids of the segment, 64 at a time, one per lane. Every wave loads
+    // the same window, so the validity flag is uniform over the workgroup.
+    // An id outside [0, num_blocks) poisons the segment (NaN output and lse)
+    // and is replaced by block 0, so that no copy ever leaves the cache.
     const int seg_len = max(0, seg_hi - seg_lo);
     int bt_base = 0;
     int bt_lane = 0;
+    bool bad = false;
     auto load_ids = [&]() {
       const int j = bt_base + min(lane, max(0, seg_len - bt_base - 1));
       bt_lane = seg_len > 0 ? ((const int32_t*)a.block_table)[(int64_t)b * a.max_blocks + seg_lo + j] : 0;
+    };
+    auto check_ids = [&]() {   // after the load has landed
+      const bool inval = bt_lane < 0 || (int64_t)bt_lane >= a.num_blocks;
+      bad = bad || __any(inval && bt_base + lane < seg_len);
+      bt_lane = inval ? 0 : bt_lane;
     };
     auto tile_src = [&](int idx) {
       idx = min(idx, n_run - 1);
@@ -1665,6 +1697,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         rel -= 64;
         load_ids();
         wait_vmcnt<0>();
+        check_ids();
       }
       const int64_t phys = uniform(__builtin_amdgcn_readlane(bt_lane, rel));
       return a.kv + (phys * kBT + ((t_begin + idx) & 1) * kTile) * kRowBytes;
@@ -1683,10 +1716,51 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       }
     };
 
-    wait_vmcnt<0>();
+    // The first block-id window, then the first two tiles (ring stages 0, 1)
+    // and the query rows, all in flight together.
     load_ids();
     wait_vmcnt<0>();
+    check_ids();
+    bf16x8 qf[36];
     if (n_run > 0) {
+      issue(0);
+      issue(1);
+      // Query rows of this wave: load (m, g) reads line m (128 bytes, 8
+      // chunks) of rows 8g..8g+7, so every load reads whole lines. Lane l
+      // takes row 8g + (l & 7) and chunk 8m + ((l >> 3) ^ (g & 1)); rows past
+      // M read row M-1 and are zeroed below. The rows are then put into the
+      // score operand layout through this wave's own 12 KiB of ring stages
+      // 2-3 (idle until the loop starts), three lines at a time: the load's
+      // 16 bytes go to unit 8 (c ^ (g & 1)) + (t & 7) of 1 KiB block 4 m' + g
+      // (m' = m mod 3) for chunk c of the line and row t, which keeps both
+      // the stores and the operand reads free of bank conflicts.
+      const uint16_t* qw = a.q + (int64_t)b * a.M * kDK;
+      const int row0 = mt * MT + 32 * wave;
+      u32x4 raw[36];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint16_t* src = qw + (int64_t)min(row0 + 8 * g + (lane & 7), a.M - 1) * kDK +
+                              8 * ((lane >> 3) ^ (g & 1));
+#pragma unroll
+        for (int m = 0; m < 9; ++m) raw[4 * m + g] = *reinterpret_cast<const u32x4*>(src + 64 * m);
+      }
+      LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_stage[2] + 12288 * wave;
+      const int g = l32 >> 3;
+      const LDS_AS uint8_t* qs = stg + 1024 * g + 128 * (hi ^ (g & 1)) + 16 * (l32 & 7);
+      const uint32_t sg = row_ok ? a.q_sign2 : 0u;
+      const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int rd3 = 0; rd3 < 3; ++rd3) {
+#pragma unroll
+        for (int j = 0; j < 12; ++j)
+          *reinterpret_cast<LDS_AS u32x4*>(stg + 1024 * j + 16 * lane) = raw[12 * rd3 + j];
+#pragma unroll
+        for (int s = 0; s < 12; ++s) {
+          const u32x4 z = *reinterpret_cast<const LDS_AS u32x4*>(qs + 4096 * (s >> 2) + 256 * (s & 3));
+          qf[12 * rd3 + s] = __builtin_bit_cast(bf16x8, (z ^ sg) & keep);
+        }
+      }
+      lds_barrier();   // every wave holds its query rows; stages 2-3 are free
       // "tile -1" (value product before the first tile) reads stage 3 with
       // P = 0: both are zero-filled so that it adds exact zeros
       for (int u = tid; u < kTileBytes / 16; u += NT)
@@ -1694,19 +1768,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
             f32x4{0.f, 0.f, 0.f, 0.f};
       s_p[wave][0][lane] = u32x4{0u, 0u, 0u, 0u};
       s_p[wave][1][lane] = u32x4{0u, 0u, 0u, 0u};
-      issue(0);
-      issue(1);
-    }
-    bf16x8 qf[36];
-    {
-      const uint16_t* qrow = a.q + ((int64_t)b * a.M + (row_ok ? r : 0)) * kDK;
-      const uint32_t sg = a.q_sign2;
+    } else {
 #pragma unroll
-      for (int s = 0; s < 36; ++s) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (row_ok) z = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hi) ^ sg;
-        qf[s] = __builtin_bit_cast(bf16x8, z);
-      }
+      for (int s = 0; s < 36; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
 
     // iteration it: scores + softmax of tile it (it < n_run), value product
@@ -1738,8 +1802,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       const uint8_t* nsrc = tile_src(it + 2);
       const uint32_t ndst = lds_addr_of(s_stage[(it + 2) % NST]) + 1024 * wave;
 
-      // ---- interleave: score MFMA k (k < 36) and value MFMA q = k (q < 32);
-      // value step q = (kk, cb, rb) with kk = q / 16, cb = (q / 4) % 4, rb = q % 4
+      // value step q = (kk, cb, rb) with kk = q / 16, cb = (q / 4) % 4,
+      // rb = q % 4: O^T block (rb, cb) += V^T (column block cb, token half kk)
+      // x P^T (rows of wave rb, token half kk)
       f32x16 s;
       auto rd = [&](int k) { return lds_read_b128(st + 1024 * k + ((k & 1) ? kofs1 : kofs0)); };
       auto vread = [&](int kk, int cb) {
@@ -1752,63 +1817,97 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) pf[rb] = __builtin_bit_cast(bf16x8, s_p[rb][0][lane]);
       bf16x8 va[2] = {vread(0, 0), vread(0, 1)};
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k = 0; k < 36; ++k) {
-        mfma_score(s, kf[k % KPF], qf[k], k == 0);
-        if (k + KPF < 36) kf[k % KPF] = rd(k + KPF);
-        if (k < 32) {
-          const int q = k, kk = q >> 4, cb = (q >> 2) & 3, rb = q & 3;
-          o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb & 1], pf[rb], o[4 * rb + cb], 0, 0, 0);
-          if (rb == 3) {
-            // next V^T operand two column blocks ahead (token half changes at 16)
-            const int nq = q + 5, nkk = nq >> 4, ncb = (nq >> 2) & 3;
-            if (nq < 32) va[cb & 1] = vread(nkk, ncb);
-          }
-          if (q == 15) {
-#pragma unroll
-            for (int r2 = 0; r2 < 4; ++r2) pf[r2] = __builtin_bit_cast(bf16x8, s_p[r2][1][lane]);
-          }
+      auto pv_step = [&](auto qc) {
+        constexpr int q = decltype(qc)::value, cb = (q >> 2) & 3, rb = q & 3;
+        o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb & 1], pf[rb], o[4 * rb + cb], 0, 0, 0);
+        if constexpr (rb == 3 && q + 5 < 32) {
+          // next V^T operand two column blocks ahead (token half changes at 16)
+          constexpr int nq = q + 5;
+          va[cb & 1] = vread(nq >> 4, (nq >> 2) & 3);
         }
-        if ((k & 3) == 1) dma16_sbase(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        if constexpr (q == 15) {
+#pragma unroll
+          for (int r2 = 0; r2 < 4; ++r2) pf[r2] = __builtin_bit_cast(bf16x8, s_p[r2][1][lane]);
+        }
+      };
+      // positions past the visible length (last tile, causal rows) score -inf
+      const bool masked = !__all(t0 + kTile <= n_vis);
+      const int limx = masked ? n_vis - t0 - 4 * hi : kTile;
+      __builtin_amdgcn_sched_barrier(0);
 
+      // ---- phase A: the dependent score chain of tile it (36 MFMAs), the
+      // first NA value steps of tile it-1 and the copy of tile it+2
+      unroll<36>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        mfma_score(s, kf[k % KPF], qf[k], k == 0);
+        if constexpr (k + KPF < 36) kf[k % KPF] = rd(k + KPF);
+        if constexpr (k < NA) pv_step(std::integral_constant<int, k>{});
+        if constexpr ((k & 3) == 1) dma16_sbase(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
+        __builtin_amdgcn_sched_barrier(0);
+      });
       mfma_vgpr_drain(s);
 
-      // ---- online softmax of tile it (own rows)
+      // ---- phase B: the remaining value steps, with the online softmax of
+      // tile it (own rows) cut into short VALU steps between them. It runs on
+      // every iteration and is committed only when tile it exists; the empty
+      // asm statements keep each step's results where the step stands, so
+      // that nothing is sunk into the commit below. The row maximum pairs the
+      // two lane halves with a lane swap; the reference maximum moves only
+      // when it is exceeded by more than the threshold.
+      const float c = a.scale_mag_log2;
+      float x[16];
+      float mx0 = 0.f, mx1 = 0.f, m_new = m_run, alpha = 1.f, neg_m = 0.f, psum = 0.f;
+      bool raise = false;
       uint32_t pw[8];
-      float alpha = 1.f;
-      bool raise_any = false;
-      if (has_s) {
-        const float c = a.scale_mag_log2;
-        const bool masked = !__all(t0 + kTile <= n_vis);
-        const int lim = n_vis - t0 - 4 * hi;
-        float x[16];
+      constexpr int NSM = 13;
+      auto sm_step = [&](auto jc) {
+        constexpr int st = decltype(jc)::value;
+        if constexpr (st < 2) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          x[i] = masked ? ((8 * (i >> 2) + (i & 3) < lim) ? s[i] * c : -INFINITY) : s[i] * c;
-        float lmax = x[0];
+          for (int i = 8 * st; i < 8 * st + 8; ++i) x[i] = s[i] * c;
+          if constexpr (st == 1) {
+            if (masked) {
 #pragma unroll
-        for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, x[i]);
-        raise_any = __any(lmax > m_run + kRescaleThreshold);
-        if (__builtin_expect(raise_any, 0)) {
-          const float rmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
-          const bool raise = rmax > m_run + kRescaleThreshold;
-          alpha = raise ? __builtin_amdgcn_exp2f(m_run - rmax) : 1.f;
-          l_run *= alpha;
-          if (raise) m_run = rmax;
-        }
-        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-        float psum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
+              for (int i = 0; i < 16; ++i) x[i] = 8 * (i >> 2) + (i & 3) < limx ? x[i] : -INFINITY;
+            }
+          }
+        } else if constexpr (st == 2) {
+          mx0 = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], x[4], x[5]), max3f(x[6], x[7], x[7]));
+        } else if constexpr (st == 3) {
+          mx1 = max3f(max3f(x[8], x[9], x[10]), max3f(x[11], x[12], x[13]), max3f(x[14], x[15], x[15]));
+        } else if constexpr (st == 4) {
+          const float lmax = max3f(mx0, mx1, mx1);
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lmax), __float_as_uint(lmax),
+                                                           false, false);
+          const float rmax = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+          raise = rmax > m_run + kRescaleThreshold;
+          m_new = raise ? rmax : m_run;
+          alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+          neg_m = m_new == -INFINITY ? 0.f : -m_new;
+          asm volatile("" : "+v"(m_new), "+v"(alpha), "+v"(neg_m));
+        } else {
+          constexpr int j = st - 5;
           const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
           const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
           psum += p0 + p1;
           pw[j] = pack_bf16x2(p0, p1);
+          asm volatile("" : "+v"(psum), "+v"(pw[j]));
         }
-        l_run += psum;
+      };
+      constexpr int NB = 32 - NA;
+      unroll<NB>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        pv_step(std::integral_constant<int, NA + i>{});
+        unroll<NSM>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if constexpr ((j * NB) / NSM == i) sm_step(jc);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      const bool raise_any = has_s && __any(raise);
+      if (has_s) {
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
       }
       lds_barrier();              // every wave has read P(it-1) and tile it-1
       if (has_s) {
