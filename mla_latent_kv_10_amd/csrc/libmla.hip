@@ -1548,8 +1548,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_quad_kernel(DecodeParams a)
 // SrcC dependency needs no wait states. mfma_vgpr_drain() must follow the
 // last one before VALU code reads the result.
 __device__ __forceinline__ void mfma_score(f32x16& acc, const bf16x8& a, const bf16x8& b, bool first) {
-  if (first)
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "v"(b));
+  if (first)   // early clobber: the result must not share registers with A or B
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
   else
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
@@ -1582,20 +1582,18 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   constexpr int NST = 4;                  // ring stages
   constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
   constexpr int KPF = 3;                  // score operands in flight
-  constexpr int NA = 0;                   // value steps interleaved with the score chain
 
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NST][kTileBytes];
   __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];   // P, B-operand layout
   __shared__ float s_alpha[MT];
-  __shared__ int s_flag[NW];
+  __shared__ __attribute__((aligned(16))) int s_flag[NW];
   // aliases inside ring stage 3, which is idle before the first tile and
   // after the last one
   int* s_pre = reinterpret_cast<int*>(s_stage[3]);                  // [B+1]
   int* s_misc = reinterpret_cast<int*>(s_stage[3] + 4 * (kMaxBatch + 8));
   float* s_lsum = reinterpret_cast<float*>(s_stage[3]);            // epilogue
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
-  const int hi = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6);
 
   int v = blockIdx.x;
   const int G = gridDim.x;
@@ -1633,22 +1631,28 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   int pre_b = b_first <= b_last ? uniform(s_pre[b_first]) : 0;
   __syncthreads();   // ring stage 3 is free from here on
 
-  const int r = mt * MT + 32 * wave + l32;   // row whose scores this lane computes
-  const bool row_ok = r < a.M;
-  const int q_i = row_ok ? r / a.H : 0;
   const int cbase = 128 * wave;              // first output column of this wave
 
-  const int kofs0 = 16 * tile_unit(l32, hi);
-  const int kofs1 = 16 * tile_unit(l32, 2 + hi) - 1024;
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
-  const int vc = cbase / 8 + 2 * (g16 & 1) + (vq >> 1);
-  const int vofs0 = 16 * tile_unit(4 * vh + vs, vc) + 8 * (vq & 1);
-  const int vofs1 = 16 * tile_unit(8 + 4 * vh + vs, vc) + 8 * (vq & 1);
-  const int dchunk = 2 * wave + hi;
-  const uint32_t doff = (uint32_t)((l32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
-
   for (int b = b_first; b <= b_last; ++b) {
+    // Per-lane constants are derived here, from a lane index the compiler
+    // cannot see through, so that they are not hoisted out of the sequence
+    // loop and kept (spilled) across it.
+    int tid_s = tid;
+    asm volatile("" : "+v"(tid_s));
+    const int lane = tid_s & 63, hi = lane >> 5, l32 = lane & 31;
+    const int r = mt * MT + 32 * wave + l32;   // row whose scores this lane computes
+    const bool row_ok = r < a.M;
+    const int q_i = row_ok ? r / a.H : 0;
+    const int kofs0 = 16 * tile_unit(l32, hi);
+    const int kofs1 = 16 * tile_unit(l32, 2 + hi) - 1024;
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
+    const int vc = cbase / 8 + 2 * (g16 & 1) + (vq >> 1);
+    const int vofs0 = 16 * tile_unit(4 * vh + vs, vc) + 8 * (vq & 1);
+    const int vofs1 = 16 * tile_unit(8 + 4 * vh + vs, vc) + 8 * (vq & 1);
+    const int dchunk = 2 * wave + hi;
+    const uint32_t doff = (uint32_t)((l32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
+
     const int L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
     const int pre_e = pre_b + (L + kBT - 1) / kBT;
     const int seg_lo = max(p_lo, pre_b) - pre_b, seg_hi = min(p_hi, pre_e) - pre_b;
@@ -1666,10 +1670,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     const int n_vis = row_ok ? L - a.s_q + 1 + q_i : 0x7fffffff;
 
     f32x16 o[16];
+    float zero = 0.f;
+    asm volatile("" : "+v"(zero));   // no kernel-wide zero vector to keep alive
 #pragma unroll
     for (int j = 0; j < 16; ++j)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[j][i] = 0.f;
+      for (int i = 0; i < 16; ++i) o[j][i] = zero;
     float m_run = -INFINITY, l_run = 0.f;
 
     // Block ids of the segment, 64 at a time, one per lane. Every wave loads
@@ -1786,19 +1792,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         clear_tail((LDS_AS uint8_t*)s_stage[it % NST], L - t0);
         lds_barrier();
       }
-      // a row's reference maximum moved at tile it-1: rescale its
-      // accumulators (which then hold tiles up to it-2) in every wave
-      {
-        const int f = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
-        if (__builtin_expect(f != 0 && it >= 2, 0)) {
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            const float al = s_flag[rb] ? s_alpha[32 * rb + l32] : 1.f;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) acc_scale(o[4 * rb + cb], al);
-          }
-        }
-      }
+      // rescale requests of tile it-1, read now and acted on after phase A
+      const u32x4 flg = *reinterpret_cast<const u32x4*>(s_flag);
       const uint8_t* nsrc = tile_src(it + 2);
       const uint32_t ndst = lds_addr_of(s_stage[(it + 2) % NST]) + 1024 * wave;
 
@@ -1813,10 +1808,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       bf16x8 kf[KPF];
 #pragma unroll
       for (int j = 0; j < KPF; ++j) kf[j] = rd(j);
-      bf16x8 pf[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) pf[rb] = __builtin_bit_cast(bf16x8, s_p[rb][0][lane]);
-      bf16x8 va[2] = {vread(0, 0), vread(0, 1)};
+      bf16x8 pf[4], va[2];   // value operands, loaded in phase A's last third
       auto pv_step = [&](auto qc) {
         constexpr int q = decltype(qc)::value, cb = (q >> 2) & 3, rb = q & 3;
         o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb & 1], pf[rb], o[4 * rb + cb], 0, 0, 0);
@@ -1825,27 +1817,43 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
           constexpr int nq = q + 5;
           va[cb & 1] = vread(nq >> 4, (nq >> 2) & 3);
         }
-        if constexpr (q == 15) {
-#pragma unroll
-          for (int r2 = 0; r2 < 4; ++r2) pf[r2] = __builtin_bit_cast(bf16x8, s_p[r2][1][lane]);
-        }
+        // P^T of the second token half: each row block right after its last
+        // use in the first half, four steps ahead of its first use
+        if constexpr (q >= 12 && q < 16) pf[rb] = __builtin_bit_cast(bf16x8, s_p[rb][1][lane]);
       };
       // positions past the visible length (last tile, causal rows) score -inf
       const bool masked = !__all(t0 + kTile <= n_vis);
       const int limx = masked ? n_vis - t0 - 4 * hi : kTile;
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- phase A: the dependent score chain of tile it (36 MFMAs), the
-      // first NA value steps of tile it-1 and the copy of tile it+2
+      // ---- phase A: the dependent score chain of tile it (36 MFMAs) and the
+      // copy of tile it+2; in its last third the first value operands of
+      // tile it-1 are read
       unroll<36>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         mfma_score(s, kf[k % KPF], qf[k], k == 0);
         if constexpr (k + KPF < 36) kf[k % KPF] = rd(k + KPF);
-        if constexpr (k < NA) pv_step(std::integral_constant<int, k>{});
+        if constexpr (k >= 24 && k < 28) pf[k - 24] = __builtin_bit_cast(bf16x8, s_p[k - 24][0][lane]);
+        if constexpr (k == 29) va[0] = vread(0, 0);
+        if constexpr (k == 31) va[1] = vread(0, 1);
         if constexpr ((k & 3) == 1) dma16_sbase(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
         __builtin_amdgcn_sched_barrier(0);
       });
       mfma_vgpr_drain(s);
+
+      // a row's reference maximum moved at tile it-1: rescale its
+      // accumulators (which then hold tiles up to it-2) in every wave before
+      // the value product of tile it-1 adds to them
+      u32x4 flags = flg;
+      asm volatile("" : "+v"(flags));   // keeps the read's wait out of phase A
+      if (__builtin_expect((flags[0] | flags[1] | flags[2] | flags[3]) != 0 && it >= 2, 0)) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const float al = flags[rb] ? s_alpha[32 * rb + l32] : 1.f;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) acc_scale(o[4 * rb + cb], al);
+        }
+      }
 
       // ---- phase B: the remaining value steps, with the online softmax of
       // tile it (own rows) cut into short VALU steps between them. It runs on
@@ -1894,10 +1902,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
           asm volatile("" : "+v"(psum), "+v"(pw[j]));
         }
       };
-      constexpr int NB = 32 - NA;
+      constexpr int NB = 32;
       unroll<NB>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        pv_step(std::integral_constant<int, NA + i>{});
+        pv_step(ic);
         unroll<NSM>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
           if constexpr ((j * NB) / NSM == i) sm_step(jc);
