@@ -2040,26 +2040,10 @@ __device__ __forceinline__ void merge_row(int n, PartPtr part, uint16_t* out_row
   if (lane == 0) *lse_out = L;
 }
 
-struct SplitParts {   // parts of a split sequence inside the decode workspace (bf16)
-  const uint16_t* part_o;
-  const float* part_lse;
-  int M, r, first, pre_b, P, T;
-  __device__ int slot(int s) const {
-    const int p = first + s;
-    return 2 * p + ((s == 0 && pre_b > part_start(p, P, T)) ? 1 : 0);
-  }
-  __device__ const float* lse(int s) const { return part_lse + (int64_t)slot(s) * M + r; }
-  __device__ void o8(int s, int lane, float x[8]) const {
-    const uint4 v = *reinterpret_cast<const uint4*>(part_o + ((int64_t)slot(s) * M + r) * kDL + 8 * lane);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = __builtin_bit_cast(float, w[e] << 16);
-      x[2 * e + 1] = __builtin_bit_cast(float, w[e] & 0xffff0000u);
-    }
-  }
-};
-
+// Merge the parts of one split row (one wave per row, 8 columns per lane).
+// Every part's lse is loaded at once, one part per lane; the parts' value
+// rows are then read eight at a time, all eight loads in flight together,
+// and weighted by w_s = exp(lse_s - L) with L the merged lse.
 __global__ __launch_bounds__(kThreads) void mla_split_combine_kernel(DecodeParams a) {
   const int b = blockIdx.x;
   const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -2068,9 +2052,81 @@ __global__ __launch_bounds__(kThreads) void mla_split_combine_kernel(DecodeParam
   if (pre_e <= pre_b) return;
   const int fp = part_of(pre_b, a.P, T), lp = part_of(pre_e - 1, a.P, T);
   if (lp == fp) return;
-  SplitParts parts{a.part_o, a.part_lse, a.M, r, fp, pre_b, a.P, T};
+  const int n = lp - fp + 1;
+  const int lane = threadIdx.x & 63;
+  const bool first_shifted = pre_b > part_start(fp, a.P, T);
+  auto slot = [&](int s) { return 2 * (fp + s) + ((s == 0 && first_shifted) ? 1 : 0); };
   const int64_t row = (int64_t)b * a.M + r;
-  merge_row(lp - fp + 1, parts, a.out + row * kDL, a.lse + row);
+  uint16_t* out_row = a.out + row * kDL;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  // max (and NaN) over the parts' lse
+  float m = -INFINITY;
+  bool has_nan = false;
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int s = s0 + lane;
+    const float l = s < n ? a.part_lse[(int64_t)slot(s) * a.M + r] : -INFINITY;
+    has_nan |= isnan(l);
+    m = fmaxf(m, l);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  has_nan = __any(has_nan);
+  if (has_nan || m == -INFINITY) {
+    const float fill = has_nan ? __builtin_nanf("") : 0.f;
+    const uint32_t h = f32_to_bf16_bits(fill);
+    const uint32_t w = h | (h << 16);
+    *reinterpret_cast<uint4*>(out_row + 8 * lane) = uint4{w, w, w, w};
+    if (lane == 0) a.lse[row] = has_nan ? __builtin_nanf("") : -INFINITY;
+    return;
+  }
+  // merged lse
+  float tot = 0.f;
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int s = s0 + lane;
+    if (s < n) tot += __builtin_amdgcn_exp2f((a.part_lse[(int64_t)slot(s) * a.M + r] - m) * kLog2e);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+  const float L = m + __log2f(tot) * 0.69314718055994531f;
+
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int nr = min(64, n - s0);
+    // this round's weights, part s0 + i in lane i
+    const float wl = lane < nr
+        ? __builtin_amdgcn_exp2f((a.part_lse[(int64_t)slot(s0 + lane) * a.M + r] - L) * kLog2e)
+        : 0.f;
+    for (int c0 = 0; c0 < nr; c0 += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + j < nr)
+          v[j] = *reinterpret_cast<const uint4*>(
+              a.part_o + ((int64_t)slot(s0 + c0 + j) * a.M + r) * kDL + 8 * lane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (c0 + j < nr) {
+          const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), c0 + j));
+          const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += w * __builtin_bit_cast(float, u[e] << 16);
+            acc[2 * e + 1] += w * __builtin_bit_cast(float, u[e] & 0xffff0000u);
+          }
+        }
+      }
+    }
+  }
+  uint4 pk;
+  pk.x = f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+  pk.y = f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+  pk.z = f32_to_bf16_bits(acc[4]) | ((uint32_t)f32_to_bf16_bits(acc[5]) << 16);
+  pk.w = f32_to_bf16_bits(acc[6]) | ((uint32_t)f32_to_bf16_bits(acc[7]) << 16);
+  *reinterpret_cast<uint4*>(out_row + 8 * lane) = pk;
+  if (lane == 0) a.lse[row] = L;
 }
 
 struct DenseParts {   // caller-provided partials [S, R, 512] / [S, R]

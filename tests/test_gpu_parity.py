@@ -206,6 +206,42 @@ def test_repeat_runs_are_bit_identical():
     assert np.array_equal(bits1, bits2) and np.array_equal(lse1, lse2)
 
 
+def test_graph_replay_matches_eager():
+    """A decode step captured in a HIP graph (split plan + decode + combine,
+    the way the benchmark replays it) gives the eager result bit for bit on
+    every replay, with eager work and synchronisations between replays."""
+    w = wl.make_workload("graph", 4, 1, 128, [700, 1300, 64, 2100], seed=21, table="permuted")
+    t = device_inputs(w)
+    out = torch.empty((w.B, w.s_q, w.H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.s_q, w.H), dtype=torch.float32, device="cuda")
+    prob = mla.make_problem(t["q"], t["kv"], t["bt"], kv_dtype=mla.KV_BF16, max_seqlen=w.max_seqlen,
+                            num_parts=16)
+    ws = torch.empty(max(16, mla.workspace_size(prob)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        mla.mla_decode(t["q"], t["kv"], t["bt"], t["sl"], w.softmax_scale, out, lse,
+                       max_seqlen=w.max_seqlen, num_parts=16, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+    ref_lse = lse.clone()
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), *oracle_rows(w), what="graph eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        out.fill_(0)
+        lse.fill_(0)
+        other = run_gpu(w, t, num_parts=3)      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"replay {rep}: out"
+        assert torch.equal(lse, ref_lse), f"replay {rep}: lse"
+        del other
+
+
 def test_absorbed_query_end_to_end():
     """Feed bf16(q~) built from random W_UK to the GPU; W_UV applied to its
     latent output must match the decompressed per-head definition."""
