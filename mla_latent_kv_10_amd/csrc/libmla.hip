@@ -1779,19 +1779,30 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       for (int s = 0; s < 36; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
 
-    // iteration it: scores + softmax of tile it (it < n_run), value product
-    // of tile it-1 (it >= 1; "tile -1" adds zeros), tile it+2 streams in
+    // Iteration it: scores and softmax of tile it (it < n_run), value product
+    // of tile it-1 (it >= 1; "tile -1" adds zeros); tile it+2 streams in.
+    // The first score operands of tile it are read at the end of iteration
+    // it-1, before the barrier that publishes P(it-1), so that their LDS
+    // latency is not exposed at the start of the score chain.
+    bf16x8 kf[KPF];
+    auto rd_at = [&](int t, int k) {
+      return lds_read_b128((const LDS_AS uint8_t*)s_stage[t % NST] + 1024 * k + ((k & 1) ? kofs1 : kofs0));
+    };
+    if (n_run > 0) {
+      wait_vmcnt<LPW>();          // tile 0 landed; tile 1 may be in flight
+      lds_barrier();              // ... in every wave's part; stage 3 and P zeroed
+#pragma unroll
+      for (int j2 = 0; j2 < KPF; ++j2) kf[j2] = rd_at(0, j2);
+    }
     for (int it = 0; n_run > 0 && it <= n_run; ++it) {
-      wait_vmcnt<LPW>();          // tile it landed; tile it+1 may be in flight
-      lds_barrier();              // ... and P(it-1), alpha, flags are visible
+      // P(it-1), alpha and flags of every wave are visible: their writes were
+      // issued before the KPF score reads now in flight, and LDS operations
+      // of a wave complete in order
+      if (it > 0) asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KPF) : "memory");
       const bool has_s = it < n_run;
       const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage[it % NST];
       const LDS_AS uint8_t* sp = (const LDS_AS uint8_t*)s_stage[(it + NST - 1) % NST];
       const int t0 = (t_begin + it) * kTile;
-      if (has_s && L - t0 < kTile) {     // last tile: zero rows past the end
-        clear_tail((LDS_AS uint8_t*)s_stage[it % NST], L - t0);
-        lds_barrier();
-      }
       // rescale requests of tile it-1, read now and acted on after phase A
       const u32x4 flg = *reinterpret_cast<const u32x4*>(s_flag);
       const uint8_t* nsrc = tile_src(it + 2);
@@ -1805,9 +1816,6 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       auto vread = [&](int kk, int cb) {
         return vt_fragment(sp + vofs0 + 2048 * cb + 256 * kk, sp + vofs1 + 2048 * cb + 256 * kk);
       };
-      bf16x8 kf[KPF];
-#pragma unroll
-      for (int j = 0; j < KPF; ++j) kf[j] = rd(j);
       bf16x8 pf[4], va[2];   // value operands, loaded in phase A's last third
       auto pv_step = [&](auto qc) {
         constexpr int q = decltype(qc)::value, cb = (q >> 2) & 3, rb = q & 3;
@@ -1821,7 +1829,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         // use in the first half, four steps ahead of its first use
         if constexpr (q >= 12 && q < 16) pf[rb] = __builtin_bit_cast(bf16x8, s_p[rb][1][lane]);
       };
-      // positions past the visible length (last tile, causal rows) score -inf
+      // positions past the visible length (last tile, causal rows) score -inf;
+      // in the last tile they may hold anything (their rows are zeroed only
+      // after this tile's scores), the mask replaces whatever they score
       const bool masked = !__all(t0 + kTile <= n_vis);
       const int limx = masked ? n_vis - t0 - 4 * hi : kTile;
       __builtin_amdgcn_sched_barrier(0);
@@ -1855,51 +1865,69 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         }
       }
 
-      // ---- phase B: the remaining value steps, with the online softmax of
-      // tile it (own rows) cut into short VALU steps between them. It runs on
-      // every iteration and is committed only when tile it exists; the empty
-      // asm statements keep each step's results where the step stands, so
-      // that nothing is sunk into the commit below. The row maximum pairs the
-      // two lane halves with a lane swap; the reference maximum moves only
-      // when it is exceeded by more than the threshold.
+      // ---- phase B: the value steps of tile it-1, with the online softmax of
+      // tile it (own rows) cut into 28 short VALU steps between them (at most
+      // about four VALU instructions and one exponential each, which is what
+      // the shadow of one MFMA holds). It runs on every iteration and is
+      // committed only when tile it exists; the empty asm statements keep each
+      // step's results where the step stands, so that nothing is sunk into
+      // the commit below. The row maximum pairs the two lane halves with a
+      // lane swap; the reference maximum moves only when it is exceeded by
+      // more than the threshold.
       const float c = a.scale_mag_log2;
       float x[16];
-      float mx0 = 0.f, mx1 = 0.f, m_new = m_run, alpha = 1.f, neg_m = 0.f, psum = 0.f;
+      float m01 = 0.f, m02 = 0.f, m03 = 0.f, m04 = 0.f, m05 = 0.f, m06 = 0.f, lmax = 0.f, rmax = 0.f;
+      float m_new = m_run, alpha = 1.f, neg_m = 0.f, psum = 0.f, pprev = 0.f;
       bool raise = false;
       uint32_t pw[8];
-      constexpr int NSM = 13;
+      constexpr int NSM = 28;
       auto sm_step = [&](auto jc) {
-        constexpr int st = decltype(jc)::value;
-        if constexpr (st < 2) {
+        constexpr int st_ = decltype(jc)::value;
+        if constexpr (st_ < 4) {
 #pragma unroll
-          for (int i = 8 * st; i < 8 * st + 8; ++i) x[i] = s[i] * c;
-          if constexpr (st == 1) {
+          for (int i2 = 4 * st_; i2 < 4 * st_ + 4; ++i2) x[i2] = s[i2] * c;
+          if constexpr (st_ == 3) {
             if (masked) {
 #pragma unroll
-              for (int i = 0; i < 16; ++i) x[i] = 8 * (i >> 2) + (i & 3) < limx ? x[i] : -INFINITY;
+              for (int i2 = 0; i2 < 16; ++i2) x[i2] = 8 * (i2 >> 2) + (i2 & 3) < limx ? x[i2] : -INFINITY;
             }
           }
-        } else if constexpr (st == 2) {
-          mx0 = max3f(max3f(x[0], x[1], x[2]), max3f(x[3], x[4], x[5]), max3f(x[6], x[7], x[7]));
-        } else if constexpr (st == 3) {
-          mx1 = max3f(max3f(x[8], x[9], x[10]), max3f(x[11], x[12], x[13]), max3f(x[14], x[15], x[15]));
-        } else if constexpr (st == 4) {
-          const float lmax = max3f(mx0, mx1, mx1);
+        } else if constexpr (st_ == 4) {
+          m01 = max3f(x[0], x[1], x[2]);
+          m02 = max3f(x[3], x[4], x[5]);
+        } else if constexpr (st_ == 5) {
+          m03 = max3f(x[6], x[7], x[8]);
+          m04 = max3f(x[9], x[10], x[11]);
+        } else if constexpr (st_ == 6) {
+          m05 = max3f(x[12], x[13], x[14]);
+          m06 = max3f(x[15], m01, m02);
+        } else if constexpr (st_ == 7) {
+          lmax = max3f(max3f(m03, m04, m05), m06, m06);
+        } else if constexpr (st_ == 8) {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lmax), __float_as_uint(lmax),
                                                            false, false);
-          const float rmax = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+          rmax = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
+        } else if constexpr (st_ == 9) {
           raise = rmax > m_run + kRescaleThreshold;
           m_new = raise ? rmax : m_run;
+          asm volatile("" : "+v"(m_new));
+        } else if constexpr (st_ == 10) {
           alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+          asm volatile("" : "+v"(alpha));
+        } else if constexpr (st_ == 11) {
           neg_m = m_new == -INFINITY ? 0.f : -m_new;
-          asm volatile("" : "+v"(m_new), "+v"(alpha), "+v"(neg_m));
+          asm volatile("" : "+v"(neg_m));
         } else {
-          constexpr int j = st - 5;
-          const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
-          const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
-          psum += p0 + p1;
-          pw[j] = pack_bf16x2(p0, p1);
-          asm volatile("" : "+v"(psum), "+v"(pw[j]));
+          constexpr int j2 = st_ - 12;
+          const float p = __builtin_amdgcn_exp2f(x[j2] + neg_m);
+          psum += p;
+          if constexpr (j2 & 1) {
+            pw[j2 >> 1] = pack_bf16x2(pprev, p);
+            asm volatile("" : "+v"(psum), "+v"(pw[j2 >> 1]));
+          } else {
+            pprev = p;
+            asm volatile("" : "+v"(psum), "+v"(pprev));
+          }
         }
       };
       constexpr int NB = 32;
@@ -1907,8 +1935,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         constexpr int i = decltype(ic)::value;
         pv_step(ic);
         unroll<NSM>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          if constexpr ((j * NB) / NSM == i) sm_step(jc);
+          constexpr int j2 = decltype(jc)::value;
+          if constexpr (1 + j2 == i) sm_step(jc);
         });
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -1916,14 +1944,20 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       if (has_s) {
         l_run = l_run * alpha + psum;
         m_run = m_new;
+        // last tile: zero rows past the end; its V serves the next iteration
+        if (L - t0 < kTile) clear_tail((LDS_AS uint8_t*)s_stage[it % NST], L - t0);
       }
-      lds_barrier();              // every wave has read P(it-1) and tile it-1
+      wait_vmcnt<LPW>();          // tile it+1 landed (this wave's part); tile it+2 in flight
+      lds_barrier();              // every wave has read P(it-1) and tile it-1; tile it+1 visible
       if (has_s) {
         s_p[wave][0][lane] = u32x4{pw[0], pw[1], pw[2], pw[3]};
         s_p[wave][1][lane] = u32x4{pw[4], pw[5], pw[6], pw[7]};
         if (raise_any && hi == 0) s_alpha[32 * wave + l32] = alpha;
       }
       if (lane == 0) s_flag[wave] = raise_any ? 1 : 0;
+      asm volatile("" ::: "memory");   // the writes above are issued before the reads below
+#pragma unroll
+      for (int j2 = 0; j2 < KPF; ++j2) kf[j2] = rd_at(it + 1, j2);
     }
 
     // ---- epilogue (as in the 128-row kernel): rows staged through the idle
