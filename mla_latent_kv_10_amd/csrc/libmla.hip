@@ -1722,51 +1722,55 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       }
     };
 
-    // The first block-id window, then the first two tiles (ring stages 0, 1)
-    // and the query rows, all in flight together.
+    // The first block-id window, the query rows, then the first two tiles
+    // (ring stages 0, 1).
     load_ids();
     wait_vmcnt<0>();
     check_ids();
     bf16x8 qf[36];
     if (n_run > 0) {
-      issue(0);
-      issue(1);
-      // Query rows of this wave: load (m, g) reads line m (128 bytes, 8
-      // chunks) of rows 8g..8g+7, so every load reads whole lines. Lane l
-      // takes row 8g + (l & 7) and chunk 8m + ((l >> 3) ^ (g & 1)); rows past
-      // M read row M-1 and are zeroed below. The rows are then put into the
-      // score operand layout through this wave's own 12 KiB of ring stages
-      // 2-3 (idle until the loop starts), three lines at a time: the load's
-      // 16 bytes go to unit 8 (c ^ (g & 1)) + (t & 7) of 1 KiB block 4 m' + g
-      // (m' = m mod 3) for chunk c of the line and row t, which keeps both
-      // the stores and the operand reads free of bank conflicts.
-      const uint16_t* qw = a.q + (int64_t)b * a.M * kDK;
+      // Query rows of this wave: its 32 consecutive rows are one contiguous
+      // 36 KiB block, read as 36 contiguous KiB (lane l of load j takes the
+      // 16-byte chunk 64 j + l: row t = (64 j + l) / 72, chunk c = that mod
+      // 72), which the memory path serves much faster than loads spread over
+      // rows. Rows past M read row M-1 and are zeroed after the read. Each
+      // chunk is stored into the K-tile layout (unit 32 c + (t ^ 4 (c & 3)))
+      // of ring stage w (the ring is idle until the first tiles are issued)
+      // and read back in the score operand layout with the conflict-free
+      // fragment reads used for the K tiles.
+      const uint8_t* qblk = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * a.M * kDK);
       const int row0 = mt * MT + 32 * wave;
+      const int rmax = a.M - 1 - row0;          // last valid row of the block
       u32x4 raw[36];
+      {
+        int t = 0, c = lane;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint16_t* src = qw + (int64_t)min(row0 + 8 * g + (lane & 7), a.M - 1) * kDK +
-                              8 * ((lane >> 3) ^ (g & 1));
-#pragma unroll
-        for (int m = 0; m < 9; ++m) raw[4 * m + g] = *reinterpret_cast<const u32x4*>(src + 64 * m);
-      }
-      LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_stage[2] + 12288 * wave;
-      const int g = l32 >> 3;
-      const LDS_AS uint8_t* qs = stg + 1024 * g + 128 * (hi ^ (g & 1)) + 16 * (l32 & 7);
-      const uint32_t sg = row_ok ? a.q_sign2 : 0u;
-      const uint32_t keep = row_ok ? 0xffffffffu : 0u;
-#pragma unroll
-      for (int rd3 = 0; rd3 < 3; ++rd3) {
-#pragma unroll
-        for (int j = 0; j < 12; ++j)
-          *reinterpret_cast<LDS_AS u32x4*>(stg + 1024 * j + 16 * lane) = raw[12 * rd3 + j];
-#pragma unroll
-        for (int s = 0; s < 12; ++s) {
-          const u32x4 z = *reinterpret_cast<const LDS_AS u32x4*>(qs + 4096 * (s >> 2) + 256 * (s & 3));
-          qf[12 * rd3 + s] = __builtin_bit_cast(bf16x8, (z ^ sg) & keep);
+        for (int j = 0; j < 36; ++j) {
+          raw[j] = *reinterpret_cast<const u32x4*>(qblk + (int64_t)(row0 + min(t, rmax)) * kRowBytes + 16 * c);
+          c += 64;
+          if (c >= 72) { c -= 72; ++t; }
         }
       }
-      lds_barrier();   // every wave holds its query rows; stages 2-3 are free
+      {
+        LDS_AS uint8_t* stq = (LDS_AS uint8_t*)s_stage[wave];
+        int t = 0, c = lane;
+#pragma unroll
+        for (int j = 0; j < 36; ++j) {
+          *reinterpret_cast<LDS_AS u32x4*>(stq + 16 * (32 * c + (t ^ (4 * (c & 3))))) = raw[j];
+          c += 64;
+          if (c >= 72) { c -= 72; ++t; }
+        }
+        const uint32_t sg = row_ok ? a.q_sign2 : 0u;
+        const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int s2 = 0; s2 < 36; ++s2) {
+          const u32x4 z = __builtin_bit_cast(u32x4, lds_read_b128(stq + 1024 * s2 + ((s2 & 1) ? kofs1 : kofs0)));
+          qf[s2] = __builtin_bit_cast(bf16x8, (z ^ sg) & keep);
+        }
+      }
+      lds_barrier();   // every wave holds its query rows; the ring is free
+      issue(0);
+      issue(1);
       // "tile -1" (value product before the first tile) reads stage 3 with
       // P = 0: both are zero-filled so that it adds exact zeros
       for (int u = tid; u < kTileBytes / 16; u += NT)
