@@ -201,10 +201,14 @@ __device__ void plan_prefix(const int32_t* __restrict__ seqlens, int B, int max_
 
 // Rescale threshold of the online softmax (log2 units). The reference
 // maximum used for the exponentials only moves when a tile's scores exceed
-// it by more than this, so probabilities stay below 2^8 and the output
-// accumulators are rescaled rarely (in practice on a segment's first tile).
-// The result is the same softmax; only the reference point changes.
-constexpr float kRescaleThreshold = 8.0f;
+// it by more than this, so the output accumulators are rescaled rarely (in
+// practice on a segment's first tile, even with heavy-tailed scores). The
+// probabilities then stay below 2^48: bf16 keeps the fp32 exponent range and
+// rounds relatively, and the fp32 sums over at most 2^21 tokens stay finite
+// for cache values below 5e17; an exponent that underflows would underflow
+// against the true maximum as well. The result is the same softmax; only the
+// reference point changes.
+constexpr float kRescaleThreshold = 48.0f;
 
 // LDS-DMA with an SGPR base and a per-lane 32-bit offset (no per-tile
 // address arithmetic); lane l's 16 bytes land at lds_addr + 16 l.
@@ -1863,9 +1867,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       if (__builtin_expect((flags[0] | flags[1] | flags[2] | flags[3]) != 0 && it >= 2, 0)) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-          const float al = flags[rb] ? s_alpha[32 * rb + l32] : 1.f;
+          if (flags[rb]) {           // only the row blocks whose maximum moved
+            const float al = s_alpha[32 * rb + l32];
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc_scale(o[4 * rb + cb], al);
+            for (int cb = 0; cb < 4; ++cb) acc_scale(o[4 * rb + cb], al);
+          }
         }
       }
 
