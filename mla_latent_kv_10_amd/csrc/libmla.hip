@@ -201,14 +201,18 @@ __device__ void plan_prefix(const int32_t* __restrict__ seqlens, int B, int max_
 
 // Rescale threshold of the online softmax (log2 units). The reference
 // maximum used for the exponentials only moves when a tile's scores exceed
-// it by more than this, so the output accumulators are rescaled rarely (in
-// practice on a segment's first tile, even with heavy-tailed scores). The
-// probabilities then stay below 2^48: bf16 keeps the fp32 exponent range and
-// rounds relatively, and the fp32 sums over at most 2^21 tokens stay finite
-// for cache values below 5e17; an exponent that underflows would underflow
-// against the true maximum as well. The result is the same softmax; only the
+// it by more than this, and when it moves it is set kRefHeadroom above the
+// new row maximum, so a later score has to exceed that maximum by 96 before
+// the output accumulators are rescaled again: in practice only a segment's
+// first tile sets it, even with heavy-tailed scores. The probabilities stay
+// below 2^48: bf16 keeps the fp32 exponent range and rounds relatively, and
+// the fp32 sums over at most 2^21 tokens stay finite for cache values below
+// 5e17. A score 78 or more below the row maximum may underflow to zero; its
+// weight relative to the maximum's is then below 2^-78, far under the bf16
+// rounding of the probabilities. The result is the same softmax; only the
 // reference point changes.
 constexpr float kRescaleThreshold = 48.0f;
+constexpr float kRefHeadroom = 48.0f;
 
 // LDS-DMA with an SGPR base and a per-lane 32-bit offset (no per-tile
 // address arithmetic); lane l's 16 bytes land at lds_addr + 16 l.
@@ -657,8 +661,9 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
           const bool raise = tmax > m_run + kRescaleThreshold ||
                              (m_run == -INFINITY && tmax > -INFINITY);
           if (__any(raise)) {
-            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.f;
-            if (raise) m_run = tmax;
+            const float m_new = tmax + kRefHeadroom;
+            const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+            if (raise) m_run = m_new;
             l_run *= alpha;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
@@ -675,8 +680,9 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
         tmax = smax;
         if (__builtin_expect(__any(raise_lane), 0)) {
           const bool raise = raise_lane;
-          const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.f;
-          if (raise) m_run = tmax;
+          const float m_new = tmax + kRefHeadroom;
+          const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+          if (raise) m_run = m_new;
           l_run *= alpha;
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct)
@@ -1093,13 +1099,14 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
         // on it, the accumulators are rescaled, the probabilities redone
         const float rmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
         const bool raise = rmax > m_run + kRescaleThreshold;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - rmax) : 1.f;
+        const float m_new = rmax + kRefHeadroom;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         if (__any(raise && m_run != -INFINITY)) {
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) acc_scale(o[ct], alpha);
         }
         l_run *= alpha;
-        if (raise) m_run = rmax;
+        if (raise) m_run = m_new;
         const float neg_m2 = m_run == -INFINITY ? 0.f : -m_run;
         psum = 0.f;
 #pragma unroll
@@ -1416,9 +1423,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_quad_kernel(DecodeParams a)
       if (__builtin_expect(raise_any, 0)) {
         const float rmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
         const bool raise = rmax > m_run + kRescaleThreshold;
-        alpha = raise ? __builtin_amdgcn_exp2f(m_run - rmax) : 1.f;
+        const float m_new = rmax + kRefHeadroom;
+        alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         l_run *= alpha;
-        if (raise) m_run = rmax;
+        if (raise) m_run = m_new;
       }
       const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
       float psum = 0.f;
@@ -1919,7 +1927,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
           rmax = max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), __uint_as_float(sw[1]));
         } else if constexpr (st_ == 9) {
           raise = rmax > m_run + kRescaleThreshold;
-          m_new = raise ? rmax : m_run;
+          m_new = raise ? rmax + kRefHeadroom : m_run;
           asm volatile("" : "+v"(m_new));
         } else if constexpr (st_ == 10) {
           alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
