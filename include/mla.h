@@ -98,8 +98,10 @@ typedef struct {
                                  not depend on it. */
   int32_t kv_dtype;           /* mla_kv_dtype */
   int32_t num_parts;          /* 0: automatic; else P >= 1 KV partitions (see mla_plan) */
-  int32_t m_tile;             /* 0: automatic; else 32, 64 or 128 query rows
-                                 per workgroup (128: bf16 cache only) */
+  int32_t m_tile;             /* 0: automatic; else 16, 32, 64 or 128 query rows
+                                 per workgroup (16 and 128: bf16 cache only).
+                                 Automatic picks 16 for a bf16 cache with
+                                 seqlen_q * num_heads <= 16. */
 } mla_problem;
 
 /* Bytes of device workspace mla_decode needs for *p (written to *bytes, host).

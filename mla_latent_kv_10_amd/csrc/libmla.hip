@@ -1192,6 +1192,354 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
   }
 }
 
+// ------------------------------------------- bf16 decode kernel (16-row tile)
+
+// For at most 16 query rows per sequence (16 heads and one query token, or 8
+// heads and two): the rows fit the N side of v_mfma_f32_16x16x32_bf16, so no
+// padded rows reach the matrix cores, and the query fragments of a wave take
+// 20 VGPRs. Wave w:
+//  * computes partial scores S^T (32 tokens x 16 rows) of a tile over its
+//    share of the 576-column contraction: k-steps of 32 columns 0-4, 5-9,
+//    10-13, 14-17;
+//  * after one barrier, sums the four partials from LDS (in the same order in
+//    every wave, so all waves hold the same scores) and runs the online
+//    softmax on them: per lane, 8 tokens of one row;
+//  * accumulates the value product O^T += V^T P^T for output columns
+//    128w..128w+127; the probabilities are already its B operand (token
+//    order permuted, with the V^T operand read in the same order).
+// The tile stream does not stop at a sequence boundary: the first three tiles
+// of the next segment are issued while the current one finishes, block ids
+// are loaded two segments ahead and query fragments one segment ahead, so a
+// boundary costs one drain of the memory counter (after the output stores)
+// instead of a chain of dependent loads.
+struct NarrowSeg {
+  int b, L, pre_e, seg_lo, seg_len, t_begin, n, slot;
+  bool split;
+};
+
+__global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams a) {
+  constexpr int NW = 4;
+  constexpr int NT = 64 * NW;
+  constexpr int MT = 16;                  // query rows per workgroup
+  constexpr int NST = 4;                  // ring stages
+  constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
+  constexpr int KQ = 5;                   // k-steps of a wave (at most)
+
+  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NST][kTileBytes];
+  __shared__ __attribute__((aligned(16))) f32x4 s_x[NW][2][64];   // partial scores
+  // plan scratch, inside ring stage 3 until the first tile is issued
+  int* s_pre = reinterpret_cast<int*>(s_stage[3]);
+  int* s_misc = reinterpret_cast<int*>(s_stage[3] + 4 * (kMaxBatch + 8));
+
+  const int tid = threadIdx.x, wave = uniform(tid >> 6);
+  const int lane = tid & 63, i16 = lane & 15, g = lane >> 4;
+
+  int v = blockIdx.x;
+  const int G = gridDim.x;
+  if ((G & 7) == 0) v = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int part = v / a.m_tiles, mt = v % a.m_tiles;
+
+  plan_prefix<NT>(a.seqlens, a.B, a.max_blocks, s_pre, s_misc);
+  const int T = uniform(s_pre[a.B]);
+  const int P = a.P;
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= a.B; b += NT) a.ws_prefix[b] = s_pre[b];
+  const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
+  if (tid == 0) {
+    s_misc[8] = 0x7fffffff;
+    s_misc[9] = -1;
+  }
+  __syncthreads();
+  for (int b = tid; b < a.B; b += NT) {
+    const int lo = s_pre[b], hi2 = s_pre[b + 1];
+    bool mine;
+    if (hi2 > lo) {
+      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
+    } else {
+      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
+      mine = owner == part;
+    }
+    if (mine) {
+      atomicMin(&s_misc[8], b);
+      atomicMax(&s_misc[9], b);
+    }
+  }
+  __syncthreads();
+  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+  const int pre_first = b_first <= b_last ? uniform(s_pre[b_first]) : 0;
+  __syncthreads();   // ring stage 3 is free from here on
+  if (b_first > b_last) return;
+
+  // ---- per-lane constants
+  const int r = mt * MT + i16;               // query row of this lane
+  const bool row_ok = r < a.M;
+  const int q_i = row_ok ? r / a.H : 0;
+  const int ks0 = 4 * wave + min(wave, 2);   // first k-step of this wave
+  const bool five = wave < 2;                // waves 0, 1 take five k-steps
+  // Score operand (A, tokens x columns): token 16 tb + i16, columns
+  // 32 ks + 8 g .. +7 = unit 32 (4 ks + g) + (token ^ 4 g); tb = 1 adds 256.
+  const int kofs = 512 * g + 16 * (i16 ^ (4 * g));
+  // Value operand (A, columns x tokens), transposing reads: lane 4 s + q of
+  // group g points at token 4 g + s (+16 for the second read), columns
+  // 128 w + 16 ct + 4 q .. +3, i.e. chunk 16 w + 2 ct + (q >> 1).
+  const int vs = i16 >> 2, vq = i16 & 3;
+  int vb[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      vb[par][h] = 8192 * wave + 512 * (vq >> 1) +
+                   16 * ((16 * h + 4 * g + vs) ^ (4 * (2 * par + (vq >> 1)))) + 8 * (vq & 1);
+  // LDS-DMA: load j of this wave fills units 64 k .. 64 k + 63, k = wave + 4 j
+  const int dchunk = 2 * wave + (lane >> 5), dl32 = lane & 31;
+  const uint32_t doff = (uint32_t)((dl32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
+
+  // ---- segments: the part's share of sequences b_first .. b_last
+  auto make_seg = [&](int b, int pre_b) {
+    NarrowSeg s;
+    s.b = b;
+    if (b > b_last) {
+      s.L = 0; s.pre_e = pre_b; s.seg_lo = 0; s.seg_len = 0; s.t_begin = 0; s.n = 0;
+      s.slot = 0; s.split = false;
+      return s;
+    }
+    s.L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
+    s.pre_e = pre_b + (s.L + kBT - 1) / kBT;
+    s.seg_lo = max(p_lo, pre_b) - pre_b;
+    const int seg_hi = min(p_hi, s.pre_e) - pre_b;
+    s.seg_len = max(0, seg_hi - s.seg_lo);
+    s.split = false;
+    s.slot = 0;
+    if (s.pre_e > pre_b) {
+      const int fp = part_of(pre_b, P, T), lp = part_of(s.pre_e - 1, P, T);
+      s.split = lp > fp;
+      s.slot = 2 * part + ((part == fp && pre_b > p_lo) ? 1 : 0);
+    }
+    s.t_begin = 2 * s.seg_lo;
+    const int t_end = min(2 * seg_hi, (s.L + kTile - 1) / kTile);
+    // an empty pool has no block to stand in for invalid ids: nothing is
+    // streamed and the id check poisons the segment
+    s.n = a.num_blocks > 0 ? max(0, t_end - s.t_begin) : 0;
+    return s;
+  };
+  // Block ids base .. base+63 of a segment, one per lane (the last one
+  // repeated past the end). Checked once landed: an id outside
+  // [0, num_blocks) poisons the segment (NaN output and lse) and is replaced
+  // by block 0, so that no copy ever leaves the cache.
+  auto load_ids = [&](const NarrowSeg& s, int base) {
+    if (s.seg_len == 0) return 0;
+    const int j = base + min(lane, max(0, s.seg_len - base - 1));
+    return ((const int32_t*)a.block_table)[(int64_t)s.b * a.max_blocks + s.seg_lo + j];
+  };
+  auto check_ids = [&](const NarrowSeg& s, int base, int& ids, bool& bad) {
+    const bool inval = ids < 0 || (int64_t)ids >= a.num_blocks;
+    bad = bad || __any(inval && base + lane < s.seg_len);
+    ids = inval ? 0 : ids;
+  };
+  auto load_q = [&](const NarrowSeg& s, u32x4* dst) {
+    if (s.b > b_last) return;
+    const uint16_t* qrow = a.q + ((int64_t)s.b * a.M + (row_ok ? r : 0)) * kDK + 8 * g;
+#pragma unroll
+    for (int j = 0; j < KQ; ++j)
+      dst[j] = *reinterpret_cast<const u32x4*>(qrow + 32 * min(ks0 + j, 17));
+  };
+
+  NarrowSeg sc = make_seg(b_first, pre_first);
+  NarrowSeg sn = make_seg(b_first + 1, sc.pre_e);
+  int ids_c = load_ids(sc, 0), ids_n = load_ids(sn, 0), ids_nn = 0;
+  bool bad_c = false, bad_n = false, bad_nn = false;
+  u32x4 qn[KQ];
+  load_q(sc, qn);
+  wait_vmcnt<0>();
+  check_ids(sc, 0, ids_c, bad_c);
+  check_ids(sn, 0, ids_n, bad_n);
+
+  int g_base = 0;   // stream index of the current segment's first tile
+  int iss = 0;      // tiles issued so far (stream order)
+  int bt_base = 0;  // first block of the current segment's id window
+  // Next tile of the stream: the current segment's, then at most three of the
+  // next segment's.
+  auto issuable = [&]() { return iss < g_base + sc.n + min(sn.n, 3); };
+  auto issue_one = [&]() {
+    const int rel = iss - g_base;
+    int64_t phys;
+    int half;
+    if (rel < sc.n) {
+      int rb = (rel >> 1) - bt_base;
+      if (rb >= 64) {
+        bt_base += 64;
+        rb -= 64;
+        ids_c = load_ids(sc, bt_base);
+        wait_vmcnt<0>();
+        check_ids(sc, bt_base, ids_c, bad_c);
+      }
+      phys = uniform(__builtin_amdgcn_readlane(ids_c, rb));
+      half = rel & 1;
+    } else {
+      const int idx = rel - sc.n;
+      phys = uniform(__builtin_amdgcn_readlane(ids_n, idx >> 1));
+      half = idx & 1;
+    }
+    const uint8_t* src = a.kv + (phys * kBT + half * kTile) * kRowBytes;
+    const uint32_t dst = lds_addr_of(s_stage[iss % NST]) + 1024 * wave;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) dma16_sbase(src + 128 * j, doff, dst + 4096 * j);
+    ++iss;
+  };
+  // Tokens past the end of the sequence in its last tile are cleared, so that
+  // whatever unused cache slots hold cannot reach the value product.
+  auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
+    for (int u = tid; u < kTile * 72; u += NT) {
+      const int c = u >> 5, pos = u & 31;
+      if ((pos ^ (4 * (c & 3))) >= valid)
+        *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  for (int b = b_first; b <= b_last; ++b) {
+    // Here every earlier memory operation has completed: the query rows of
+    // this segment are in qn, its first id window in ids_c (checked), and
+    // the next segment's in ids_n (checked).
+    bf16x8 qf[KQ];
+    {
+      const uint32_t sg = row_ok ? a.q_sign2 : 0u;
+      const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int j = 0; j < KQ; ++j) qf[j] = __builtin_bit_cast(bf16x8, (qn[j] ^ sg) & keep);
+    }
+    const NarrowSeg snn = make_seg(b + 2, sn.pre_e);
+    ids_nn = load_ids(snn, 0);
+    load_q(sn, qn);
+    bt_base = 0;
+    while (iss <= g_base + 2 && issuable()) issue_one();
+
+    const int n_vis = row_ok ? sc.L - a.s_q + 1 + q_i : 0x7fffffff;
+    f32x4 o[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int it = 0; it < sc.n; ++it) {
+      const int ahead = iss - (g_base + it + 1);   // tiles issued after this one (<= 2)
+      if (ahead >= 2) wait_vmcnt<2 * LPW>();
+      else if (ahead == 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      lds_barrier();   // tile it visible; every wave is done with tile it-1 and s_x
+      if (iss <= g_base + it + 3 && issuable()) issue_one();
+      LDS_AS uint8_t* st = (LDS_AS uint8_t*)s_stage[(g_base + it) % NST];
+      const int t0 = (sc.t_begin + it) * kTile;
+      if (sc.L - t0 < kTile) clear_tail(st, sc.L - t0);
+
+      // partial scores over this wave's k-steps, two 16-token blocks
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KQ; ++j) {
+        if (j == KQ - 1 && !five) break;
+        const LDS_AS uint8_t* kp = st + 2048 * (ks0 + j) + kofs;
+        const bf16x8 k0 = lds_read_b128(kp), k1 = lds_read_b128(kp + 256);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[j], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[j], acc1, 0, 0, 0);
+      }
+      s_x[wave][0][lane] = acc0;
+      s_x[wave][1][lane] = acc1;
+      lds_barrier();   // partials visible (and the cleared tail)
+      f32x4 sum0 = s_x[0][0][lane], sum1 = s_x[0][1][lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        sum0 += s_x[w][0][lane];
+        sum1 += s_x[w][1][lane];
+      }
+
+      // online softmax: element j of the lane is token 16 (j >> 2) + 4 g + (j & 3)
+      const float c = a.scale_mag_log2;
+      const bool masked = !__all(t0 + kTile <= n_vis);
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float sj = (j < 4 ? sum0[j] : sum1[j - 4]) * c;
+        const int tok = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
+        x[j] = (masked && tok >= n_vis) ? -INFINITY : sj;
+      }
+      float lmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      if (__builtin_expect(__any(lmax > m_run + kRescaleThreshold), 0)) {
+        // the four lanes of a row agree on its maximum
+        float rmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+        rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+        const bool raise = rmax > m_run + kRescaleThreshold;
+        const float m_new = rmax + kRefHeadroom;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        if (__any(raise && m_run != -INFINITY)) {
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct) o[ct] *= alpha;
+        }
+        l_run *= alpha;
+        if (raise) m_run = m_new;
+      }
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      uint32_t pw[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
+        const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
+        psum += p0 + p1;
+        pw[j] = pack_bf16x2(p0, p1);
+      }
+      l_run += psum;
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+
+      // value product, output columns 128 wave + 16 ct + 4 g + (0..3) of row i16
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const bf16x8 vf = vt_fragment(st + vb[ct & 1][0] + 1024 * ct, st + vb[ct & 1][1] + 1024 * ct);
+        o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[ct], 0, 0, 0);
+      }
+    }
+
+    // ---- epilogue: final rows, or bf16 partials of a split sequence
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    if (bad_c) lse_v = __builtin_nanf("");
+    if (row_ok) {
+      const int64_t row = (int64_t)b * a.M + r;
+      uint16_t* dst = sc.split ? a.part_o + ((int64_t)sc.slot * a.M + r) * kDL : a.out + row * kDL;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        uint32_t w0, w1;
+        if (bad_c) {
+          w0 = w1 = 0x7FC07FC0u;
+        } else {
+          w0 = pack_bf16x2(o[ct][0] * inv_l, o[ct][1] * inv_l);
+          w1 = pack_bf16x2(o[ct][2] * inv_l, o[ct][3] * inv_l);
+        }
+        *reinterpret_cast<uint64_t*>(dst + 128 * wave + 16 * ct + 4 * g) =
+            (uint64_t)w0 | ((uint64_t)w1 << 32);
+      }
+      if (wave == 0 && g == 0) {
+        if (sc.split) a.part_lse[(int64_t)sc.slot * a.M + r] = lse_v;
+        else a.lse[row] = lse_v;
+      }
+    }
+
+    // Drain: the stores above, the prefetched tiles of the next segment, its
+    // query rows and the id window after it. (Stores and loads may complete
+    // out of order, so no partial count is exact after a store.)
+    wait_vmcnt<0>();
+    check_ids(snn, 0, ids_nn, bad_nn);
+    g_base += sc.n;
+    sc = sn;
+    sn = snn;
+    ids_c = ids_n;
+    ids_n = ids_nn;
+    bad_c = bad_n;
+    bad_n = bad_nn;
+    bad_nn = false;
+  }
+}
+
 // ------------------------------------------ bf16 decode kernel (128-row tile)
 
 // 128 query rows per workgroup, so every cache tile is streamed into exactly
@@ -1678,7 +2026,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     const int t_begin = 2 * seg_lo;
     const int t_end = min(2 * seg_hi, (L + kTile - 1) / kTile);
     const int n_tiles = max(0, t_end - t_begin);
-    const int n_run = n_tiles;
+    // an empty pool has no block to stand in for invalid ids: nothing is
+    // streamed and the id check below poisons the segment
+    const int n_run = a.num_blocks > 0 ? n_tiles : 0;
     const int n_vis = row_ok ? L - a.s_q + 1 + q_i : 0x7fffffff;
 
     f32x16 o[16];
@@ -2269,6 +2619,7 @@ int device_cus() {
 }
 
 struct Plan {
+  bool narrow;   // 16-row tile (bf16 cache)
   int HG, CG, MT, m_tiles, P, M;
   size_t off_prefix, off_lse, off_o, bytes;
 };
@@ -2293,8 +2644,9 @@ mla_status validate_problem(const mla_problem* p) {
   if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_Q8_0)
     return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);
   if (p->num_parts < 0) return fail(MLA_ERR_INVALID_ARG, "num_parts must be >= 0");
-  if (p->m_tile != 0 && p->m_tile != 32 && p->m_tile != 64 && p->m_tile != 128)
-    return fail(MLA_ERR_INVALID_ARG, "m_tile must be 0, 32, 64 or 128 (got %d)", p->m_tile);
+  if (p->m_tile != 0 && p->m_tile != 16 && p->m_tile != 32 && p->m_tile != 64 &&
+      p->m_tile != 128)
+    return fail(MLA_ERR_INVALID_ARG, "m_tile must be 0, 16, 32, 64 or 128 (got %d)", p->m_tile);
   return MLA_OK;
 }
 
@@ -2305,16 +2657,20 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   if (s != MLA_OK) return s;
   const int M = p->seqlen_q * p->num_heads;
   pl->M = M;
-  // Row tile. bf16 cache: 32, 64 or 128 rows per workgroup (1, 2 or 4 row
-  // groups of 32, each wave owning whole rows); the smallest tile that holds
-  // all rows of a sequence, so the cache is streamed once per part. q8_0
-  // cache: 32 or 64 rows, each row group's work split over CG waves. More rows
-  // than one tile holds take several row tiles per KV part, placed on the
-  // same XCD so the second read of each cache tile hits L2.
+  // Row tile. bf16 cache: 16 rows per workgroup (the four waves split the
+  // score contraction and the output columns), or 32, 64 or 128 (1, 2 or 4
+  // row groups of 32, each wave owning whole rows); the smallest tile that
+  // holds all rows of a sequence, so the cache is streamed once per part.
+  // q8_0 cache: 32 or 64 rows, each row group's work split over CG waves. More
+  // rows than one tile holds take several row tiles per KV part, placed on
+  // the same XCD so the second read of each cache tile hits L2.
   const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
-  if (q8 && p->m_tile == 128)
-    return fail(MLA_ERR_UNSUPPORTED, "m_tile 128 is not available for the q8_0 cache");
-  if (p->m_tile) {
+  if (q8 && (p->m_tile == 128 || p->m_tile == 16))
+    return fail(MLA_ERR_UNSUPPORTED, "m_tile %d is not available for the q8_0 cache", p->m_tile);
+  pl->narrow = !q8 && (p->m_tile == 16 || (p->m_tile == 0 && M <= 16));
+  if (pl->narrow) {
+    pl->HG = 1;
+  } else if (p->m_tile) {
     pl->HG = p->m_tile / 32;
   } else if (q8) {
     pl->HG = M <= 32 ? 1 : 2;
@@ -2327,7 +2683,7 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
     if (q8 && (cg == 2 || cg == 4)) pl->CG = cg;
   }
   if (!q8) pl->CG = 4 / pl->HG;
-  pl->MT = 32 * pl->HG;
+  pl->MT = pl->narrow ? 16 : 32 * pl->HG;
   pl->m_tiles = (M + pl->MT - 1) / pl->MT;
   int P = p->num_parts;
   if (P == 0) {
@@ -2373,6 +2729,11 @@ hipError_t launch_decode(const DecodeParams& dp, int grid, hipStream_t stream) {
 
 hipError_t launch_pipe(const DecodeParams& dp, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(mla_decode_pipe_kernel, dim3(grid), dim3(256), 0, stream, dp);
+  return hipGetLastError();
+}
+
+hipError_t launch_narrow(const DecodeParams& dp, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_decode_narrow_kernel, dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -2479,7 +2840,9 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
   const int grid = pl.P * pl.m_tiles;
   hipError_t e;
   const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
-  if (!q8) {
+  if (pl.narrow) {
+    e = launch_narrow(dp, grid, stream);
+  } else if (!q8) {
     switch (pl.HG) {
       case 1: e = launch_rows<1>(dp, grid, stream); break;
       case 2: e = launch_rows<2>(dp, grid, stream); break;

@@ -37,6 +37,14 @@ SMALL = [
     ("h128_mt32", 2, 1, 128, [300, 1000], "permuted", "bf16", 32),
     ("h128_mt64", 2, 1, 128, [300, 1000], "permuted", "bf16", 64),
     ("h64_mt64_q8", 2, 1, 64, [513, 64], "sequential", "q8_0", 64),
+    # 16-row tile: causal pairs, several row tiles, many short segments per
+    # part (the stream runs on across sequence boundaries, also over empty
+    # ones), and segments longer than one 64-block id window
+    ("h8_pair", 3, 2, 8, [2, 700, 129], "permuted", "bf16", 0),
+    ("h40_mt16", 2, 1, 40, [500, 77], "permuted", "bf16", 16),
+    ("h16_many", 24, 1, 16, [1, 0, 31, 32, 33, 64, 65, 0, 0, 2, 96, 97, 127, 128, 129, 3,
+                             0, 191, 300, 1, 63, 0, 20, 257], "permuted", "bf16", 0),
+    ("h16_long", 2, 1, 16, [5000, 4161], "permuted", "bf16", 0),
 ]
 
 
@@ -124,8 +132,9 @@ def test_one_hot_probe_returns_the_exact_row(H):
             assert np.abs(lse[b, 0] - 4096.0).max() <= 1e-3
 
 
-def test_empty_rows_and_causal_visibility():
-    w = wl.make_workload("deg", 4, 2, 16, [0, 1, 2, 130], seed=9, table="permuted")
+@pytest.mark.parametrize("H", [16, 8])
+def test_empty_rows_and_causal_visibility(H):
+    w = wl.make_workload("deg", 4, 2, H, [0, 1, 2, 130], seed=9, table="permuted")
     for parts in (1, 3):
         out, lse, _ = run_gpu(w, num_parts=parts)
         compare(out, lse, *oracle_rows(w), what=f"degenerate P={parts}")
@@ -143,6 +152,46 @@ def test_invalid_block_ids_poison_only_their_sequence():
     w.block_table[1, 2] = -1
     out, lse, _ = run_gpu(w, num_parts=2)
     assert np.all(np.isnan(lse[1])) and np.all(np.isfinite(lse[[0, 2]]))
+
+
+def test_invalid_block_id_in_a_later_id_window():
+    """16-row tile: block ids are read 64 at a time; a bad id in the second
+    window of a long segment poisons that sequence only."""
+    w = wl.make_workload("bad2", 3, 1, 16, [300, 4500, 700], seed=11)
+    w.block_table[1, 66] = w.num_blocks + 1
+    for parts in (1, 3):
+        out, lse, _ = run_gpu(w, num_parts=parts)
+        compare(out, lse, *oracle_rows(w), what=f"invalid id, later window P={parts}")
+        assert np.all(np.isnan(lse[1])) and np.all(np.isnan(out[1]))
+        assert np.all(np.isfinite(lse[[0, 2]]))
+
+
+@pytest.mark.parametrize("H,kvd", [(16, "bf16"), (40, "bf16"), (128, "bf16"), (16, "q8_0")])
+def test_empty_pool_poisons_every_nonempty_sequence(H, kvd):
+    """num_blocks = 0: no block id is valid, so every sequence with tokens is
+    poisoned and nothing is read from the cache; empty sequences stay empty."""
+    import ctypes
+    w = wl.make_workload("nopool", 3, 1, H, [100, 0, 700], seed=12, table="permuted", kv_dtype=kvd)
+    t = device_inputs(w)
+    out = torch.empty((w.B, 1, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, 1, H), dtype=torch.float32, device="cuda")
+    prob = mla.make_problem(t["q"], t["kv"], t["bt"], kv_dtype=mla.KV_BF16 if kvd == "bf16"
+                            else mla.KV_Q8_0, max_seqlen=w.max_seqlen, num_parts=2)
+    prob.num_blocks = 0
+    ws = torch.empty(max(16, mla.workspace_size(prob)), dtype=torch.uint8, device="cuda")
+    vp = ctypes.c_void_p
+    sc = vp(t["kv_scales"].data_ptr()) if t["kv_scales"] is not None else None
+    st = mla.lib().mla_decode(ctypes.byref(prob), vp(t["q"].data_ptr()), vp(t["kv"].data_ptr()), sc,
+                              vp(t["bt"].data_ptr()), vp(t["sl"].data_ptr()),
+                              ctypes.c_float(w.softmax_scale), vp(out.data_ptr()),
+                              vp(lse.data_ptr()), vp(ws.data_ptr()), ws.numel(),
+                              vp(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, mla.lib().mla_last_error().decode()
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    ls = lse.cpu().numpy()
+    assert np.all(np.isnan(ls[[0, 2]])) and np.all(np.isnan(o[[0, 2]]))
+    assert np.all(np.isneginf(ls[1])) and np.all(o[1] == 0)
 
 
 def test_combine_entry_point_matches_the_oracle():
