@@ -798,6 +798,23 @@ __device__ __forceinline__ void acc_scale(f32x16& acc, float alpha) {
   }
 }
 
+// The same for a 4-register accumulator (16x16 MFMA).
+__device__ __forceinline__ void acc_scale4(f32x4& acc, float alpha) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = acc[i];
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(x), "=&v"(t)
+        : "v"(alpha));
+    acc[i] = x;
+  }
+}
+
 // ------------------------------------------------- bf16 decode kernel (rows)
 
 // One workgroup = 4 waves (one per SIMD) on one KV partition for a tile of
@@ -1360,7 +1377,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
   // Next tile of the stream: the current segment's, then at most three of the
   // next segment's.
   auto issuable = [&]() { return iss < g_base + sc.n + min(sn.n, 3); };
-  auto issue_one = [&]() {
+  // Source and ring slot of the next tile of the stream; advances the stream.
+  auto next_tile = [&](const uint8_t*& src, uint32_t& dst) {
     const int rel = iss - g_base;
     int64_t phys;
     int half;
@@ -1380,11 +1398,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
       phys = uniform(__builtin_amdgcn_readlane(ids_n, idx >> 1));
       half = idx & 1;
     }
-    const uint8_t* src = a.kv + (phys * kBT + half * kTile) * kRowBytes;
-    const uint32_t dst = lds_addr_of(s_stage[iss % NST]) + 1024 * wave;
+    src = a.kv + (phys * kBT + half * kTile) * kRowBytes;
+    dst = lds_addr_of(s_stage[iss % NST]) + 1024 * wave;
+    ++iss;
+  };
+  auto issue_one = [&]() {
+    const uint8_t* src;
+    uint32_t dst;
+    next_tile(src, dst);
 #pragma unroll
     for (int j = 0; j < LPW; ++j) dma16_sbase(src + 128 * j, doff, dst + 4096 * j);
-    ++iss;
   };
   // Tokens past the end of the sequence in its last tile are cleared, so that
   // whatever unused cache slots hold cannot reach the value product.
@@ -1425,76 +1448,113 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
       else if (ahead == 1) wait_vmcnt<LPW>();
       else wait_vmcnt<0>();
       lds_barrier();   // tile it visible; every wave is done with tile it-1 and s_x
-      if (iss <= g_base + it + 3 && issuable()) issue_one();
+      // tile it+3 of the stream goes to the stage tile it-1 used; its copies
+      // are spread over the score products below
+      const bool do_iss = iss <= g_base + it + 3 && issuable();
+      const uint8_t* isrc = a.kv;
+      uint32_t idst = 0;
+      if (do_iss) next_tile(isrc, idst);
       LDS_AS uint8_t* st = (LDS_AS uint8_t*)s_stage[(g_base + it) % NST];
       const int t0 = (sc.t_begin + it) * kTile;
       if (sc.L - t0 < kTile) clear_tail(st, sc.L - t0);
 
-      // partial scores over this wave's k-steps, two 16-token blocks
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      // partial scores over this wave's k-steps, two 16-token blocks; all
+      // operand reads first
+      bf16x8 kf[2 * KQ];
 #pragma unroll
       for (int j = 0; j < KQ; ++j) {
         if (j == KQ - 1 && !five) break;
         const LDS_AS uint8_t* kp = st + 2048 * (ks0 + j) + kofs;
-        const bf16x8 k0 = lds_read_b128(kp), k1 = lds_read_b128(kp + 256);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[j], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[j], acc1, 0, 0, 0);
+        kf[2 * j] = lds_read_b128(kp);
+        kf[2 * j + 1] = lds_read_b128(kp + 256);
       }
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KQ; ++j) {
+        if (j == KQ - 1 && !five) break;
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[2 * j], qf[j], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[2 * j + 1], qf[j], acc1, 0, 0, 0);
+        if (j < 4 && do_iss) {
+          dma16_sbase(isrc + 256 * j, doff, idst + 8192 * j);
+          dma16_sbase(isrc + 256 * j + 128, doff, idst + 8192 * j + 4096);
+        }
+      }
+      if (do_iss) dma16_sbase(isrc + 128 * (LPW - 1), doff, idst + 4096 * (LPW - 1));
       s_x[wave][0][lane] = acc0;
       s_x[wave][1][lane] = acc1;
       lds_barrier();   // partials visible (and the cleared tail)
-      f32x4 sum0 = s_x[0][0][lane], sum1 = s_x[0][1][lane];
+      // value operands of the tile, in flight while the softmax runs
+      bf16x8 vf[8];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) {
-        sum0 += s_x[w][0][lane];
-        sum1 += s_x[w][1][lane];
-      }
+      for (int ct = 0; ct < 8; ++ct)
+        vf[ct] = vt_fragment(st + vb[ct & 1][0] + 1024 * ct, st + vb[ct & 1][1] + 1024 * ct);
+      // the four partials as (p[w] + p[w^1]) + (p[w^2] + p[w^3]), this wave's
+      // own from registers: addition commutes, so every wave forms the same
+      // pairs and holds the same sums
+      const f32x4 sum0 = (acc0 + s_x[wave ^ 1][0][lane]) + (s_x[wave ^ 2][0][lane] + s_x[wave ^ 3][0][lane]);
+      const f32x4 sum1 = (acc1 + s_x[wave ^ 1][1][lane]) + (s_x[wave ^ 2][1][lane] + s_x[wave ^ 3][1][lane]);
 
-      // online softmax: element j of the lane is token 16 (j >> 2) + 4 g + (j & 3)
+      // online softmax: element j of the lane is token 16 (j >> 2) + 4 g + (j & 3).
+      // Interior tiles (every token visible to every row) skip the mask and
+      // fold the scale into the exponent's FMA; masked tiles scale first and
+      // then select, so that a masked token is -inf whatever the scale.
       const float c = a.scale_mag_log2;
-      const bool masked = !__all(t0 + kTile <= n_vis);
-      float x[8];
+      float alpha = 1.f;      // rescale factor of this lane's row (rare)
+      bool rescale = false;   // some row's accumulators need it
+      auto softmax = [&](auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float sj = (j < 4 ? sum0[j] : sum1[j - 4]) * c;
-        const int tok = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
-        x[j] = (masked && tok >= n_vis) ? -INFINITY : sj;
-      }
-      float lmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      if (__builtin_expect(__any(lmax > m_run + kRescaleThreshold), 0)) {
-        // the four lanes of a row agree on its maximum
-        float rmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-        const bool raise = rmax > m_run + kRescaleThreshold;
-        const float m_new = rmax + kRefHeadroom;
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        if (__any(raise && m_run != -INFINITY)) {
-#pragma unroll
-          for (int ct = 0; ct < 8; ++ct) o[ct] *= alpha;
+        for (int j = 0; j < 8; ++j) {
+          const float sj = j < 4 ? sum0[j] : sum1[j - 4];
+          if (MASKED) {
+            const int tok = t0 + 16 * (j >> 2) + 4 * g + (j & 3);
+            x[j] = tok < n_vis ? sj * c : -INFINITY;
+          } else {
+            x[j] = sj;
+          }
         }
-        l_run *= alpha;
-        if (raise) m_run = m_new;
-      }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-      uint32_t pw[4];
-      float psum = 0.f;
+        float lmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        if (!MASKED) lmax *= c;
+        if (__builtin_expect(__any(lmax > m_run + kRescaleThreshold), 0)) {
+          // the four lanes of a row agree on its maximum
+          float rmax = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+          rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+          const bool raise = rmax > m_run + kRescaleThreshold;
+          const float m_new = rmax + kRefHeadroom;
+          alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+          rescale = __any(raise && m_run != -INFINITY);
+          l_run *= alpha;
+          if (raise) m_run = m_new;
+        }
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+        uint32_t pw[4];
+        float psum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
-        const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
-        psum += p0 + p1;
-        pw[j] = pack_bf16x2(p0, p1);
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(MASKED ? x[2 * j] + neg_m
+                                                         : __builtin_fmaf(x[2 * j], c, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(MASKED ? x[2 * j + 1] + neg_m
+                                                         : __builtin_fmaf(x[2 * j + 1], c, neg_m));
+          psum += p0 + p1;
+          pw[j] = pack_bf16x2(p0, p1);
+        }
+        l_run += psum;
+        return __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      };
+      const bf16x8 pb = __all(t0 + kTile <= n_vis) ? softmax(std::integral_constant<bool, false>{})
+                                                   : softmax(std::integral_constant<bool, true>{});
+
+      if (__builtin_expect(rescale, 0)) {
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc_scale4(o[ct], alpha);
       }
-      l_run += psum;
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 
       // value product, output columns 128 wave + 16 ct + 4 g + (0..3) of row i16
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const bf16x8 vf = vt_fragment(st + vb[ct & 1][0] + 1024 * ct, st + vb[ct & 1][1] + 1024 * ct);
-        o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[ct], 0, 0, 0);
-      }
+      for (int ct = 0; ct < 8; ++ct)
+        o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct], pb, o[ct], 0, 0, 0);
     }
 
     // ---- epilogue: final rows, or bf16 partials of a split sequence
