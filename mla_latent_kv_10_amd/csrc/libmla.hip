@@ -1600,367 +1600,6 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
   }
 }
 
-// ------------------------------------------ bf16 decode kernel (128-row tile)
-
-// 128 query rows per workgroup, so every cache tile is streamed into exactly
-// one CU (the LDS-DMA fill rate per CU is the scarce resource). Wave w:
-//  * computes the full 576-column scores and the softmax of rows 32w..32w+31
-//    (its query fragments stay in registers);
-//  * publishes those rows' probabilities (bf16, already in the value
-//    product's B-operand layout) through LDS;
-//  * accumulates the value product of all 128 rows for output columns
-//    128w..128w+127, so each V^T operand read from LDS feeds four MFMAs.
-// Two barriers per 32-token tile: one for the tile (3-stage LDS-DMA ring,
-// two tiles in flight), one for the probabilities. The reference maximum of
-// the online softmax moves rarely; when a row's does, its owner publishes the
-// factor and every wave rescales that row's accumulators.
-__global__ __launch_bounds__(256, 1) void mla_decode_quad_kernel(DecodeParams a) {
-  constexpr int NW = 4;
-  constexpr int NT = 64 * NW;
-  constexpr int MT = 128;
-  constexpr int NST = 3;                  // ring stages
-  constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
-  constexpr int KPF = 3;                  // score operands in flight
-
-  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NST][kTileBytes];
-  // probabilities: [row group][token half][lane] x 16 bytes (B-operand layout)
-  __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];
-  __shared__ float s_alpha[MT];           // rescale factor per row (rare path)
-  __shared__ float s_lsum[MT];            // softmax denominators (epilogue)
-  __shared__ int s_flag[NW];
-  __shared__ int s_pre[kMaxBatch + 1];
-  __shared__ int s_misc[16];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
-  const int hi = lane >> 5, l32 = lane & 31;
-
-  int v = blockIdx.x;
-  const int G = gridDim.x;
-  if ((G & 7) == 0) v = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int part = v / a.m_tiles, mt = v % a.m_tiles;
-
-  plan_prefix<NT>(a.seqlens, a.B, a.max_blocks, s_pre, s_misc);
-  const int T = uniform(s_pre[a.B]);
-  const int P = a.P;
-  if (blockIdx.x == 0)
-    for (int b = tid; b <= a.B; b += NT) a.ws_prefix[b] = s_pre[b];
-  const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
-
-  if (tid == 0) {
-    s_misc[8] = 0x7fffffff;
-    s_misc[9] = -1;
-  }
-  __syncthreads();
-  for (int b = tid; b < a.B; b += NT) {
-    const int lo = s_pre[b], hi2 = s_pre[b + 1];
-    bool mine;
-    if (hi2 > lo) {
-      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
-    } else {
-      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
-      mine = owner == part;
-    }
-    if (mine) {
-      atomicMin(&s_misc[8], b);
-      atomicMax(&s_misc[9], b);
-    }
-  }
-  __syncthreads();
-  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
-
-  const int r = mt * MT + 32 * wave + l32;   // row whose scores this lane computes
-  const bool row_ok = r < a.M;
-  const int q_i = row_ok ? r / a.H : 0;
-  const int cbase = 128 * wave;              // first output column of this wave
-
-  const int kofs0 = 16 * tile_unit(l32, hi);
-  const int kofs1 = 16 * tile_unit(l32, 2 + hi) - 1024;
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
-  const int vc = cbase / 8 + 2 * (g16 & 1) + (vq >> 1);
-  const int vofs0 = 16 * tile_unit(4 * vh + vs, vc) + 8 * (vq & 1);
-  const int vofs1 = 16 * tile_unit(8 + 4 * vh + vs, vc) + 8 * (vq & 1);
-  const int dchunk = 2 * wave + hi;
-  const uint32_t doff = (uint32_t)((l32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
-
-  for (int b = b_first; b <= b_last; ++b) {
-    const int pre_b = uniform(s_pre[b]), pre_e = uniform(s_pre[b + 1]);
-    const int L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
-    const int seg_lo = max(p_lo, pre_b) - pre_b, seg_hi = min(p_hi, pre_e) - pre_b;
-    bool split = false;
-    int slot = 0;
-    if (pre_e > pre_b) {
-      const int fp = part_of(pre_b, P, T), lp = part_of(pre_e - 1, P, T);
-      split = lp > fp;
-      slot = 2 * part + ((part == fp && pre_b > p_lo) ? 1 : 0);
-    }
-    const int t_begin = 2 * seg_lo;
-    const int t_end = min(2 * seg_hi, (L + kTile - 1) / kTile);
-    const int n_tiles = max(0, t_end - t_begin);
-    const CONST_AS int32_t* bt =
-        (const CONST_AS int32_t*)a.block_table + (int64_t)b * a.max_blocks;
-
-    int bad_local = 0;
-    for (int j = seg_lo + tid; j < seg_hi; j += NT) {
-      const int id = bt[j];
-      if (id < 0 || (int64_t)id >= a.num_blocks) bad_local = 1;
-    }
-    const bool bad = __syncthreads_or(bad_local) != 0;
-    const int n_run = bad ? 0 : n_tiles;
-
-    const int n_vis = row_ok ? L - a.s_q + 1 + q_i : 0x7fffffff;
-
-    // o[4 rb + cb]: rows 32 rb .. +31 of the tile, columns cbase + 32 cb .. +31
-    f32x16 o[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[j][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-
-    // Block ids of the segment, 64 at a time, one per lane: a tile's id is a
-    // v_readlane away, with no memory access on the tile loop's path.
-    const int seg_len = max(0, seg_hi - seg_lo);
-    int bt_base = 0;
-    int bt_lane = 0;
-    auto load_ids = [&]() {
-      const int j = bt_base + min(lane, max(0, seg_len - bt_base - 1));
-      bt_lane = seg_len > 0 ? ((const int32_t*)a.block_table)[(int64_t)b * a.max_blocks + seg_lo + j] : 0;
-    };
-    // Source of tile idx (segment-relative; past the segment: its last tile,
-    // reloaded as a harmless dummy so that every iteration issues one tile).
-    auto tile_src = [&](int idx) {
-      idx = min(idx, n_run - 1);
-      int rel = (idx >> 1) - bt_base;
-      if (rel >= 64) {            // next 64 ids (segments longer than 64 blocks)
-        bt_base += 64;
-        rel -= 64;
-        load_ids();
-        wait_vmcnt<0>();
-      }
-      const int64_t phys = uniform(__builtin_amdgcn_readlane(bt_lane, rel));
-      return a.kv + (phys * kBT + ((t_begin + idx) & 1) * kTile) * kRowBytes;
-    };
-    auto issue = [&](int idx) {
-      const uint32_t dst = lds_addr_of(s_stage[idx % NST]) + 1024 * wave;
-      const uint8_t* src = tile_src(idx);
-#pragma unroll
-      for (int j = 0; j < LPW; ++j) dma16_sbase(src + 128 * j, doff, dst + 4096 * j);
-    };
-    auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
-      for (int u = tid; u < kTile * 72; u += NT) {
-        const int c = u >> 5, pos = u & 31;
-        if ((pos ^ (4 * (c & 3))) >= valid)
-          *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    };
-
-    wait_vmcnt<0>();
-    load_ids();
-    wait_vmcnt<0>();
-    if (n_run > 0) {
-      issue(0);
-      issue(1);
-    }
-    // the query rows load while the first tiles stream in (the compiler's
-    // waits for these loads also cover the earlier LDS-DMA loads)
-    bf16x8 qf[36];
-    {
-      const uint16_t* qrow = a.q + ((int64_t)b * a.M + (row_ok ? r : 0)) * kDK;
-      const uint32_t sg = a.q_sign2;
-#pragma unroll
-      for (int s = 0; s < 36; ++s) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (row_ok) z = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * hi) ^ sg;
-        qf[s] = __builtin_bit_cast(bf16x8, z);
-      }
-    }
-    for (int it = 0; it < n_run; ++it) {
-      // ---- tile it has landed (tile it+1 may still be in flight); the stage
-      // of tile it-1 is free for tile it+2
-      wait_vmcnt<LPW>();
-      lds_barrier();
-      const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage[it % NST];
-      // tile it+2 streams into the free stage, one load every four score
-      // MFMAs: a burst of loads would stall this wave on a full memory queue
-      const uint8_t* nsrc = tile_src(it + 2);
-      const uint32_t ndst = lds_addr_of(s_stage[(it + 2) % NST]) + 1024 * wave;
-      const int t0 = (t_begin + it) * kTile;
-      {
-        const int valid = L - t0;
-        if (valid < kTile) {
-          clear_tail((LDS_AS uint8_t*)s_stage[it % NST], valid);
-          lds_barrier();
-        }
-      }
-
-      // ---- scores S^T (tokens x own rows): register i is token
-      // 8(i>>2) + 4hi + (i&3)
-      f32x16 s;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = 0.f;
-      {
-        auto rd = [&](int k) { return lds_read_b128(st + 1024 * k + ((k & 1) ? kofs1 : kofs0)); };
-        bf16x8 kf[KPF];
-#pragma unroll
-        for (int j = 0; j < KPF; ++j) kf[j] = rd(j);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < 36; ++k) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k % KPF], qf[k], s, 0, 0, 0);
-          if (k + KPF < 36) kf[k % KPF] = rd(k + KPF);
-          if ((k & 3) == 1) dma16_sbase(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-
-      // ---- online softmax of the own rows (log2 domain)
-      const float c = a.scale_mag_log2;
-      const bool masked = !__all(t0 + kTile <= n_vis);
-      const int lim = n_vis - t0 - 4 * hi;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        x[i] = masked ? ((8 * (i >> 2) + (i & 3) < lim) ? s[i] * c : -INFINITY) : s[i] * c;
-      float lmax = x[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) lmax = fmaxf(lmax, x[i]);
-      float alpha = 1.f;
-      const bool want = lmax > m_run + kRescaleThreshold;
-      const bool raise_any = __any(want);
-      if (__builtin_expect(raise_any, 0)) {
-        const float rmax = fmaxf(lmax, __shfl_xor(lmax, 32, 64));
-        const bool raise = rmax > m_run + kRescaleThreshold;
-        const float m_new = rmax + kRefHeadroom;
-        alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        l_run *= alpha;
-        if (raise) m_run = m_new;
-      }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-      float psum = 0.f;
-      uint32_t pw[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
-        const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
-        psum += p0 + p1;
-        pw[j] = pack_bf16x2(p0, p1);
-      }
-      l_run += psum;
-      s_p[wave][0][lane] = u32x4{pw[0], pw[1], pw[2], pw[3]};
-      s_p[wave][1][lane] = u32x4{pw[4], pw[5], pw[6], pw[7]};
-      if (raise_any && hi == 0) s_alpha[32 * wave + l32] = alpha;
-      if (lane == 0) s_flag[wave] = raise_any ? 1 : 0;
-      lds_barrier();
-
-      // ---- a row's reference maximum moved: rescale its accumulators in
-      // every wave (on a segment's first tile they are still zero)
-      {
-        const int f = s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3];
-        if (__builtin_expect(f != 0 && it > 0, 0)) {
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) {
-            const float al = s_flag[rb] ? s_alpha[32 * rb + l32] : 1.f;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) acc_scale(o[4 * rb + cb], al);
-          }
-        }
-      }
-
-      // ---- value product of all 128 rows, own 128 columns:
-      // O^T(columns x rows) += V^T P^T, each V^T operand shared by 4 row blocks
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 pf[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) pf[rb] = __builtin_bit_cast(bf16x8, s_p[rb][kk][lane]);
-        auto vread = [&](int cb) {
-          return vt_fragment(st + vofs0 + 2048 * cb + 256 * kk, st + vofs1 + 2048 * cb + 256 * kk);
-        };
-        bf16x8 va[2] = {vread(0), vread(1)};
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb)
-            o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb & 1], pf[rb], o[4 * rb + cb], 0, 0, 0);
-          if (cb + 2 < 4) va[cb & 1] = vread(cb + 2);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-
-    // ---- epilogue: every wave needs the denominators of all 128 rows. The
-    // normalised bf16 rows go through LDS (the ring is idle now) so that the
-    // global stores are whole 256-byte row segments, 16 bytes per lane.
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    if (bad) lse_v = __builtin_nanf("");
-    wait_vmcnt<0>();                   // ring loads (including dummies) have landed
-    if (hi == 0) s_lsum[32 * wave + l32] = l_tot;
-    lds_barrier();
-    constexpr int kStageRow = 272;     // bytes per staged row: 256 + 16 of padding
-    uint16_t* dst_base = split ? a.part_o + ((int64_t)slot * a.M) * kDL
-                               : a.out + ((int64_t)b * a.M) * kDL;
-    LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_stage[0] + wave * (64 * kStageRow);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // rows 64 half .. 64 half + 63 of the tile, this wave's 128 columns
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int rb = 2 * half + q;
-        const float lt = s_lsum[32 * rb + l32];
-        // an invalid block id makes the whole sequence NaN
-        const float inv_l = bad ? __builtin_nanf("") : (lt > 0.f ? 1.f / lt : 0.f);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x16& acc = o[4 * rb + cb];
-            const uint32_t w0 = pack_bf16x2(acc[4 * g + 0] * inv_l, acc[4 * g + 1] * inv_l);
-            const uint32_t w1 = pack_bf16x2(acc[4 * g + 2] * inv_l, acc[4 * g + 3] * inv_l);
-            const int col = 32 * cb + 8 * g + 4 * hi;
-            *reinterpret_cast<LDS_AS uint64_t*>(stg + (32 * q + l32) * kStageRow + 2 * col) =
-                (uint64_t)w0 | ((uint64_t)w1 << 32);
-          }
-      }
-      lds_barrier();
-      // 64 rows x 256 bytes: lane = 16 bytes, 4 rows per store instruction.
-      // The lane index is made opaque here so that the compiler cannot hoist
-      // (and spill) the sixteen store addresses out of the sequence loop.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int rl0 = ln >> 4, cl = 8 * (ln & 15);
-      const int row0 = mt * MT + 64 * half;
-      uint16_t* gdst = dst_base + (int64_t)(row0 + rl0) * kDL + cbase + cl;
-      const LDS_AS uint8_t* lsrc = stg + rl0 * kStageRow + 2 * cl;
-      if (row0 + 64 <= a.M) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          *reinterpret_cast<u32x4*>(gdst + 4 * i * kDL) =
-              *reinterpret_cast<const LDS_AS u32x4*>(lsrc + 4 * i * kStageRow);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (row0 + rl0 + 4 * i < a.M)
-            *reinterpret_cast<u32x4*>(gdst + 4 * i * kDL) =
-                *reinterpret_cast<const LDS_AS u32x4*>(lsrc + 4 * i * kStageRow);
-      }
-      lds_barrier();
-    }
-    if (row_ok && hi == 0) {
-      const int64_t row = (int64_t)b * a.M + r;
-      if (!split)
-        a.lse[row] = lse_v;
-      else
-        a.part_lse[(int64_t)slot * a.M + r] = lse_v;
-    }
-    wait_vmcnt<0>();     // no LDS-DMA may outlive the ring's use
-    if (b < b_last) __syncthreads();   // the ring and the exchange buffers are reused
-  }
-}
-
-
 // Score-chain MFMA with its accumulator in VGPRs. With 256 AGPRs holding the
 // value-product accumulators there is no AGPR room for the score tile, so it
 // is pinned to VGPRs here (C/D of an MFMA may live in either file). `first`
@@ -1987,14 +1626,22 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
 
 // --------------------------- bf16 decode kernel (128-row tile, pipelined)
 
-// Same division of work as the 128-row kernel above (each wave: scores and
-// softmax of 32 rows, value product of all 128 rows for 128 columns), but the
-// value product of tile i-1 is interleaved with the score product of tile i:
-// the independent value MFMAs fill the latency of the dependent score chain,
-// and the transposing V reads mix with the score operand reads. A 4-stage
-// ring keeps tile i-1 resident while tile i is scored and tiles i+1, i+2
-// stream in. The plan prefix and the epilogue's scratch live in ring space
-// that is idle at those times, which keeps LDS under 160 KiB.
+// 128 query rows per workgroup, so every cache tile is streamed into exactly
+// one CU (the LDS-DMA fill rate per CU is the scarce resource). Wave w:
+//  * computes the full 576-column scores and the softmax of rows 32w..32w+31
+//    (its query fragments stay in registers);
+//  * publishes those rows' probabilities (bf16, already in the value
+//    product's B-operand layout) through LDS;
+//  * accumulates the value product of all 128 rows for output columns
+//    128w..128w+127, so each V^T operand read from LDS feeds four MFMAs.
+// The value product of tile i-1 is interleaved with the score product of
+// tile i: the independent value MFMAs fill the latency of the dependent score
+// chain, and the transposing V reads mix with the score operand reads. A
+// 4-stage ring keeps tile i-1 resident while tile i is scored and tiles i+1,
+// i+2 stream in. The reference maximum of the online softmax moves rarely;
+// when a row's does, its owner publishes the factor and every wave rescales
+// that row's accumulators. The plan prefix and the epilogue's scratch live in
+// ring space that is idle at those times, which keeps LDS under 160 KiB.
 __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a) {
   constexpr int NW = 4;
   constexpr int NT = 64 * NW;
@@ -2721,11 +2368,11 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   // score contraction and the output columns), or 32, 64 or 128 (1, 2 or 4
   // row groups of 32, each wave owning whole rows); the smallest tile that
   // holds all rows of a sequence, so the cache is streamed once per part.
-  // q8_0 cache: 32 or 64 rows, each row group's work split over CG waves. More
+  // q8_0 cache: 32 or 64 rows, each row group's work split over 4 waves. More
   // rows than one tile holds take several row tiles per KV part, placed on
   // the same XCD so the second read of each cache tile hits L2.
   const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
-  if (q8 && (p->m_tile == 128 || p->m_tile == 16))
+  if (q8 && (p->m_tile == 16 || p->m_tile == 128))
     return fail(MLA_ERR_UNSUPPORTED, "m_tile %d is not available for the q8_0 cache", p->m_tile);
   pl->narrow = !q8 && (p->m_tile == 16 || (p->m_tile == 0 && M <= 16));
   if (pl->narrow) {
@@ -2737,12 +2384,7 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   } else {
     pl->HG = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   }
-  pl->CG = 4;
-  if (const char* e = getenv("MLA_SPLIT_WAYS")) {   // tuning hook (q8_0): waves per row group
-    const int cg = atoi(e);
-    if (q8 && (cg == 2 || cg == 4)) pl->CG = cg;
-  }
-  if (!q8) pl->CG = 4 / pl->HG;
+  pl->CG = q8 ? 4 : 4 / pl->HG;
   pl->MT = pl->narrow ? 16 : 32 * pl->HG;
   pl->m_tiles = (M + pl->MT - 1) / pl->MT;
   int P = p->num_parts;
@@ -2794,11 +2436,6 @@ hipError_t launch_pipe(const DecodeParams& dp, int grid, hipStream_t stream) {
 
 hipError_t launch_narrow(const DecodeParams& dp, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(mla_decode_narrow_kernel, dim3(grid), dim3(256), 0, stream, dp);
-  return hipGetLastError();
-}
-
-hipError_t launch_quad(const DecodeParams& dp, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_decode_quad_kernel, dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -2906,19 +2543,13 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
     switch (pl.HG) {
       case 1: e = launch_rows<1>(dp, grid, stream); break;
       case 2: e = launch_rows<2>(dp, grid, stream); break;
-      case 4: e = getenv("MLA_ROWS128") ? launch_rows<4>(dp, grid, stream)
-                  : getenv("MLA_QUAD") ? launch_quad(dp, grid, stream)
-                                        : launch_pipe(dp, grid, stream); break;
+      case 4: e = launch_pipe(dp, grid, stream); break;
       default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
     }
+  } else if (pl.HG == 2) {
+    e = launch_decode<2, 4, true>(dp, grid, stream);
   } else {
-    switch (pl.HG * 10 + pl.CG) {
-      case 14: e = launch_decode<1, 4, true>(dp, grid, stream); break;
-      case 12: e = launch_decode<1, 2, true>(dp, grid, stream); break;
-      case 24: e = launch_decode<2, 4, true>(dp, grid, stream); break;
-      case 22: e = launch_decode<2, 2, true>(dp, grid, stream); break;
-      default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
-    }
+    e = launch_decode<1, 4, true>(dp, grid, stream);
   }
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   if (pl.P > 1) {

@@ -45,6 +45,12 @@ SMALL = [
     ("h16_many", 24, 1, 16, [1, 0, 31, 32, 33, 64, 65, 0, 0, 2, 96, 97, 127, 128, 129, 3,
                              0, 191, 300, 1, 63, 0, 20, 257], "permuted", "bf16", 0),
     ("h16_long", 2, 1, 16, [5000, 4161], "permuted", "bf16", 0),
+    # q8_0 64-row tile: two row tiles of causal pairs, a padded row tile, many
+    # short segments and a segment longer than one id window
+    ("h64_pair_q8", 2, 2, 64, [300, 2000], "permuted", "q8_0", 0),
+    ("h40_q8", 3, 1, 40, [65, 700, 33], "permuted", "q8_0", 0),
+    ("h128_q8_many", 12, 1, 128, [1, 0, 31, 33, 64, 65, 130, 0, 2, 300, 97, 5000],
+     "permuted", "q8_0", 0),
 ]
 
 
@@ -192,6 +198,23 @@ def test_empty_pool_poisons_every_nonempty_sequence(H, kvd):
     ls = lse.cpu().numpy()
     assert np.all(np.isnan(ls[[0, 2]])) and np.all(np.isnan(o[[0, 2]]))
     assert np.all(np.isneginf(ls[1])) and np.all(o[1] == 0)
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_q8_late_spike_rescales_accumulated_rows(H):
+    """q8_0: a token far into the sequence scores far above everything before
+    it, so the reference maximum moves after many tiles have accumulated and
+    the accumulators are rescaled; the result is (nearly) that token's row."""
+    w = wl.make_workload("spike", 2, 1, H, [1500, 900], seed=14, table="permuted", kv_dtype="q8_0")
+    d = 7
+    w.q[..., 512 + d] = int(wl.f32_to_bf16_bits(np.float32([32.0]))[0])
+    for b, t in ((0, 1300), (1, 700)):
+        blk, pos = w.block_table[b, t // 64], t % 64
+        w.kv[blk, pos, 512 + d] = 127
+        w.kv_scales[blk, pos, (512 + d) // 32] = int(np.float16(4.0).view(np.uint16))
+    for parts in (1, 0):
+        out, lse, _ = run_gpu(w, num_parts=parts)
+        compare(out, lse, *oracle_rows(w), what=f"q8 late spike H={H} P={parts}")
 
 
 def test_combine_entry_point_matches_the_oracle():
