@@ -2,25 +2,26 @@
 // gfx950 (MI355X). The operation and the C ABI are defined in include/mla.h.
 //
 // Design in brief (CDNA4):
-//  * One workgroup = 4 waves on one CU, processing one KV partition of the
-//    cache for a tile of 32*HG query rows. Waves split the rows in groups of
-//    32 (HG groups) and, when HG < 4, split each group's work CG = 4/HG ways:
-//    the 576-wide score contraction by columns (partial scores summed through
-//    LDS) and the 512-wide value product by output columns.
+//  * One workgroup = 4 waves on one CU (8 for the 64-row q8_0 tile),
+//    processing one KV partition of the cache for a tile of query rows:
+//    16 rows (mla_decode_narrow_kernel), 32 or 64 (mla_decode_rows_kernel),
+//    128 (mla_decode_pipe_kernel) for a bf16 cache; 32 or 64
+//    (mla_decode_kernel) for a q8_0 cache.
 //  * The cache streams through LDS in 32-token tiles (half a 64-token block,
-//    36 KiB), fetched with global_load_lds_dwordx4 (direct to LDS, no VGPRs)
-//    into a 3-stage ring, so two tiles are in flight while one is consumed.
-//  * Scores are computed transposed, S^T = K q~^T, on v_mfma_f32_32x32x16_bf16
-//    with tokens on the M side and heads on the N side. The accumulator then
-//    holds, per lane, 16 tokens of one head: row max / row sum need only one
-//    cross-lane step, and the probabilities P^T are already laid out as the
-//    B operand of the value product O^T += V^T P^T, so P never leaves
-//    registers. V^T operands come from the same LDS tile through
+//    36 KiB in bf16), fetched with global_load_lds_dwordx4 (direct to LDS, no
+//    VGPRs) into a 3- or 4-stage ring, so two or three tiles are in flight
+//    while one is consumed.
+//  * Scores are computed transposed, S^T = K q~^T, with tokens on the M side
+//    and heads on the N side of the MFMA: each lane's accumulator then holds
+//    tokens of one head, which is the B-operand layout of the value product
+//    O^T += V^T P^T. V^T operands come from the same LDS tile through
 //    ds_read_b64_tr_b16 (transposing reads), since V is the latent itself.
-//  * Online softmax in the log2 domain (exp2 on v_exp_f32), fp32 accumulators.
+//  * Online softmax in the log2 domain (exp2 on v_exp_f32), fp32 accumulators,
+//    with a reference maximum that moves rarely (so the accumulators are
+//    rarely rescaled).
 //  * Split-KV: the blocks of all sequences, laid end to end, are cut into P
 //    equal parts (the plan, recomputed from seqlens inside every kernel, so
-//    the host never synchronises). A sequence that spans parts leaves fp32
+//    the host never synchronises). A sequence that spans parts leaves bf16
 //    partials (normalised O and lse) and a second kernel merges them with a
 //    log-sum-exp combine.
 #include <hip/hip_runtime.h>
@@ -254,6 +255,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
+// Decode kernel with the work of each 32-row group split over CG waves (the
+// q8_0 cache: HG = 1 or 2 row groups, CG = 4). The 576-column score
+// contraction is split by columns (partial scores summed through LDS) and the
+// 512-wide value product by output columns. q8_0: the scores are exact (the
+// int8 values are exact in bf16; each 32-column group's partial sum is scaled
+// by its fp16 scale in fp32), and the value product reads an LDS tile of
+// bf16(scale * int8) written once per tile by all threads.
 template <int HG, int CG, bool Q8>
 __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParams a) {
   constexpr int NW = HG * CG;             // waves per workgroup
