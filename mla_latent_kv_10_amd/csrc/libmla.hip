@@ -2157,14 +2157,22 @@ __device__ __forceinline__ void merge_row(int n, PartPtr part, uint16_t* out_row
   if (lane == 0) *lse_out = L;
 }
 
-// Merge the parts of one split row (one wave per row, 8 columns per lane).
-// Every part's lse is loaded at once, one part per lane; the parts' value
-// rows are then read eight at a time, all eight loads in flight together,
-// and weighted by w_s = exp(lse_s - L) with L the merged lse.
-__global__ __launch_bounds__(kThreads) void mla_split_combine_kernel(DecodeParams a) {
+// Merge the parts of one split row (8 columns per lane). WPR = 1: one wave
+// per row; WPR = 4 (sequences cut into many parts, few rows): the four waves
+// of a workgroup share one row, each merging a quarter of its parts, and the
+// four partial sums are added in LDS in a fixed order. Every wave loads every
+// part's lse at once, one part per lane, and its first four parts' value rows
+// in the same round trip (they are needed unless the row is poisoned or
+// empty); later rows are read four at a time. Each row is weighted by
+// w_s = exp(lse_s - L), L the merged lse.
+template <int WPR>
+__global__ __launch_bounds__(kThreads, 8) void mla_split_combine_kernel(DecodeParams a) {
+  static_assert(WPR == 1 || WPR == 4, "waves per row");
+  __shared__ float s_acc[WPR - 1 > 0 ? WPR - 1 : 1][8][64];
   const int b = blockIdx.x;
-  const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (r >= a.M) return;
+  const int wv = uniform(threadIdx.x >> 6);
+  const int r = WPR == 1 ? blockIdx.y * 4 + wv : blockIdx.y;
+  if (r >= a.M) return;   // uniform over the workgroup when WPR = 4
   const int pre_b = a.ws_prefix[b], pre_e = a.ws_prefix[b + 1], T = a.ws_prefix[a.B];
   if (pre_e <= pre_b) return;
   const int fp = part_of(pre_b, a.P, T), lp = part_of(pre_e - 1, a.P, T);
@@ -2173,16 +2181,30 @@ __global__ __launch_bounds__(kThreads) void mla_split_combine_kernel(DecodeParam
   const int lane = threadIdx.x & 63;
   const bool first_shifted = pre_b > part_start(fp, a.P, T);
   auto slot = [&](int s) { return 2 * (fp + s) + ((s == 0 && first_shifted) ? 1 : 0); };
+  auto o_row = [&](int s) {
+    return *reinterpret_cast<const uint4*>(a.part_o + ((int64_t)slot(s) * a.M + r) * kDL + 8 * lane);
+  };
+  auto lse_of = [&](int s) { return a.part_lse[(int64_t)slot(s) * a.M + r]; };
   const int64_t row = (int64_t)b * a.M + r;
   uint16_t* out_row = a.out + row * kDL;
   constexpr float kLog2e = 1.4426950408889634f;
-
+  constexpr int kRound = 4;
+  const int lo = (wv % WPR) * n / WPR, hi = (wv % WPR + 1) * n / WPR;   // this wave's parts
+  // The lse values first, so that waiting for them leaves the value rows in
+  // flight. Both are read without branches (indexes clamped to the last part,
+  // n >= 2 here): loads behind branches would make the compiler wait for all
+  // of them at the join.
+  const float lse_raw = lse_of(min(lane, n - 1));
+  uint4 v[kRound];
+#pragma unroll
+  for (int j = 0; j < kRound; ++j) v[j] = o_row(min(lo + j, n - 1));
+  const float lse0 = lane < n ? lse_raw : -INFINITY;   // parts 0..63
   // max (and NaN) over the parts' lse
-  float m = -INFINITY;
-  bool has_nan = false;
-  for (int s0 = 0; s0 < n; s0 += 64) {
+  float m = lse0;
+  bool has_nan = isnan(lse0);
+  for (int s0 = 64; s0 < n; s0 += 64) {
     const int s = s0 + lane;
-    const float l = s < n ? a.part_lse[(int64_t)slot(s) * a.M + r] : -INFINITY;
+    const float l = s < n ? lse_of(s) : -INFINITY;
     has_nan |= isnan(l);
     m = fmaxf(m, l);
   }
@@ -2190,6 +2212,7 @@ __global__ __launch_bounds__(kThreads) void mla_split_combine_kernel(DecodeParam
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   has_nan = __any(has_nan);
   if (has_nan || m == -INFINITY) {
+    if (wv % WPR != 0) return;
     const float fill = has_nan ? __builtin_nanf("") : 0.f;
     const uint32_t h = f32_to_bf16_bits(fill);
     const uint32_t w = h | (h << 16);
@@ -2198,44 +2221,53 @@ __global__ __launch_bounds__(kThreads) void mla_split_combine_kernel(DecodeParam
     return;
   }
   // merged lse
-  float tot = 0.f;
-  for (int s0 = 0; s0 < n; s0 += 64) {
+  float tot = lane < n ? __builtin_amdgcn_exp2f((lse0 - m) * kLog2e) : 0.f;
+  for (int s0 = 64; s0 < n; s0 += 64) {
     const int s = s0 + lane;
-    if (s < n) tot += __builtin_amdgcn_exp2f((a.part_lse[(int64_t)slot(s) * a.M + r] - m) * kLog2e);
+    if (s < n) tot += __builtin_amdgcn_exp2f((lse_of(s) - m) * kLog2e);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
   const float L = m + __log2f(tot) * 0.69314718055994531f;
-
+  // weights of parts 0..63, part i in lane i; later parts' weights are
+  // computed when they are used
+  const float wl0 = lane < n ? __builtin_amdgcn_exp2f((lse0 - L) * kLog2e) : 0.f;
+  auto weight_of = [&](int s) {
+    if (s < 64) return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl0), s));
+    return __builtin_amdgcn_exp2f((lse_of(s) - L) * kLog2e);
+  };
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int s0 = 0; s0 < n; s0 += 64) {
-    const int nr = min(64, n - s0);
-    // this round's weights, part s0 + i in lane i
-    const float wl = lane < nr
-        ? __builtin_amdgcn_exp2f((a.part_lse[(int64_t)slot(s0 + lane) * a.M + r] - L) * kLog2e)
-        : 0.f;
-    for (int c0 = 0; c0 < nr; c0 += 8) {
-      uint4 v[8];
+  for (int c0 = lo; c0 < hi; c0 += kRound) {
+    if (c0 != lo) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (c0 + j < nr)
-          v[j] = *reinterpret_cast<const uint4*>(
-              a.part_o + ((int64_t)slot(s0 + c0 + j) * a.M + r) * kDL + 8 * lane);
+      for (int j = 0; j < kRound; ++j) v[j] = o_row(min(c0 + j, n - 1));
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (c0 + j < nr) {
-          const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), c0 + j));
-          const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    for (int j = 0; j < kRound; ++j) {
+      if (c0 + j < hi) {
+        const float w = weight_of(c0 + j);
+        const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += w * __builtin_bit_cast(float, u[e] << 16);
-            acc[2 * e + 1] += w * __builtin_bit_cast(float, u[e] & 0xffff0000u);
-          }
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += w * __builtin_bit_cast(float, u[e] << 16);
+          acc[2 * e + 1] += w * __builtin_bit_cast(float, u[e] & 0xffff0000u);
         }
       }
     }
+  }
+  if constexpr (WPR > 1) {
+    if (wv > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[wv - 1][e][lane] = acc[e];
+    }
+    __syncthreads();
+    if (wv > 0) return;
+#pragma unroll
+    for (int k = 0; k < WPR - 1; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += s_acc[k][e][lane];
   }
   uint4 pk;
   pk.x = f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
@@ -2561,8 +2593,12 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
   }
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   if (pl.P > 1) {
-    hipLaunchKernelGGL(mla_split_combine_kernel, dim3(p->batch, (pl.M + 3) / 4), dim3(kThreads), 0,
-                       stream, dp);
+    // few rows with many parts each: four waves per row
+    if ((int64_t)pl.P >= 16 * (int64_t)p->batch)
+      hipLaunchKernelGGL(mla_split_combine_kernel<4>, dim3(p->batch, pl.M), dim3(kThreads), 0, stream, dp);
+    else
+      hipLaunchKernelGGL(mla_split_combine_kernel<1>, dim3(p->batch, (pl.M + 3) / 4), dim3(kThreads), 0,
+                         stream, dp);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   }

@@ -141,7 +141,7 @@ def test_one_hot_probe_returns_the_exact_row(H):
 @pytest.mark.parametrize("H", [16, 8])
 def test_empty_rows_and_causal_visibility(H):
     w = wl.make_workload("deg", 4, 2, H, [0, 1, 2, 130], seed=9, table="permuted")
-    for parts in (1, 3):
+    for parts in (1, 3, 64):   # 64: the combine's four-waves-per-row form
         out, lse, _ = run_gpu(w, num_parts=parts)
         compare(out, lse, *oracle_rows(w), what=f"degenerate P={parts}")
         assert np.all(np.isneginf(lse[0])) and np.all(out[0] == 0)
@@ -151,7 +151,7 @@ def test_empty_rows_and_causal_visibility(H):
 def test_invalid_block_ids_poison_only_their_sequence():
     w = wl.make_workload("bad", 3, 1, 128, [300, 300, 300], seed=10)
     w.block_table[1, 2] = w.num_blocks + 5
-    for parts in (1, 4):
+    for parts in (1, 4, 48):   # 48: the combine's four-waves-per-row form
         out, lse, _ = run_gpu(w, num_parts=parts)
         compare(out, lse, *oracle_rows(w), what=f"invalid ids P={parts}")
         assert np.all(np.isnan(lse[1])) and np.all(np.isnan(out[1]))
@@ -165,7 +165,7 @@ def test_invalid_block_id_in_a_later_id_window():
     window of a long segment poisons that sequence only."""
     w = wl.make_workload("bad2", 3, 1, 16, [300, 4500, 700], seed=11)
     w.block_table[1, 66] = w.num_blocks + 1
-    for parts in (1, 3):
+    for parts in (1, 3, 48):
         out, lse, _ = run_gpu(w, num_parts=parts)
         compare(out, lse, *oracle_rows(w), what=f"invalid id, later window P={parts}")
         assert np.all(np.isnan(lse[1])) and np.all(np.isnan(out[1]))
