@@ -508,30 +508,66 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
         // values themselves (exact in bf16), each 32-column group's partial
         // sum times that token's fp16 scale in fp32.
         __builtin_amdgcn_sched_barrier(0);
-        f32x16 snt, accg;
+        f32x16 snt;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) snt[i] = accg[i] = 0.f;
+        for (int i = 0; i < 16; ++i) snt[i] = 0.f;
         const LDS_AS uint8_t* srow = st + kQ8TileBytes + l32 * kQ8ScaleRowBytes;
+        const LDS_AS uint8_t* kraw = st + (32 * cg * KS + l32) * 16 + 8 * hi;
+        // The wave's k-steps s = cg KS + ks cover columns 16s .. 16s+15; a
+        // group (32 columns) is k-steps 2g, 2g+1. PAR = parity of the wave's
+        // first k-step fixes, at compile time, where its groups start and end.
+        // Each group accumulates from zero into one of two accumulators, and
+        // is scaled into the scores one k-step after its last MFMA, so the
+        // scaling never waits for the matrix core. The raw operands are read
+        // two k-steps ahead.
+        auto score_steps = [&](auto parc) {
+          constexpr int PAR = decltype(parc)::value;
+          f32x16 acc[2];
+          uint64_t raw[KS];
+          float dg[2] = {0.f, 0.f};
+          raw[0] = *reinterpret_cast<const LDS_AS uint64_t*>(kraw);
+          if constexpr (KS > 1) raw[1] = *reinterpret_cast<const LDS_AS uint64_t*>(kraw + 512);
+          auto scale_of = [&](int ks) {
+            const uint16_t sbits = *reinterpret_cast<const LDS_AS uint16_t*>(
+                srow + ((cg * KS + ks) >> 1) * 2);
+            return (float)__builtin_bit_cast(_Float16, sbits);
+          };
+          auto flush = [&](int buf, float d) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int s = cg * KS + ks;              // columns 16s .. 16s+15
-          const uint64_t raw = *reinterpret_cast<const LDS_AS uint64_t*>(
-              st + (32 * s + l32) * 16 + 8 * hi);
-          bf16x8 kf;
+            for (int i = 0; i < 16; ++i) snt[i] += d * acc[buf][i];
+          };
+          // group boundaries and accumulator buffers, all known at compile time
+          constexpr auto starts = [](int ks) { return ks == 0 || ((PAR + ks) & 1) == 0; };
+          constexpr auto ends = [](int ks) { return ks == KS - 1 || ((PAR + ks) & 1) == 1; };
+          constexpr auto buf_of = [](int ks) {
+            int n = -1;
+            for (int j = 0; j <= ks; ++j) n += (j == 0 || ((PAR + j) & 1) == 0) ? 1 : 0;
+            return n & 1;
+          };
+          unroll<KS>([&](auto kc) {
+            constexpr int ks = decltype(kc)::value;
+            constexpr int buf = buf_of(ks);
+            if constexpr (ks + 2 < KS)
+              raw[ks + 2] = *reinterpret_cast<const LDS_AS uint64_t*>(kraw + 512 * (ks + 2));
+            bf16x8 kf;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) kf[e] = (__bf16)(float)(int8_t)(raw >> (8 * e));
-          accg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, accg, 0, 0, 0);
-          if ((s & 1) || ks == KS - 1) {           // group s/2 done for this wave
-            const uint16_t sbits =
-                *reinterpret_cast<const LDS_AS uint16_t*>(srow + (s >> 1) * 2);
-            const float d = (float)__builtin_bit_cast(_Float16, sbits);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              snt[i] += d * accg[i];
-              accg[i] = 0.f;
+            for (int e = 0; e < 8; ++e) kf[e] = (__bf16)(float)(int8_t)(raw[ks] >> (8 * e));
+            if constexpr (starts(ks)) {
+              const f32x16 zero = {};
+              acc[buf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, zero, 0, 0, 0);
+              dg[buf] = scale_of(ks);
+            } else {
+              acc[buf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, acc[buf], 0, 0, 0);
             }
-          }
-        }
+            // the group that ended one k-step ago is scaled now
+            if constexpr (ks > 0 && ends(ks - 1)) flush(buf_of(ks - 1), dg[buf_of(ks - 1)]);
+          });
+          flush(buf_of(KS - 1), dg[buf_of(KS - 1)]);
+        };
+        if (cg & 1)
+          score_steps(std::integral_constant<int, (KS & 1)>{});
+        else
+          score_steps(std::integral_constant<int, 0>{});
         // transpose through LDS, summing the CG partials for this slice
         float* mine = s_sx[wave];
 #pragma unroll
