@@ -224,6 +224,16 @@ __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, ui
                : "memory", "m0");
 }
 
+// The same copy with the non-temporal cache policy: the line is not kept in
+// L2 for reuse. Only for copies that read whole 128-byte lines each (a line
+// read in pieces by several instructions would be fetched once per piece).
+__device__ __forceinline__ void dma16_sbase_nt(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // f(std::integral_constant<int, I>) for I = 0 .. N-1, fully unrolled.
 template <typename F, int... I>
 __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>) {
@@ -1337,23 +1347,35 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
   const int q_i = row_ok ? r / a.H : 0;
   const int ks0 = 4 * wave + min(wave, 2);   // first k-step of this wave
   const bool five = wave < 2;                // waves 0, 1 take five k-steps
+  // Tile layout of this kernel (row groups): the tile is cut into 36 blocks
+  // of 8 tokens x 8 chunks (16-byte units, 8 columns each), block
+  // 4 C + R holding tokens 8R..8R+7 and chunks 8C..8C+7 at 1 KiB per block.
+  // Inside a block, token 8R + r and chunk 8C + c sit at unit
+  // r | ((R ^ c) & 1) << 3 | (c >> 1) << 4 (c taken mod 8). One LDS-DMA copy
+  // fills one block from eight whole 128-byte lines, so the copies can use the
+  // non-temporal policy; the reads below touch 16 (score) or 32 (value)
+  // different 16-byte bank groups per access, i.e. no bank conflicts.
+  //
   // Score operand (A, tokens x columns): token 16 tb + i16, columns
-  // 32 ks + 8 g .. +7 = unit 32 (4 ks + g) + (token ^ 4 g); tb = 1 adds 256.
-  const int kofs = 512 * g + 16 * (i16 ^ (4 * g));
+  // 32 ks + 8 g .. +7 (chunk 4 ks + g): byte 4096 (ks >> 1) + 512 (ks & 1)
+  // + kofs; tb = 1 adds 2048.
+  const int kofs = 1024 * (i16 >> 3) + 16 * (i16 & 7) + 128 * ((i16 >> 3) ^ (g & 1)) +
+                   256 * (g >> 1);
   // Value operand (A, columns x tokens), transposing reads: lane 4 s + q of
   // group g points at token 4 g + s (+16 for the second read), columns
-  // 128 w + 16 ct + 4 q .. +3, i.e. chunk 16 w + 2 ct + (q >> 1).
+  // 128 w + 16 ct + 4 q .. +3, i.e. chunk 16 w + 2 ct + (q >> 1): byte
+  // vb[h] + 4096 (ct >> 2) + 256 (ct & 3).
   const int vs = i16 >> 2, vq = i16 & 3;
-  int vb[2][2];
+  int vb[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      vb[par][h] = 8192 * wave + 512 * (vq >> 1) +
-                   16 * ((16 * h + 4 * g + vs) ^ (4 * (2 * par + (vq >> 1)))) + 8 * (vq & 1);
-  // LDS-DMA: load j of this wave fills units 64 k .. 64 k + 63, k = wave + 4 j
-  const int dchunk = 2 * wave + (lane >> 5), dl32 = lane & 31;
-  const uint32_t doff = (uint32_t)((dl32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
+  for (int h = 0; h < 2; ++h)
+    vb[h] = 8192 * wave + 2048 * h + 1024 * (g >> 1) + 16 * (4 * (g & 1) + vs) +
+            128 * ((g >> 1) ^ (vq >> 1)) + 8 * (vq & 1);
+  // LDS-DMA: copy j of wave w fills block 4 j + w (tokens 8w..8w+7, chunks
+  // 8j..8j+7); lane l takes token 8w + (l & 7), chunk 8j + c with
+  // c = 2 (l >> 4) + (((l >> 3) ^ w) & 1), which lands at unit l of the block.
+  const uint32_t doff = (uint32_t)((8 * wave + (lane & 7)) * kRowBytes +
+                                   16 * (2 * (lane >> 4) + (((lane >> 3) ^ wave) & 1)));
 
   // ---- segments: the part's share of sequences b_first .. b_last
   auto make_seg = [&](int b, int pre_b) {
@@ -1451,14 +1473,14 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
     uint32_t dst;
     next_tile(src, dst);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) dma16_sbase(src + 128 * j, doff, dst + 4096 * j);
+    for (int j = 0; j < LPW; ++j) dma16_sbase_nt(src + 128 * j, doff, dst + 4096 * j);
   };
   // Tokens past the end of the sequence in its last tile are cleared, so that
   // whatever unused cache slots hold cannot reach the value product.
   auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
     for (int u = tid; u < kTile * 72; u += NT) {
-      const int c = u >> 5, pos = u & 31;
-      if ((pos ^ (4 * (c & 3))) >= valid)
+      const int token = 8 * ((u >> 6) & 3) + (u & 7);
+      if (token >= valid)
         *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
@@ -1508,9 +1530,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
 #pragma unroll
       for (int j = 0; j < KQ; ++j) {
         if (j == KQ - 1 && !five) break;
-        const LDS_AS uint8_t* kp = st + 2048 * (ks0 + j) + kofs;
+        const int ks = ks0 + j;
+        const LDS_AS uint8_t* kp = st + 4096 * (ks >> 1) + 512 * (ks & 1) + kofs;
         kf[2 * j] = lds_read_b128(kp);
-        kf[2 * j + 1] = lds_read_b128(kp + 256);
+        kf[2 * j + 1] = lds_read_b128(kp + 2048);
       }
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1519,11 +1542,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[2 * j], qf[j], acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[2 * j + 1], qf[j], acc1, 0, 0, 0);
         if (j < 4 && do_iss) {
-          dma16_sbase(isrc + 256 * j, doff, idst + 8192 * j);
-          dma16_sbase(isrc + 256 * j + 128, doff, idst + 8192 * j + 4096);
+          dma16_sbase_nt(isrc + 256 * j, doff, idst + 8192 * j);
+          dma16_sbase_nt(isrc + 256 * j + 128, doff, idst + 8192 * j + 4096);
         }
       }
-      if (do_iss) dma16_sbase(isrc + 128 * (LPW - 1), doff, idst + 4096 * (LPW - 1));
+      if (do_iss) dma16_sbase_nt(isrc + 128 * (LPW - 1), doff, idst + 4096 * (LPW - 1));
       s_x[wave][0][lane] = acc0;
       s_x[wave][1][lane] = acc1;
       lds_barrier();   // partials visible (and the cleared tail)
@@ -1531,7 +1554,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
       bf16x8 vf[8];
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
-        vf[ct] = vt_fragment(st + vb[ct & 1][0] + 1024 * ct, st + vb[ct & 1][1] + 1024 * ct);
+        vf[ct] = vt_fragment(st + vb[0] + 4096 * (ct >> 2) + 256 * (ct & 3),
+                             st + vb[1] + 4096 * (ct >> 2) + 256 * (ct & 3));
       // the four partials as (p[w] + p[w^1]) + (p[w^2] + p[w^3]), this wave's
       // own from registers: addition commutes, so every wave forms the same
       // pairs and holds the same sums
