@@ -1692,6 +1692,23 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
 }
 
+// Row-group tile layout of the 128-row kernel: block 4 C + R (1 KiB) holds
+// tokens 8R..8R+7 and chunks 8C..8C+7 (16-byte units); token 8R + r, chunk
+// 8C + c sits in its block at unit (r & 3) | ((r >> 2) ^ c) & 1) << 2 |
+// ((R ^ (c >> 1)) & 1) << 3 | (c & 1) << 4 | (c >> 2 & 1) << 5. Every LDS-DMA
+// copy fills one block from eight whole 128-byte lines, and the score reads
+// (32 tokens x two chunks) and the transposing value reads (4 tokens x 4
+// chunks per 32 lanes) each hit distinct 16-byte bank groups.
+__device__ __forceinline__ int rg_unit(int t, int c) {
+  const int R = t >> 3, r = t & 7, C = c >> 3, cc = c & 7;
+  return 64 * (4 * C + R) + ((r & 3) | ((((r >> 2) ^ cc) & 1) << 2) |
+                             (((R ^ (cc >> 1)) & 1) << 3) | ((cc & 1) << 4) |
+                             (((cc >> 2) & 1) << 5));
+}
+// Byte offset of score k-step k (chunks 2k, 2k+1) that does not depend on
+// the lane.
+__device__ __forceinline__ constexpr int kstep_ofs(int k) { return 4096 * (k >> 2) + 512 * ((k >> 1) & 1); }
+
 // --------------------------- bf16 decode kernel (128-row tile, pipelined)
 
 // 128 query rows per workgroup, so every cache tile is streamed into exactly
@@ -1710,13 +1727,22 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
 // when a row's does, its owner publishes the factor and every wave rescales
 // that row's accumulators. The plan prefix and the epilogue's scratch live in
 // ring space that is idle at those times, which keeps LDS under 160 KiB.
+template <bool NT>
 __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a) {
   constexpr int NW = 4;
-  constexpr int NT = 64 * NW;
+  constexpr int NTH = 64 * NW;
   constexpr int MT = 128;
   constexpr int NST = 4;                  // ring stages
   constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
   constexpr int KPF = 3;                  // score operands in flight
+  // LDS-DMA copy of one block (NT: non-temporal, when no other workgroup
+  // reads the same tiles)
+  auto copy = [](const void* src, uint32_t off, uint32_t dst) {
+    if constexpr (NT)
+      dma16_sbase_nt(src, off, dst);
+    else
+      dma16_sbase(src, off, dst);
+  };
 
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NST][kTileBytes];
   __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];   // P, B-operand layout
@@ -1735,11 +1761,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   if ((G & 7) == 0) v = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int part = v / a.m_tiles, mt = v % a.m_tiles;
 
-  plan_prefix<NT>(a.seqlens, a.B, a.max_blocks, s_pre, s_misc);
+  plan_prefix<NTH>(a.seqlens, a.B, a.max_blocks, s_pre, s_misc);
   const int T = uniform(s_pre[a.B]);
   const int P = a.P;
   if (blockIdx.x == 0)
-    for (int b = tid; b <= a.B; b += NT) a.ws_prefix[b] = s_pre[b];
+    for (int b = tid; b <= a.B; b += NTH) a.ws_prefix[b] = s_pre[b];
   const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
 
   if (tid == 0) {
@@ -1747,7 +1773,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     s_misc[9] = -1;
   }
   __syncthreads();
-  for (int b = tid; b < a.B; b += NT) {
+  for (int b = tid; b < a.B; b += NTH) {
     const int lo = s_pre[b], hi2 = s_pre[b + 1];
     bool mine;
     if (hi2 > lo) {
@@ -1778,15 +1804,28 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     const int r = mt * MT + 32 * wave + l32;   // row whose scores this lane computes
     const bool row_ok = r < a.M;
     const int q_i = row_ok ? r / a.H : 0;
-    const int kofs0 = 16 * tile_unit(l32, hi);
-    const int kofs1 = 16 * tile_unit(l32, 2 + hi) - 1024;
+    // Score operand of k-step k (token l32, chunk 2k + hi): byte
+    // 4096 (k >> 2) + 512 ((k >> 1) & 1) + (k odd ? kofs1 : kofs0).
+    const int kR = l32 >> 3, kr = l32 & 7;
+    const int kpart = 1024 * kR + 16 * ((kr & 3) | ((((kr >> 2) ^ hi) & 1) << 2) | (hi << 4));
+    const int kofs0 = kpart + 128 * (kR & 1);
+    const int kofs1 = kpart + 128 * ((kR & 1) ^ 1);
+    // Value operand (transposing reads): lane (g16, i16) points at token
+    // 4 vh + vs (+8 for the second read, +16 kk), chunk
+    // 16 w + 4 cb + 2 (g16 & 1) + (vq >> 1), half vq & 1: byte
+    // vofs{0,1} + 4096 (cb >> 1) + 512 (cb & 1) + 2048 kk.
     const int g16 = lane >> 4, i16 = lane & 15;
     const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
-    const int vc = cbase / 8 + 2 * (g16 & 1) + (vq >> 1);
-    const int vofs0 = 16 * tile_unit(4 * vh + vs, vc) + 8 * (vq & 1);
-    const int vofs1 = 16 * tile_unit(8 + 4 * vh + vs, vc) + 8 * (vq & 1);
-    const int dchunk = 2 * wave + hi;
-    const uint32_t doff = (uint32_t)((l32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
+    const int vlane = 8192 * wave + 16 * vs + 64 * (vh ^ (vq >> 1)) + 256 * (vq >> 1) + 8 * (vq & 1);
+    const int vofs0 = vlane + 128 * (g16 & 1);
+    const int vofs1 = vlane + 1024 + 128 * ((g16 & 1) ^ 1);
+    // LDS-DMA: copy j of wave w fills block 4 j + w (tokens 8w..8w+7, chunks
+    // 8j..8j+7) from eight whole 128-byte lines; lane l's token and chunk
+    // invert the in-block placement so that it lands at unit l.
+    const int dc0 = (lane >> 4) & 1;
+    const int dr = (lane & 3) | ((((lane >> 2) & 1) ^ dc0) << 2);
+    const int dcc = dc0 | ((((lane >> 3) ^ wave) & 1) << 1) | (((lane >> 5) & 1) << 2);
+    const uint32_t doff = (uint32_t)((8 * wave + dr) * kRowBytes + 16 * dcc);
 
     const int L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
     const int pre_e = pre_b + (L + kBT - 1) / kBT;
@@ -1849,12 +1888,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       const uint32_t dst = lds_addr_of(s_stage[idx % NST]) + 1024 * wave;
       const uint8_t* src = tile_src(idx);
 #pragma unroll
-      for (int j = 0; j < LPW; ++j) dma16_sbase(src + 128 * j, doff, dst + 4096 * j);
+      for (int j = 0; j < LPW; ++j) copy(src + 128 * j, doff, dst + 4096 * j);
     };
     auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
-      for (int u = tid; u < kTile * 72; u += NT) {
-        const int c = u >> 5, pos = u & 31;
-        if ((pos ^ (4 * (c & 3))) >= valid)
+      for (int u = tid; u < kTile * 72; u += NTH) {
+        const int c0 = (u >> 4) & 1;
+        const int token = 8 * ((u >> 6) & 3) + ((u & 3) | ((((u >> 2) & 1) ^ c0) << 2));
+        if (token >= valid)
           *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     };
@@ -1893,7 +1933,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         int t = 0, c = lane;
 #pragma unroll
         for (int j = 0; j < 36; ++j) {
-          *reinterpret_cast<LDS_AS u32x4*>(stq + 16 * (32 * c + (t ^ (4 * (c & 3))))) = raw[j];
+          *reinterpret_cast<LDS_AS u32x4*>(stq + 16 * rg_unit(t, c)) = raw[j];
           c += 64;
           if (c >= 72) { c -= 72; ++t; }
         }
@@ -1901,7 +1941,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         const uint32_t keep = row_ok ? 0xffffffffu : 0u;
 #pragma unroll
         for (int s2 = 0; s2 < 36; ++s2) {
-          const u32x4 z = __builtin_bit_cast(u32x4, lds_read_b128(stq + 1024 * s2 + ((s2 & 1) ? kofs1 : kofs0)));
+          const u32x4 z = __builtin_bit_cast(u32x4, lds_read_b128(stq + kstep_ofs(s2) + ((s2 & 1) ? kofs1 : kofs0)));
           qf[s2] = __builtin_bit_cast(bf16x8, (z ^ sg) & keep);
         }
       }
@@ -1910,7 +1950,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       issue(1);
       // "tile -1" (value product before the first tile) reads stage 3 with
       // P = 0: both are zero-filled so that it adds exact zeros
-      for (int u = tid; u < kTileBytes / 16; u += NT)
+      for (int u = tid; u < kTileBytes / 16; u += NTH)
         *reinterpret_cast<LDS_AS f32x4*>((LDS_AS uint8_t*)s_stage[3] + 16 * u) =
             f32x4{0.f, 0.f, 0.f, 0.f};
       s_p[wave][0][lane] = u32x4{0u, 0u, 0u, 0u};
@@ -1927,7 +1967,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     // latency is not exposed at the start of the score chain.
     bf16x8 kf[KPF];
     auto rd_at = [&](int t, int k) {
-      return lds_read_b128((const LDS_AS uint8_t*)s_stage[t % NST] + 1024 * k + ((k & 1) ? kofs1 : kofs0));
+      return lds_read_b128((const LDS_AS uint8_t*)s_stage[t % NST] + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0));
     };
     if (n_run > 0) {
       wait_vmcnt<LPW>();          // tile 0 landed; tile 1 may be in flight
@@ -1953,9 +1993,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       // rb = q % 4: O^T block (rb, cb) += V^T (column block cb, token half kk)
       // x P^T (rows of wave rb, token half kk)
       f32x16 s;
-      auto rd = [&](int k) { return lds_read_b128(st + 1024 * k + ((k & 1) ? kofs1 : kofs0)); };
+      auto rd = [&](int k) { return lds_read_b128(st + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0)); };
       auto vread = [&](int kk, int cb) {
-        return vt_fragment(sp + vofs0 + 2048 * cb + 256 * kk, sp + vofs1 + 2048 * cb + 256 * kk);
+        const int o = 4096 * (cb >> 1) + 512 * (cb & 1) + 2048 * kk;
+        return vt_fragment(sp + vofs0 + o, sp + vofs1 + o);
       };
       bf16x8 pf[4], va[2];   // value operands, loaded in phase A's last third
       auto pv_step = [&](auto qc) {
@@ -1987,7 +2028,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         if constexpr (k >= 24 && k < 28) pf[k - 24] = __builtin_bit_cast(bf16x8, s_p[k - 24][0][lane]);
         if constexpr (k == 29) va[0] = vread(0, 0);
         if constexpr (k == 31) va[1] = vread(0, 1);
-        if constexpr ((k & 3) == 1) dma16_sbase(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
+        if constexpr ((k & 3) == 1) copy(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
         __builtin_amdgcn_sched_barrier(0);
       });
       mfma_vgpr_drain(s);
@@ -2530,7 +2571,10 @@ hipError_t launch_decode(const DecodeParams& dp, int grid, hipStream_t stream) {
 }
 
 hipError_t launch_pipe(const DecodeParams& dp, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_decode_pipe_kernel, dim3(grid), dim3(256), 0, stream, dp);
+  if (dp.m_tiles == 1)
+    hipLaunchKernelGGL(mla_decode_pipe_kernel<true>, dim3(grid), dim3(256), 0, stream, dp);
+  else
+    hipLaunchKernelGGL(mla_decode_pipe_kernel<false>, dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
