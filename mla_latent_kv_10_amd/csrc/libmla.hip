@@ -10,7 +10,9 @@
 //  * The cache streams through LDS in 32-token tiles (half a 64-token block,
 //    36 KiB in bf16), fetched with global_load_lds_dwordx4 (direct to LDS, no
 //    VGPRs) into a 3- or 4-stage ring, so two or three tiles are in flight
-//    while one is consumed.
+//    while one is consumed. In the 128- and 16-row kernels each copy
+//    instruction reads eight whole 128-byte lines (row-group tile layouts),
+//    which allows the non-temporal cache policy for tiles read only once.
 //  * Scores are computed transposed, S^T = K q~^T, with tokens on the M side
 //    and heads on the N side of the MFMA: each lane's accumulator then holds
 //    tokens of one head, which is the B-operand layout of the value product
@@ -157,8 +159,8 @@ __device__ __forceinline__ bf16x8 vt_fragment(const LDS_AS uint8_t* p0, const LD
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// LDS tile layout (bf16, 32 tokens x 576 columns = 36 KiB): chunk-major in
-// 16-byte units (8 columns of one token). Unit 32c + (t ^ 4(c & 3)) holds
+// LDS tile layout of the 32/64-row and q8_0 kernels (bf16, 32 tokens x 576
+// columns = 36 KiB): chunk-major in 16-byte units (8 columns of one token). Unit 32c + (t ^ 4(c & 3)) holds
 // columns 8c..8c+7 of token t. Reading one chunk row for 32 tokens (the
 // score operand) covers 512 contiguous bytes; the XOR spreads the four
 // chunks a 32-lane half touches in a transposing read (the value operand)
