@@ -871,6 +871,23 @@ __device__ __forceinline__ void acc_scale4(f32x4& acc, float alpha) {
   }
 }
 
+// Row-group tile layout of the 128-row kernel: block 4 C + R (1 KiB) holds
+// tokens 8R..8R+7 and chunks 8C..8C+7 (16-byte units); token 8R + r, chunk
+// 8C + c sits in its block at unit (r & 3) | ((r >> 2) ^ c) & 1) << 2 |
+// ((R ^ (c >> 1)) & 1) << 3 | (c & 1) << 4 | (c >> 2 & 1) << 5. Every LDS-DMA
+// copy fills one block from eight whole 128-byte lines, and the score reads
+// (32 tokens x two chunks) and the transposing value reads (4 tokens x 4
+// chunks per 32 lanes) each hit distinct 16-byte bank groups.
+__device__ __forceinline__ int rg_unit(int t, int c) {
+  const int R = t >> 3, r = t & 7, C = c >> 3, cc = c & 7;
+  return 64 * (4 * C + R) + ((r & 3) | ((((r >> 2) ^ cc) & 1) << 2) |
+                             (((R ^ (cc >> 1)) & 1) << 3) | ((cc & 1) << 4) |
+                             (((cc >> 2) & 1) << 5));
+}
+// Byte offset of score k-step k (chunks 2k, 2k+1) that does not depend on
+// the lane.
+__device__ __forceinline__ constexpr int kstep_ofs(int k) { return 4096 * (k >> 2) + 512 * ((k >> 1) & 1); }
+
 // ------------------------------------------------- bf16 decode kernel (rows)
 
 // One workgroup = 4 waves (one per SIMD) on one KV partition for a tile of
@@ -887,7 +904,7 @@ __device__ __forceinline__ void acc_scale4(f32x4& acc, float alpha) {
 // scores run, and two tiles in flight. The score product of tile i+1 is
 // issued before the softmax of tile i, so the exponentials overlap MFMA work
 // of the same wave.
-template <int HG>
+template <int HG, bool NTC>
 __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a) {
   constexpr int NW = 4;
   constexpr int NT = 64 * NW;
@@ -950,24 +967,35 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
   const int q_i = row_ok ? r / a.H : 0;
   const int cbase = cg * (kDL / CG);         // first output column of this wave
 
-  // Score operand of k-step s: chunk 2s + hi of token l32, at
-  // 1024 s + kofs[s & 1] (tile_unit layout).
-  const int kofs0 = 16 * tile_unit(l32, hi);
-  const int kofs1 = 16 * tile_unit(l32, 2 + hi) - 1024;
+  // Tiles use the row-group layout of the 128-row kernel (rg_unit): score
+  // operand of k-step s (chunk 2s + hi of token l32) at byte
+  // kstep_ofs(s) + (s odd ? kofs1 : kofs0).
+  const int kR = l32 >> 3, kr = l32 & 7;
+  const int kpart = 1024 * kR + 16 * ((kr & 3) | ((((kr >> 2) ^ hi) & 1) << 2) | (hi << 4));
+  const int kofs0 = kpart + 128 * (kR & 1);
+  const int kofs1 = kpart + 128 * ((kR & 1) ^ 1);
   // Value operand: lane (g16, i16) of column block ct, token half kk points
   // at token 16 kk + 4 (g16 >> 1) + (i16 >> 2) (+8 for the second read),
-  // columns cbase + 32 ct + 16 (g16 & 1) + 4 (i16 & 3) .. +3.
+  // columns cbase + 32 ct + 16 (g16 & 1) + 4 (i16 & 3) .. +3: byte
+  // vofs{0,1} + vct_ofs(ct) + 2048 kk.
   const int g16 = lane >> 4, i16 = lane & 15;
   const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
-  const int vc = cbase / 8 + 2 * (g16 & 1) + (vq >> 1);
-  const int vofs0 = 16 * tile_unit(4 * vh + vs, vc) + 8 * (vq & 1);
-  const int vofs1 = 16 * tile_unit(8 + 4 * vh + vs, vc) + 8 * (vq & 1);
-  // LDS-DMA: load j of this wave fills units 64k .. 64k+63, k = wave + 4j,
-  // i.e. chunk c = 2k + hi for token position l32, which holds token
-  // l32 ^ 4(c & 3). (c & 3) does not depend on j, so the source offset is
-  // doff + 128 j and the destination 1024 k.
-  const int dchunk = 2 * wave + hi;
-  const uint32_t doff = (uint32_t)((l32 ^ (4 * (dchunk & 3))) * kRowBytes + dchunk * 16);
+  const int vlane = 64 * cbase + 16 * vs + 64 * (vh ^ (vq >> 1)) + 256 * (vq >> 1) + 8 * (vq & 1);
+  const int vofs0 = vlane + 128 * (g16 & 1);
+  const int vofs1 = vlane + 1024 + 128 * ((g16 & 1) ^ 1);
+  // LDS-DMA: copy j of wave w fills block 4 j + w from eight whole 128-byte
+  // lines (as in the 128-row kernel).
+  const int dc0 = (lane >> 4) & 1;
+  const int dr = (lane & 3) | ((((lane >> 2) & 1) ^ dc0) << 2);
+  const int dcc = dc0 | ((((lane >> 3) ^ wave) & 1) << 1) | (((lane >> 5) & 1) << 2);
+  const uint32_t doff = (uint32_t)((8 * wave + dr) * kRowBytes + 16 * dcc);
+  auto copy = [](const void* src, uint32_t off, uint32_t dst) {
+    if constexpr (NTC)
+      dma16_sbase_nt(src, off, dst);
+    else
+      dma16_sbase(src, off, dst);
+  };
+  auto vct_ofs = [](int ct) { return 4096 * (ct >> 1) + 512 * (ct & 1); };
 
   for (int b = b_first; b <= b_last; ++b) {
     const int pre_b = uniform(s_pre[b]), pre_e = uniform(s_pre[b + 1]);
@@ -1028,15 +1056,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
       next_phys = block_of(idx + 1);
       const uint8_t* src = a.kv + (phys * kBT + (tt & 1) * kTile) * kRowBytes;
 #pragma unroll
-      for (int j = 0; j < LPW; ++j) dma16_sbase(src + 128 * j, doff, dst + 4096 * j);
+      for (int j = 0; j < LPW; ++j) copy(src + 128 * j, doff, dst + 4096 * j);
     };
 
     // Rows past the end of the sequence in its last tile are cleared, so that
     // whatever unused cache slots hold cannot reach the result.
     auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
       for (int u = tid; u < kTile * 72; u += NT) {
-        const int c = u >> 5, pos = u & 31;
-        if ((pos ^ (4 * (c & 3))) >= valid)
+        const int c0 = (u >> 4) & 1;
+        const int token = 8 * ((u >> 6) & 3) + ((u & 3) | ((((u >> 2) & 1) ^ c0) << 2));
+        if (token >= valid)
           *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     };
@@ -1046,7 +1075,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
       f32x16 acc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      auto rd = [&](int s) { return lds_read_b128(st + 1024 * s + ((s & 1) ? kofs1 : kofs0)); };
+      auto rd = [&](int s) { return lds_read_b128(st + kstep_ofs(s) + ((s & 1) ? kofs1 : kofs0)); };
       constexpr int D = 4;
       bf16x8 kf[D];
 #pragma unroll
@@ -1116,7 +1145,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
       uint32_t pw[8];
       f32x16 s_next;
       auto kread = [&](int s) {
-        return lds_read_b128(sn + 1024 * s + ((s & 1) ? kofs1 : kofs0));
+        return lds_read_b128(sn + kstep_ofs(s) + ((s & 1) ? kofs1 : kofs0));
       };
       // x[i]: the raw score (interior tiles) or the scaled, masked score;
       // kept so that the rare path can redo the probabilities
@@ -1202,7 +1231,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
       const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage[it % NST];
       auto vread = [&](int q) {
         const int ct = q % NCT, kk = q / NCT;
-        return vt_fragment(st + vofs0 + 2048 * ct + 256 * kk, st + vofs1 + 2048 * ct + 256 * kk);
+        const int o = vct_ofs(ct) + 2048 * kk;
+        return vt_fragment(st + vofs0 + o, st + vofs1 + o);
       };
       constexpr int NQ = 2 * NCT;
       bf16x8 va[VPF];
@@ -1693,23 +1723,6 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
   // XDL write -> VALU read of the same VGPRs: more than 18 wait states
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
 }
-
-// Row-group tile layout of the 128-row kernel: block 4 C + R (1 KiB) holds
-// tokens 8R..8R+7 and chunks 8C..8C+7 (16-byte units); token 8R + r, chunk
-// 8C + c sits in its block at unit (r & 3) | ((r >> 2) ^ c) & 1) << 2 |
-// ((R ^ (c >> 1)) & 1) << 3 | (c & 1) << 4 | (c >> 2 & 1) << 5. Every LDS-DMA
-// copy fills one block from eight whole 128-byte lines, and the score reads
-// (32 tokens x two chunks) and the transposing value reads (4 tokens x 4
-// chunks per 32 lanes) each hit distinct 16-byte bank groups.
-__device__ __forceinline__ int rg_unit(int t, int c) {
-  const int R = t >> 3, r = t & 7, C = c >> 3, cc = c & 7;
-  return 64 * (4 * C + R) + ((r & 3) | ((((r >> 2) ^ cc) & 1) << 2) |
-                             (((R ^ (cc >> 1)) & 1) << 3) | ((cc & 1) << 4) |
-                             (((cc >> 2) & 1) << 5));
-}
-// Byte offset of score k-step k (chunks 2k, 2k+1) that does not depend on
-// the lane.
-__device__ __forceinline__ constexpr int kstep_ofs(int k) { return 4096 * (k >> 2) + 512 * ((k >> 1) & 1); }
 
 // --------------------------- bf16 decode kernel (128-row tile, pipelined)
 
@@ -2587,7 +2600,10 @@ hipError_t launch_narrow(const DecodeParams& dp, int grid, hipStream_t stream) {
 
 template <int HG>
 hipError_t launch_rows(const DecodeParams& dp, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_decode_rows_kernel<HG>), dim3(grid), dim3(256), 0, stream, dp);
+  if (dp.m_tiles == 1)
+    hipLaunchKernelGGL((mla_decode_rows_kernel<HG, true>), dim3(grid), dim3(256), 0, stream, dp);
+  else
+    hipLaunchKernelGGL((mla_decode_rows_kernel<HG, false>), dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
