@@ -1,5 +1,5 @@
-"""Host-side checks of the LDS tile layouts used by the 128-row and 16-row
-decode kernels (no GPU). The index formulas below restate the kernels' own
+"""Host-side checks of the LDS tile layouts used by the bf16 decode kernels
+(128-, 32/64- and 16-row tiles; no GPU). The index formulas below restate the kernels' own
 (lane offsets of the LDS-DMA copies, score and value operand reads, tail
 clearing); the checks are that the copies fill every 16-byte unit of the
 36 KiB tile exactly once from whole 128-byte lines, that every read fetches
@@ -35,7 +35,7 @@ def _whole_lines(doff):
         assert len(lines) == 8 and all(len(v) == 8 for v in lines.values())
 
 
-# ---- 128-row kernel (32x32x16 MFMA operands)
+# ---- 128-row and 32/64-row kernels (32x32x16 MFMA operands)
 def pipe_doff(w, l):
     dc0 = (l >> 4) & 1
     dr = (l & 3) | ((((l >> 2) & 1) ^ dc0) << 2)
@@ -60,16 +60,21 @@ def test_pipe_layout():
             assert m[byte // 16] == (l32, 2 * k + hi)
             groups.setdefault(lane >> 4, []).append((byte // 16) % 16)
         assert all(len(set(v)) == 16 for v in groups.values())
-    for w, cb, kk, p in itertools.product(range(4), range(4), range(2), range(2)):
-        groups = {}                      # value operand, transposing 8-byte reads
+    # value operand, transposing 8-byte reads, for the column bases of the
+    # 128-row kernel (128 w, 4 blocks of 32 columns) and of the 32/64-row
+    # kernel with two waves per row group (256 cg, 8 blocks)
+    cases = [(128 * w, cb) for w in range(4) for cb in range(4)]
+    cases += [(256 * cg, ct) for cg in range(2) for ct in range(8)]
+    for (cbase, cb), kk, p in itertools.product(cases, range(2), range(2)):
+        groups = {}
         for lane in range(64):
             g16, i16 = lane >> 4, lane & 15
             vh, vq, vs = g16 >> 1, i16 & 3, i16 >> 2
-            vlane = 8192 * w + 16 * vs + 64 * (vh ^ (vq >> 1)) + 256 * (vq >> 1) + 8 * (vq & 1)
+            vlane = 64 * cbase + 16 * vs + 64 * (vh ^ (vq >> 1)) + 256 * (vq >> 1) + 8 * (vq & 1)
             vofs = vlane + 1024 * p + 128 * ((g16 & 1) ^ p)
             byte = vofs + 4096 * (cb >> 1) + 512 * (cb & 1) + 2048 * kk
             assert m[byte // 16] == (4 * vh + vs + 8 * p + 16 * kk,
-                                     16 * w + 4 * cb + 2 * (g16 & 1) + (vq >> 1))
+                                     cbase // 8 + 4 * cb + 2 * (g16 & 1) + (vq >> 1))
             assert (byte % 16) // 8 == vq & 1
             groups.setdefault(lane >> 5, []).append(((byte // 16) % 16, (byte % 16) // 8))
         assert all(len(set(v)) == 32 for v in groups.values())
