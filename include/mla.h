@@ -99,10 +99,10 @@ typedef struct {
   int32_t kv_dtype;           /* mla_kv_dtype */
   int32_t num_parts;          /* 0: automatic; else P >= 1 KV partitions (see mla_plan) */
   int32_t m_tile;             /* 0: automatic; else 16, 32, 64 or 128 query rows
-                                 per workgroup (16 and 128: bf16 cache only).
+                                 per workgroup (16: bf16 cache only).
                                  Automatic picks the smallest tile that holds
                                  seqlen_q * num_heads rows (16 only for bf16),
-                                 else the largest (128 bf16, 64 q8_0). */
+                                 else 128. */
 } mla_problem;
 
 /* Bytes of device workspace mla_decode needs for *p (written to *bytes, host).

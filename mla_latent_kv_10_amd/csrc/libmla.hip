@@ -2225,6 +2225,444 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   }
 }
 
+// --------------------------------- q8_0 decode kernel (128-row tile)
+
+// q8_0 cache, 128 query rows per workgroup, 4 waves; wave w computes the
+// scores and the softmax of rows 32w..32w+31 and the value product of all 128
+// rows for output columns 128w..128w+127 (the division of the 128-row bf16
+// kernel). Per 32-token tile, in four phases separated by barriers:
+//  1. the int8 tile (18 KiB) and its scales (1152 B), copied by LDS-DMA into a
+//     3-stage ring, are converted once by all threads into two bf16 tiles in
+//     the row-group layout: hi = bf16(scale * value) and
+//     lo = bf16(scale * value - hi). The product of an fp16 scale and an int8
+//     value is exact in fp32 and hi + lo equals it to within 2^-17 relative,
+//     so scores over hi and lo are the exact dequantised scores up to fp32
+//     accumulation; tokens past the end of the sequence convert to zero;
+//  2. scores S^T = K q~^T over hi and lo (two MFMA chains of 36 steps);
+//  3. online softmax of the wave's rows (lazy reference maximum), P published
+//     through LDS with the rescale requests;
+//  4. value product O^T += V^T P^T with V = hi, the dequantised value rounded
+//     to bf16.
+// Compared with converting the int8 operands in every wave and scaling each
+// 32-column group's partial score (the 32/64-row q8_0 kernel), the conversion
+// work is done once per tile for all 128 rows and the scores are pure MFMA
+// work.
+template <bool NT>
+__global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) {
+  constexpr int NW = 4;
+  constexpr int NTH = 64 * NW;
+  constexpr int MT = 128;
+  constexpr int NST = 3;                  // int8 ring stages
+  constexpr int KPF = 2;                  // score k-steps in flight (hi and lo each)
+  constexpr int CPW = 5;                  // 1 KiB copies per wave per tile (20 per tile)
+
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NST][kQ8StageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_hl[2][kTileBytes];   // hi, lo
+  __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];   // P, B-operand layout
+  __shared__ float s_alpha[MT];
+  __shared__ __attribute__((aligned(16))) int s_flag[NW];
+  // aliases inside the hi / lo tiles, which are idle before the first tile
+  // and after the last one
+  int* s_pre = reinterpret_cast<int*>(s_hl[0]);                   // [B+1]
+  int* s_misc = reinterpret_cast<int*>(s_hl[1]);
+  float* s_lsum = reinterpret_cast<float*>(s_hl[1] + 1024);       // epilogue
+  static_assert(4 * (kMaxBatch + 1) <= kTileBytes, "plan prefix fits the hi tile");
+
+  auto copy = [](const void* src, uint32_t off, uint32_t dst) {
+    if constexpr (NT)
+      dma16_sbase_nt(src, off, dst);
+    else
+      dma16_sbase(src, off, dst);
+  };
+
+  const int tid = threadIdx.x, wave = uniform(tid >> 6);
+
+  int v = blockIdx.x;
+  const int G = gridDim.x;
+  if ((G & 7) == 0) v = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int part = v / a.m_tiles, mt = v % a.m_tiles;
+
+  plan_prefix<NTH>(a.seqlens, a.B, a.max_blocks, s_pre, s_misc);
+  const int T = uniform(s_pre[a.B]);
+  const int P = a.P;
+  if (blockIdx.x == 0)
+    for (int b = tid; b <= a.B; b += NTH) a.ws_prefix[b] = s_pre[b];
+  const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
+
+  if (tid == 0) {
+    s_misc[8] = 0x7fffffff;
+    s_misc[9] = -1;
+  }
+  __syncthreads();
+  for (int b = tid; b < a.B; b += NTH) {
+    const int lo = s_pre[b], hi2 = s_pre[b + 1];
+    bool mine;
+    if (hi2 > lo) {
+      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
+    } else {
+      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
+      mine = owner == part;
+    }
+    if (mine) {
+      atomicMin(&s_misc[8], b);
+      atomicMax(&s_misc[9], b);
+    }
+  }
+  __syncthreads();
+  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+  int pre_b = b_first <= b_last ? uniform(s_pre[b_first]) : 0;
+  __syncthreads();   // the hi / lo tiles are free from here on
+
+  const int cbase = 128 * wave;              // first output column of this wave
+
+  for (int b = b_first; b <= b_last; ++b) {
+    // Per-lane constants are derived here, from a lane index the compiler
+    // cannot see through, so that they are not hoisted out of the sequence
+    // loop and kept (spilled) across it.
+    int tid_s = tid;
+    asm volatile("" : "+v"(tid_s));
+    const int lane = tid_s & 63, hi = lane >> 5, l32 = lane & 31;
+    const int r = mt * MT + 32 * wave + l32;   // row whose scores this lane computes
+    const bool row_ok = r < a.M;
+    const int q_i = row_ok ? r / a.H : 0;
+    // Score operand of k-step k (token l32, chunk 2k + hi) in the row-group
+    // layout: byte kstep_ofs(k) + (k odd ? kofs1 : kofs0).
+    const int kR = l32 >> 3, kr = l32 & 7;
+    const int kpart = 1024 * kR + 16 * ((kr & 3) | ((((kr >> 2) ^ hi) & 1) << 2) | (hi << 4));
+    const int kofs0 = kpart + 128 * (kR & 1);
+    const int kofs1 = kpart + 128 * ((kR & 1) ^ 1);
+    // Value operand (transposing reads of the hi tile): lane (g16, i16)
+    // points at token 4 vh + vs (+8 for the second read, +16 kk), chunk
+    // 16 w + 4 cb + 2 (g16 & 1) + (vq >> 1), half vq & 1.
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int vh = g16 >> 1, vq = i16 & 3, vs = i16 >> 2;
+    const int vlane = 64 * cbase + 16 * vs + 64 * (vh ^ (vq >> 1)) + 256 * (vq >> 1) + 8 * (vq & 1);
+    const int vofs0 = vlane + 128 * (g16 & 1);
+    const int vofs1 = vlane + 1024 + 128 * ((g16 & 1) ^ 1);
+
+    const int L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
+    const int pre_e = pre_b + (L + kBT - 1) / kBT;
+    const int seg_lo = max(p_lo, pre_b) - pre_b, seg_hi = min(p_hi, pre_e) - pre_b;
+    bool split = false;
+    int slot = 0;
+    if (pre_e > pre_b) {
+      const int fp = part_of(pre_b, P, T), lp = part_of(pre_e - 1, P, T);
+      split = lp > fp;
+      slot = 2 * part + ((part == fp && pre_b > p_lo) ? 1 : 0);
+    }
+    const int t_begin = 2 * seg_lo;
+    const int t_end = min(2 * seg_hi, (L + kTile - 1) / kTile);
+    const int n_tiles = max(0, t_end - t_begin);
+    // an empty pool has no block to stand in for invalid ids: nothing is
+    // streamed and the id check below poisons the segment
+    const int n_run = a.num_blocks > 0 ? n_tiles : 0;
+    const int n_vis = row_ok ? L - a.s_q + 1 + q_i : 0x7fffffff;
+
+    f32x16 o[16];
+    float zero = 0.f;
+    asm volatile("" : "+v"(zero));   // no kernel-wide zero vector to keep alive
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[j][i] = zero;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // Block ids of the segment, 64 at a time, one per lane (validated as in
+    // the bf16 kernels: an id outside the pool poisons the segment and is
+    // replaced by block 0).
+    const int seg_len = max(0, seg_hi - seg_lo);
+    int bt_base = 0;
+    int bt_lane = 0;
+    bool bad = false;
+    auto load_ids = [&]() {
+      const int j = bt_base + min(lane, max(0, seg_len - bt_base - 1));
+      bt_lane = seg_len > 0 ? ((const int32_t*)a.block_table)[(int64_t)b * a.max_blocks + seg_lo + j] : 0;
+    };
+    auto check_ids = [&]() {   // after the load has landed
+      const bool inval = bt_lane < 0 || (int64_t)bt_lane >= a.num_blocks;
+      bad = bad || __any(inval && bt_base + lane < seg_len);
+      bt_lane = inval ? 0 : bt_lane;
+    };
+    // Copies of int8 tile idx into ring stage idx % 3: copy k = wave + 4 j
+    // (k < 18: int8 bytes 1024 k .. of the tile, contiguous; k = 18, 19: the
+    // 1152 bytes of scales, the tail of copy 19 reading the first bytes again
+    // into the stage's padding).
+    auto issue = [&](int idx) {
+      int rel = (idx >> 1) - bt_base;   // lane of the segment's id window
+      if (rel >= 64) {
+        bt_base += 64;
+        rel -= 64;
+        load_ids();
+        wait_vmcnt<0>();
+        check_ids();
+      }
+      const int64_t phys = uniform(__builtin_amdgcn_readlane(bt_lane, rel));
+      const int64_t row0 = phys * kBT + ((t_begin + idx) & 1) * kTile;
+      const uint8_t* src = a.kv + row0 * kQ8RowBytes;
+      const uint8_t* ssrc = a.kv_scales + row0 * kQ8ScaleRowBytes;
+      const uint32_t dst = lds_addr_of(s_ring[idx % NST]);
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        const int k = wave + 4 * j;
+        if (k < 18) {
+          copy(src + 1024 * k, 16 * lane, dst + 1024 * k);
+        } else {
+          // scales: default policy (the tail lanes re-read a partial line)
+          const int off = 1024 * (k - 18) + 16 * lane;
+          dma16_sbase(ssrc, off < kQ8ScaleTileBytes ? off : 0, dst + kQ8TileBytes + 1024 * (k - 18));
+        }
+      }
+    };
+
+    // Query fragments of this lane's row (B operand of the score MFMA): 16
+    // bytes per k-step, read directly; rows past M read zero.
+    load_ids();
+    bf16x8 qf[36];
+    {
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q + ((int64_t)b * a.M + (row_ok ? r : 0)) * kDK);
+      const uint32_t sg = row_ok ? a.q_sign2 : 0u;
+      const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int s2 = 0; s2 < 36; ++s2) {
+        const u32x4 z = *reinterpret_cast<const u32x4*>(qrow + 32 * s2 + 16 * hi);
+        qf[s2] = __builtin_bit_cast(bf16x8, (z ^ sg) & keep);
+      }
+    }
+    wait_vmcnt<0>();
+    check_ids();
+    if (n_run > 0) issue(0);
+    if (n_run > 1) issue(1);
+
+    for (int it = 0; it < n_run; ++it) {
+      // ---- 1. int8 tile it landed (tile it+1 may be in flight); everyone is
+      // done with the previous tile's hi / lo / P
+      if (it + 1 < n_run) wait_vmcnt<CPW>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (it + 2 < n_run) issue(it + 2);
+      {
+        // Thread (w, l) converts unit 256 i + 64 w + l of the hi / lo tiles,
+        // i = 0..8: token 8 w + r(l), chunk 8 i + c(l) (the row-group
+        // placement inverted), i.e. one token per thread. All reads first,
+        // then the arithmetic; tokens past the end of the sequence read as
+        // zero.
+        const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_ring[it % NST];
+        const int valid = L - (t_begin + it) * kTile;   // tokens of the tile in the sequence
+        const int lane = tid & 63;
+        const int c0 = (lane >> 4) & 1;
+        const int rr = (lane & 3) | ((((lane >> 2) & 1) ^ c0) << 2);
+        const int cc = c0 | ((((lane >> 3) ^ wave) & 1) << 1) | (((lane >> 5) & 1) << 2);
+        const int t = 8 * wave + rr;
+        const uint32_t keep = t < valid ? 0xffffffffu : 0u;
+        const LDS_AS uint8_t* srow = st + kQ8RowBytes * t + 8 * cc;
+        const LDS_AS uint32_t* scl =
+            reinterpret_cast<const LDS_AS uint32_t*>(st + kQ8TileBytes + kQ8ScaleRowBytes * t);
+        uint64_t raw[9];
+        uint32_t sc2[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+          raw[i] = *reinterpret_cast<const LDS_AS uint64_t*>(srow + 64 * i);
+          sc2[i] = scl[i];   // scales of groups 2i, 2i+1; chunk 8i + cc is group 2i + (cc >> 2)
+        }
+        const int sh16 = 16 * (cc >> 2);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+          const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc2[i] >> sh16));
+          const uint32_t wv[2] = {(uint32_t)raw[i] & keep, (uint32_t)(raw[i] >> 32) & keep};
+          u32x4 whi, wlo;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const uint32_t word = wv[e2 >> 1];
+            const float x0 = d * (float)(int8_t)(word >> (16 * (e2 & 1)));
+            const float x1 = d * (float)(int8_t)(word >> (16 * (e2 & 1) + 8));
+            const uint32_t h = pack_bf16x2(x0, x1);
+            const float h0 = __builtin_bit_cast(float, h << 16);
+            const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+            whi[e2] = h;
+            wlo[e2] = pack_bf16x2(x0 - h0, x1 - h1);
+          }
+          const int U = tid + NTH * i;
+          *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[0] + 16 * U) = whi;
+          *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[1] + 16 * U) = wlo;
+        }
+      }
+      lds_barrier();   // hi and lo of tile it visible
+
+      // ---- 2. scores of the wave's 32 rows over hi and lo (two chains)
+      const LDS_AS uint8_t* khi = (const LDS_AS uint8_t*)s_hl[0];
+      const LDS_AS uint8_t* klo = (const LDS_AS uint8_t*)s_hl[1];
+      auto rd = [&](const LDS_AS uint8_t* base, int k) {
+        return lds_read_b128(base + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0));
+      };
+      f32x16 sh, sl;
+      bf16x8 kh[KPF], kl[KPF];
+#pragma unroll
+      for (int j2 = 0; j2 < KPF; ++j2) {
+        kh[j2] = rd(khi, j2);
+        kl[j2] = rd(klo, j2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      unroll<36>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        mfma_score(sh, kh[k % KPF], qf[k], k == 0);
+        mfma_score(sl, kl[k % KPF], qf[k], k == 0);
+        if constexpr (k + KPF < 36) {
+          kh[k % KPF] = rd(khi, k + KPF);
+          kl[k % KPF] = rd(klo, k + KPF);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      mfma_vgpr_drain(sh);
+      mfma_vgpr_drain(sl);
+
+      // ---- 3. online softmax of the wave's rows (log2 domain); element i of
+      // the lane is token 8 (i >> 2) + 4 hi + (i & 3) of row l32
+      const int t0 = (t_begin + it) * kTile;
+      const float cs = a.scale_mag_log2;
+      const bool masked = !__all(t0 + kTile <= n_vis);
+      const int limx = masked ? n_vis - t0 - 4 * hi : kTile;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float sv = (sh[i] + sl[i]) * cs;
+        x[i] = (!masked || 8 * (i >> 2) + (i & 3) < limx) ? sv : -INFINITY;
+      }
+      float lmax = max3f(x[0], x[1], x[2]);
+      lmax = max3f(lmax, x[3], x[4]);
+      lmax = max3f(lmax, x[5], x[6]);
+      lmax = max3f(lmax, x[7], x[8]);
+      lmax = max3f(lmax, x[9], x[10]);
+      lmax = max3f(lmax, x[11], x[12]);
+      lmax = max3f(lmax, x[13], x[14]);
+      lmax = fmaxf(lmax, x[15]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lmax), __float_as_uint(lmax),
+                                                       false, false);
+      const float rmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const bool raise = rmax > m_run + kRescaleThreshold;
+      const float m_new = raise ? rmax + kRefHeadroom : m_run;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+      float psum = 0.f;
+      uint32_t pw[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
+        const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
+        psum += p0 + p1;
+        pw[j] = pack_bf16x2(p0, p1);
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      const bool raise_any = __any(raise);
+      s_p[wave][0][lane] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+      s_p[wave][1][lane] = u32x4{pw[4], pw[5], pw[6], pw[7]};
+      if (raise_any && hi == 0) s_alpha[32 * wave + l32] = alpha;
+      if (lane == 0) s_flag[wave] = raise_any ? 1 : 0;
+      lds_barrier();   // P, rescale factors and flags of every wave visible
+
+      // ---- 4. value product: a row's accumulators are rescaled first when
+      // its reference maximum moved (rare)
+      const u32x4 flags = *reinterpret_cast<const u32x4*>(s_flag);
+      if (__builtin_expect((flags[0] | flags[1] | flags[2] | flags[3]) != 0, 0)) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          if (flags[rb]) {
+            const float al = s_alpha[32 * rb + l32];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) acc_scale(o[4 * rb + cb], al);
+          }
+        }
+      }
+      const LDS_AS uint8_t* sv = (const LDS_AS uint8_t*)s_hl[0];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 pf[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) pf[rb] = __builtin_bit_cast(bf16x8, s_p[rb][kk][lane]);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const int off = 4096 * (cb >> 1) + 512 * (cb & 1) + 2048 * kk;
+          const bf16x8 va = vt_fragment(sv + vofs0 + off, sv + vofs1 + off);
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb)
+            o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[rb], o[4 * rb + cb], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- epilogue: rows staged through the idle hi / lo tiles so that global
+    // stores are whole 256-byte row segments
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+    if (bad) lse_v = __builtin_nanf("");
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (hi == 0) s_lsum[32 * wave + l32] = l_tot;
+    lds_barrier();
+    constexpr int kStageRow = 272;
+    uint16_t* dst_base = split ? a.part_o + ((int64_t)slot * a.M) * kDL
+                               : a.out + ((int64_t)b * a.M) * kDL;
+    LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_hl[0] + wave * (64 * kStageRow);
+    static_assert(4 * 64 * kStageRow <= 2 * kTileBytes, "staging fits the hi / lo tiles");
+    // the row sums are read before the staging area (which covers s_lsum) is
+    // written
+    float lt_row[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) lt_row[rb] = s_lsum[32 * rb + l32];
+    lds_barrier();
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int rb = 2 * half + q;
+        const float lt = lt_row[rb];
+        const float inv_l = bad ? __builtin_nanf("") : (lt > 0.f ? 1.f / lt : 0.f);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& acc = o[4 * rb + cb];
+            const uint32_t w0 = pack_bf16x2(acc[4 * g + 0] * inv_l, acc[4 * g + 1] * inv_l);
+            const uint32_t w1 = pack_bf16x2(acc[4 * g + 2] * inv_l, acc[4 * g + 3] * inv_l);
+            const int col = 32 * cb + 8 * g + 4 * hi;
+            *reinterpret_cast<LDS_AS uint64_t*>(stg + (32 * q + l32) * kStageRow + 2 * col) =
+                (uint64_t)w0 | ((uint64_t)w1 << 32);
+          }
+      }
+      lds_barrier();
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int rl0 = ln >> 4, cl = 8 * (ln & 15);
+      const int row0 = mt * MT + 64 * half;
+      uint16_t* gdst = dst_base + (int64_t)(row0 + rl0) * kDL + cbase + cl;
+      const LDS_AS uint8_t* lsrc = stg + rl0 * kStageRow + 2 * cl;
+      if (row0 + 64 <= a.M) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          *reinterpret_cast<u32x4*>(gdst + 4 * i * kDL) =
+              *reinterpret_cast<const LDS_AS u32x4*>(lsrc + 4 * i * kStageRow);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (row0 + rl0 + 4 * i < a.M)
+            *reinterpret_cast<u32x4*>(gdst + 4 * i * kDL) =
+                *reinterpret_cast<const LDS_AS u32x4*>(lsrc + 4 * i * kStageRow);
+      }
+      lds_barrier();
+    }
+    if (row_ok && hi == 0) {
+      const int64_t row = (int64_t)b * a.M + r;
+      if (!split)
+        a.lse[row] = lse_v;
+      else
+        a.part_lse[(int64_t)slot * a.M + r] = lse_v;
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    pre_b = pre_e;
+  }
+}
+
 // ------------------------------------------------------------ combine
 
 // Merge n (lse, O) parts of one row; one wave, 8 columns per lane.
@@ -2483,6 +2921,7 @@ int device_cus() {
 
 struct Plan {
   bool narrow;   // 16-row tile (bf16 cache)
+  bool q8w;      // 128-row tile (q8_0 cache)
   int HG, CG, MT, m_tiles, P, M;
   size_t off_prefix, off_lse, off_o, bytes;
 };
@@ -2524,23 +2963,23 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   // score contraction and the output columns), or 32, 64 or 128 (1, 2 or 4
   // row groups of 32, each wave owning whole rows); the smallest tile that
   // holds all rows of a sequence, so the cache is streamed once per part.
-  // q8_0 cache: 32 or 64 rows, each row group's work split over 4 waves. More
+  // q8_0 cache: 32 or 64 rows, each row group's work split over 4 waves, or
+  // 128 rows (the tile converted once into exact bf16 hi / lo parts). More
   // rows than one tile holds take several row tiles per KV part, placed on
   // the same XCD so the second read of each cache tile hits L2.
   const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
-  if (q8 && (p->m_tile == 16 || p->m_tile == 128))
+  if (q8 && p->m_tile == 16)
     return fail(MLA_ERR_UNSUPPORTED, "m_tile %d is not available for the q8_0 cache", p->m_tile);
   pl->narrow = !q8 && (p->m_tile == 16 || (p->m_tile == 0 && M <= 16));
   if (pl->narrow) {
     pl->HG = 1;
   } else if (p->m_tile) {
     pl->HG = p->m_tile / 32;
-  } else if (q8) {
-    pl->HG = M <= 32 ? 1 : 2;
   } else {
     pl->HG = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   }
-  pl->CG = q8 ? 4 : 4 / pl->HG;
+  pl->q8w = q8 && pl->HG == 4;
+  pl->CG = q8 ? (pl->q8w ? 1 : 4) : 4 / pl->HG;
   pl->MT = pl->narrow ? 16 : 32 * pl->HG;
   pl->m_tiles = (M + pl->MT - 1) / pl->MT;
   int P = p->num_parts;
@@ -2590,6 +3029,14 @@ hipError_t launch_pipe(const DecodeParams& dp, int grid, hipStream_t stream) {
     hipLaunchKernelGGL(mla_decode_pipe_kernel<true>, dim3(grid), dim3(256), 0, stream, dp);
   else
     hipLaunchKernelGGL(mla_decode_pipe_kernel<false>, dim3(grid), dim3(256), 0, stream, dp);
+  return hipGetLastError();
+}
+
+hipError_t launch_q8w(const DecodeParams& dp, int grid, hipStream_t stream) {
+  if (dp.m_tiles == 1)
+    hipLaunchKernelGGL(mla_decode_q8w_kernel<true>, dim3(grid), dim3(256), 0, stream, dp);
+  else
+    hipLaunchKernelGGL(mla_decode_q8w_kernel<false>, dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -2708,6 +3155,8 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
       case 4: e = launch_pipe(dp, grid, stream); break;
       default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
     }
+  } else if (pl.q8w) {
+    e = launch_q8w(dp, grid, stream);
   } else if (pl.HG == 2) {
     e = launch_decode<2, 4, true>(dp, grid, stream);
   } else {

@@ -104,14 +104,13 @@ def test_workspace_size_formula(L):
 
 def test_row_tile_choices(L):
     n = ctypes.c_size_t(0)
-    # 16- and 128-row tiles exist for the bf16 cache only
+    # the 16-row tile exists for the bf16 cache only
     for mt in (16, 32, 64, 128):
         assert L.mla_workspace_size(ctypes.byref(_prob(m_tile=mt)), ctypes.byref(n)) == 0
-    for mt in (16, 128):
-        assert L.mla_workspace_size(ctypes.byref(_prob(m_tile=mt, kv_dtype=1)),
-                                    ctypes.byref(n)) == 2
-        assert "m_tile" in L.mla_last_error().decode()
-    for mt in (32, 64):
+    assert L.mla_workspace_size(ctypes.byref(_prob(m_tile=16, kv_dtype=1)),
+                                ctypes.byref(n)) == 2
+    assert "m_tile" in L.mla_last_error().decode()
+    for mt in (32, 64, 128):
         assert L.mla_workspace_size(ctypes.byref(_prob(m_tile=mt, kv_dtype=1)),
                                     ctypes.byref(n)) == 0
 
