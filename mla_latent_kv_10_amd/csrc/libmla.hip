@@ -2573,21 +2573,27 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
           }
         }
       }
+      // all value and probability operands are read before the MFMAs, so the
+      // LDS latency is paid once
       const LDS_AS uint8_t* sv = (const LDS_AS uint8_t*)s_hl[0];
+      bf16x8 pf[2][4], va[2][4];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 pf[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) pf[rb] = __builtin_bit_cast(bf16x8, s_p[rb][kk][lane]);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           const int off = 4096 * (cb >> 1) + 512 * (cb & 1) + 2048 * kk;
-          const bf16x8 va = vt_fragment(sv + vofs0 + off, sv + vofs1 + off);
+          va[kk][cb] = vt_fragment(sv + vofs0 + off, sv + vofs1 + off);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) pf[kk][rb] = __builtin_bit_cast(bf16x8, s_p[rb][kk][lane]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb)
-            o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[rb], o[4 * rb + cb], 0, 0, 0);
-        }
-      }
+            o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk][cb], pf[kk][rb], o[4 * rb + cb], 0, 0, 0);
     }
 
     // ---- epilogue: rows staged through the idle hi / lo tiles so that global
