@@ -45,12 +45,14 @@ SMALL = [
     ("h16_many", 24, 1, 16, [1, 0, 31, 32, 33, 64, 65, 0, 0, 2, 96, 97, 127, 128, 129, 3,
                              0, 191, 300, 1, 63, 0, 20, 257], "permuted", "bf16", 0),
     ("h16_long", 2, 1, 16, [5000, 4161], "permuted", "bf16", 0),
-    # q8_0 64-row tile: two row tiles of causal pairs, a padded row tile, many
-    # short segments and a segment longer than one id window
-    ("h64_pair_q8", 2, 2, 64, [300, 2000], "permuted", "q8_0", 0),
+    # q8_0: two forced 64-row tiles of causal pairs, a padded 64-row tile,
+    # many short segments and a segment longer than one id window in the
+    # 128-row kernel, and that kernel with two row tiles per part (256 rows)
+    ("h64_pair_q8", 2, 2, 64, [300, 2000], "permuted", "q8_0", 64),
     ("h40_q8", 3, 1, 40, [65, 700, 33], "permuted", "q8_0", 0),
     ("h128_q8_many", 12, 1, 128, [1, 0, 31, 33, 64, 65, 130, 0, 2, 300, 97, 5000],
      "permuted", "q8_0", 0),
+    ("h128_pair_q8", 2, 2, 128, [300, 4500], "permuted", "q8_0", 0),
 ]
 
 
