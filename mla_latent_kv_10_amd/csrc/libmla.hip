@@ -786,7 +786,7 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
       compute(it, st);
     }
 
-    // ---- epilogue: final rows, or fp32 partials of a split sequence
+    // ---- epilogue: final rows, or bf16 partials of a split sequence
     const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
     float lse_v = l_run > 0.f ? (m_run + __log2f(l_run)) * 0.69314718055994531f : -INFINITY;
     if (bad) lse_v = __builtin_nanf("");
@@ -1248,7 +1248,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
       if (PIPE) s_cur = s_next;
     }
 
-    // ---- epilogue: final rows, or fp32 partials of a split sequence
+    // ---- epilogue: final rows, or bf16 partials of a split sequence
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
