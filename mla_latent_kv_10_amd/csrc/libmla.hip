@@ -2467,7 +2467,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
         const int sh16 = 16 * (cc >> 2);
 #pragma unroll
         for (int i = 0; i < 9; ++i) {
-          const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(sc2[i] >> sh16));
+          // the scale is zeroed too: a NaN or infinite scale in an unused
+          // slot would otherwise reach the value product as 0 * inf
+          const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)((sc2[i] & keep) >> sh16));
           const uint32_t wv[2] = {(uint32_t)raw[i] & keep, (uint32_t)(raw[i] >> 32) & keep};
           u32x4 whi, wlo;
 #pragma unroll

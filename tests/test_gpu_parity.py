@@ -140,6 +140,27 @@ def test_one_hot_probe_returns_the_exact_row(H):
             assert np.abs(lse[b, 0] - 4096.0).max() <= 1e-3
 
 
+@pytest.mark.parametrize("H,kvd", [(16, "bf16"), (40, "bf16"), (128, "bf16"),
+                                   (40, "q8_0"), (128, "q8_0")])
+def test_unused_cache_slots_never_reach_the_result(H, kvd):
+    """The slots of a sequence's last block past its length hold NaN (bf16
+    rows; q8_0 scales): every kernel gives the oracle's result, which never
+    reads them."""
+    w = wl.make_workload("tailnan", 3, 1, H, [100, 65, 1000], seed=21, table="permuted",
+                         kv_dtype=kvd)
+    for b, L in enumerate(w.seqlens):
+        if L % 64:
+            blk = w.block_table[b, L // 64]
+            if kvd == "bf16":
+                w.kv[blk, L % 64:, :] = 0x7FC0        # bf16 NaN
+            else:
+                w.kv_scales[blk, L % 64:, :] = 0x7E00  # fp16 NaN
+    ref = oracle_rows(w)
+    for parts in (0, 1, 5):
+        out, lse, _ = run_gpu(w, num_parts=parts)
+        compare(out, lse, *ref, what=f"NaN past the end H={H} {kvd} P={parts}")
+
+
 @pytest.mark.parametrize("H", [16, 8])
 def test_empty_rows_and_causal_visibility(H):
     w = wl.make_workload("deg", 4, 2, H, [0, 1, 2, 130], seed=9, table="permuted")
