@@ -73,24 +73,64 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}))
 
 
-def cpu_baseline(w, n_seqs: int):
-    """Oracle on the first n_seqs sequences (all their heads), host threads."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_gbs(w, n_seqs: int, rows_per_seq=None):
+    """Time the oracle on the first n_seqs sequences (all their query rows, or
+    the first rows_per_seq of each) -> (GB/s, seconds, algorithmic bytes)."""
     import oracle
     import workload as wl
     n_seqs = max(1, min(n_seqs, w.B))
-    rows = np.arange(n_seqs * w.s_q * w.H, dtype=np.int64)
+    per = w.s_q * w.H
+    take = per if rows_per_seq is None else min(per, rows_per_seq)
+    rows = np.concatenate([np.arange(b * per, b * per + take, dtype=np.int64)
+                           for b in range(n_seqs)])
     t0 = time.perf_counter()
     oracle.decode_absorbed(w.q, w.kv, w.block_table, w.seqlens, w.softmax_scale,
                            kv_scales=w.kv_scales, rows=rows)
     dt = time.perf_counter() - t0
     sub = wl.Workload(**{**w.__dict__, "B": n_seqs, "q": w.q[:n_seqs],
                          "seqlens": w.seqlens[:n_seqs], "block_table": w.block_table[:n_seqs]})
-    nbytes, flops, _ = wl.config_flops_bytes(sub)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"first {n_seqs} of {w.B} sequences (all {w.H} heads, {int(w.seqlens[0])} "
-                      f"tokens each), fp64 two-pass oracle, same seeded inputs"}
+    nbytes, _, _ = wl.config_flops_bytes(sub)
+    if take < per:   # the cache of a sequence counts once; per-row q/out/lse for the rows run
+        nbytes -= n_seqs * (per - take) * (576 * 2 + 512 * 2 + 4)
+    return nbytes / dt / 1e9, dt, nbytes
+
+
+def cpu_baseline(w, n_seqs: int):
+    """The fp64 oracle, untuned, on the host: a bounded sample of the same
+    workload on all host threads, plus single-thread figures (the tiny
+    workload whole, and one sequence's first 16 rows of this workload)."""
+    import oracle
+    import workload as wl
+    threads = oracle.max_threads()
+    gbs, dt, _ = _oracle_gbs(w, n_seqs)
+    oracle.set_threads(1)
+    try:
+        g1, d1, _ = _oracle_gbs(wl.config_workload(1), 1)
+        g2, d2, _ = _oracle_gbs(w, 1, rows_per_seq=16)
+    finally:
+        oracle.set_threads(threads)
+    n_seqs = max(1, min(n_seqs, w.B))
+    lens = w.seqlens[:n_seqs]
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3), "cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+            "sample": f"first {n_seqs} of {w.B} sequences (all {w.s_q * w.H} query rows, "
+                      f"{int(lens.min())}..{int(lens.max())} tokens), fp64 two-pass oracle, "
+                      "same seeded inputs",
+            "single_thread": {
+                "tiny_b1_h16_l256": {"value": round(g1, 4), "unit": "GB/s",
+                                     "seconds": round(d1, 4)},
+                f"{w.name}_one_seq_16_rows": {"value": round(g2, 4), "unit": "GB/s",
+                                              "seconds": round(d2, 4)}}}
 
 
 def roofline(nbytes: int, flops: int, avg_ms: float, traffic) -> dict:
@@ -217,12 +257,15 @@ def main():
         if rec.get("source_hash") == source_hash() and rec.get("num_parts") == parts:
             traffic = rec.get("bytes_per_launch")
 
+    lo, hi = int(w.seqlens.min()), int(w.seqlens.max())
+    seqlen_desc = lo if lo == hi else f"{lo}..{hi} (mean {float(w.seqlens.mean()):.1f})"
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "q8_0 cache, bf16 MFMA",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seqlen": int(w.seqlens[0]),
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seqlen": seqlen_desc,
                    "seqlen_q": w.s_q, "kv_cache": f"{w.kv_dtype}, paged 64-token blocks, "
                    "576 = 512 latent + 64 rope", "d_latent": 512, "d_rope": 64,
                    "num_parts": parts, "m_tile": args.m_tile or "auto",

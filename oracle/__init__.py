@@ -67,6 +67,10 @@ def _load():
         lib.oracle_combine.restype = None
         lib.oracle_plan.argtypes = [i32, vp, i32, i32, vp, vp, vp, vp]
         lib.oracle_plan.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -77,6 +81,15 @@ def _c(a, dtype):
 
 def _p(a):
     return None if a is None else a.ctypes.data
+
+
+def max_threads() -> int:
+    """Host threads the oracle's parallel loops use."""
+    return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
 
 
 def bf16_value(bits: int) -> float:

@@ -36,6 +36,7 @@
  * of chosen bit patterns; partition invariants of the plan).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -78,6 +79,11 @@ double oracle_fp16_value(uint16_t bits) {
 double oracle_q8_value(int8_t qv, uint16_t scale_bits) {
   return oracle_fp16_value(scale_bits) * (double)qv;
 }
+
+/* Host threads the parallel loops below use (OpenMP), and a way to change it
+ * (timing a single core). */
+int oracle_max_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 /* ------------------------------------------------------------ paged cache */
 

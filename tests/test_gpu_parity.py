@@ -1,8 +1,8 @@
 """GPU parity of libmla against the CPU oracle (needs an MI355X).
 
-Every call goes through the C ABI (ctypes binding). Small cases compare all
-rows; the five decode workloads at full size compare a seeded sample of rows
-in the launch configuration the benchmark uses. Integer / index work (the
+Every call goes through the C ABI (ctypes binding). Every case compares all
+of its rows, the five decode workloads at full size included (in the launch
+configuration the benchmark uses). Integer / index work (the
 plan, block-table paging) must be bit-exact."""
 import math
 
@@ -13,8 +13,7 @@ import torch
 import mla_latent_kv_10_amd as mla
 import oracle
 import workload as wl
-from gpu_helpers import (compare, device_inputs, log, oracle_rows, require_library, run_gpu,
-                         sample_rows)
+from gpu_helpers import compare, device_inputs, log, oracle_rows, require_library, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -63,24 +62,27 @@ def test_small_all_rows(case, parts):
     log(f"case {name} parts={parts}")
     w = wl.make_workload(name, B, s_q, H, seqlens, seed=77, table=table, kv_dtype=kvd)
     out, lse, _ = run_gpu(w, num_parts=parts, m_tile=mt)
-    compare(out, lse, *oracle_rows(w), what=f"{name}/P={parts}")
+    compare(out, lse, *oracle_rows(w), what=f"{name}/P={parts}", kv_dtype=kvd, flat=True)
 
 
 def test_tiny_config_all_rows():
     w = wl.config_workload(1)
     log("config 1 (tiny)")
     out, lse, _ = run_gpu(w)
-    compare(out, lse, *oracle_rows(w), what="tiny")
+    compare(out, lse, *oracle_rows(w), what="tiny", flat=True)
 
 
-@pytest.mark.parametrize("cfg,n_rows", [(2, 384), (3, 384), (4, 24), (5, 160)])
-def test_full_size_config_sampled_rows(cfg, n_rows):
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_config_all_rows(cfg):
+    """Every row of each large workload, in the launch configuration the
+    benchmark uses, against the fp64 oracle."""
     w = wl.config_workload(cfg)
     log(f"config {cfg} ({w.name}): generated, rows={w.rows}")
     out, lse, _ = run_gpu(w)
-    rows = sample_rows(w, n_rows, seed=cfg)
-    compare(out.reshape(-1, 512)[rows], lse.reshape(-1)[rows], *oracle_rows(w, rows),
-            what=w.name)
+    log(f"config {cfg}: GPU done, running the oracle on all {w.rows} rows")
+    # the flat 2e-2 bound is asserted too, except with the x8 outlier rows of
+    # the long-context workload (|out| up to 30, beyond what bf16 holds to 2e-2)
+    compare(out, lse, *oracle_rows(w), what=w.name, kv_dtype=w.kv_dtype, flat=cfg != 4)
 
 
 def test_forced_part_counts_agree():
@@ -158,7 +160,7 @@ def test_unused_cache_slots_never_reach_the_result(H, kvd):
     ref = oracle_rows(w)
     for parts in (0, 1, 5):
         out, lse, _ = run_gpu(w, num_parts=parts)
-        compare(out, lse, *ref, what=f"NaN past the end H={H} {kvd} P={parts}")
+        compare(out, lse, *ref, what=f"NaN past the end H={H} {kvd} P={parts}", kv_dtype=kvd)
 
 
 @pytest.mark.parametrize("H", [16, 8])
@@ -237,7 +239,8 @@ def test_q8_late_spike_rescales_accumulated_rows(H):
         w.kv_scales[blk, pos, (512 + d) // 32] = int(np.float16(4.0).view(np.uint16))
     for parts in (1, 0):
         out, lse, _ = run_gpu(w, num_parts=parts)
-        compare(out, lse, *oracle_rows(w), what=f"q8 late spike H={H} P={parts}")
+        compare(out, lse, *oracle_rows(w), what=f"q8 late spike H={H} P={parts}",
+                kv_dtype="q8_0")
 
 
 def test_combine_entry_point_matches_the_oracle():
