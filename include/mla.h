@@ -75,6 +75,10 @@ extern "C" {
 #define MLA_Q8_GROUP 32
 #define MLA_MAX_BATCH 2048   /* sequences per call */
 #define MLA_MAX_ROWS 4096    /* s_q * H */
+/* Device workspace held by mla_decode_noalloc (per device, for the life of
+ * the process): enough for every automatic split plan on a 256-CU MI355X
+ * (at most 2 * 256 * 128 query rows of bf16 partials, 67.4 MB). */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
 
 typedef enum {
   MLA_OK = 0,
@@ -125,6 +129,26 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
                       const void* kv_scales, const int32_t* block_table,
                       const int32_t* seqlens, float softmax_scale, void* out, float* lse,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mla_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). The workspace is a library-owned device array of
+ * MLA_NOALLOC_SCRATCH_BYTES per device, created with the library's code
+ * object and held until the process ends; its address is looked up once per
+ * device on the first call made with that device current. The call itself
+ * makes no allocation of any kind. Arguments, results and errors are those of
+ * mla_decode (same kernels, same plan, bit-identical results), plus
+ * MLA_ERR_UNSUPPORTED when the problem's workspace (mla_workspace_size) would
+ * exceed MLA_NOALLOC_SCRATCH_BYTES; nothing is enqueued then. Every call on a
+ * device shares that device's array, which keeps the last call's contents:
+ * calls whose executions overlap on one device (several streams, several host
+ * threads) race and give undefined results; serialise them.
+ */
+mla_status mla_decode_noalloc(const mla_problem* p, const void* q, const void* kv_cache,
+                              const void* kv_scales, const int32_t* block_table,
+                              const int32_t* seqlens, float softmax_scale, void* out,
+                              float* lse, hipStream_t stream);
 
 /*
  * Log-sum-exp merge of num_splits partial results of the same rows, each

@@ -24,8 +24,9 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
           3: "MLA_ERR_WORKSPACE_TOO_SMALL", 4: "MLA_ERR_HIP"}
 
 # Entry points declared in include/mla.h
-EXPORTS = ("mla_workspace_size", "mla_num_parts", "mla_decode", "mla_combine", "mla_plan",
-           "mla_status_str", "mla_last_error")
+EXPORTS = ("mla_workspace_size", "mla_num_parts", "mla_decode", "mla_decode_noalloc",
+           "mla_combine", "mla_plan", "mla_status_str", "mla_last_error")
+NOALLOC_SCRATCH_BYTES = 72 << 20
 
 
 class MlaError(RuntimeError):
@@ -58,10 +59,11 @@ def lib():
         L.mla_workspace_size.argtypes = [pp, ctypes.POINTER(ctypes.c_size_t)]
         L.mla_num_parts.argtypes = [pp, ctypes.POINTER(i32)]
         L.mla_decode.argtypes = [pp, vp, vp, vp, vp, vp, f32, vp, vp, vp, ctypes.c_size_t, vp]
+        L.mla_decode_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, f32, vp, vp, vp]
         L.mla_combine.argtypes = [i32, i64, vp, vp, vp, vp, vp]
         L.mla_plan.argtypes = [pp, vp, vp, i64, vp]
-        for name in ("mla_workspace_size", "mla_num_parts", "mla_decode", "mla_combine",
-                     "mla_plan"):
+        for name in ("mla_workspace_size", "mla_num_parts", "mla_decode", "mla_decode_noalloc",
+                     "mla_combine", "mla_plan"):
             getattr(L, name).restype = ctypes.c_int
         L.mla_status_str.argtypes = [ctypes.c_int]
         L.mla_status_str.restype = ctypes.c_char_p
@@ -116,19 +118,9 @@ def _require(t: torch.Tensor, name: str, dtype, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
-def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
-               seqlens: torch.Tensor, softmax_scale: float,
-               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, *,
-               kv_scales: Optional[torch.Tensor] = None, max_seqlen: int = 0,
-               num_parts: int = 0, m_tile: int = 0,
-               workspace: Optional[torch.Tensor] = None):
-    """Decode step over a paged latent cache (see include/mla.h).
-
-    q bf16 [B, s_q, H, 576]; kv_cache bf16 [nb, 64, 576] or int8 (q8_0, with
-    kv_scales float16 [nb, 64, 18]); block_table int32 [B, max_blocks];
-    seqlens int32 [B] (device). Returns (out bf16 [B, s_q, H, 512],
-    lse float32 [B, s_q, H]). Runs on the current stream; never synchronises.
-    """
+def _decode_args(q, kv_cache, block_table, seqlens, out, lse, kv_scales, workspace,
+                 max_seqlen, num_parts, m_tile):
+    """Check the decode arguments -> (problem, out, lse, device)."""
     _require(q, "q", torch.bfloat16, 4)
     if q.shape[-1] != D_K:
         raise ValueError("q rows must be 576 wide")
@@ -165,6 +157,24 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         raise ValueError("out must be [B, s_q, H, 512] and lse [B, s_q, H]")
     prob = make_problem(q, kv_cache, block_table, kv_dtype=KV_Q8_0 if q8 else KV_BF16,
                         max_seqlen=max_seqlen, num_parts=num_parts, m_tile=m_tile)
+    return prob, out, lse, dev
+
+
+def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+               seqlens: torch.Tensor, softmax_scale: float,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, *,
+               kv_scales: Optional[torch.Tensor] = None, max_seqlen: int = 0,
+               num_parts: int = 0, m_tile: int = 0,
+               workspace: Optional[torch.Tensor] = None):
+    """Decode step over a paged latent cache (see include/mla.h).
+
+    q bf16 [B, s_q, H, 576]; kv_cache bf16 [nb, 64, 576] or int8 (q8_0, with
+    kv_scales float16 [nb, 64, 18]); block_table int32 [B, max_blocks];
+    seqlens int32 [B] (device). Returns (out bf16 [B, s_q, H, 512],
+    lse float32 [B, s_q, H]). Runs on the current stream; never synchronises.
+    """
+    prob, out, lse, dev = _decode_args(q, kv_cache, block_table, seqlens, out, lse, kv_scales,
+                                       workspace, max_seqlen, num_parts, m_tile)
     with torch.cuda.device(dev):
         ws_bytes = workspace_size(prob)
         if workspace is None:
@@ -173,6 +183,24 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
                                 _ptr(block_table), _ptr(seqlens), float(softmax_scale),
                                 _ptr(out), _ptr(lse), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out, lse
+
+
+def mla_decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                       seqlens: torch.Tensor, softmax_scale: float,
+                       out: torch.Tensor, lse: torch.Tensor, *,
+                       kv_scales: Optional[torch.Tensor] = None, max_seqlen: int = 0,
+                       num_parts: int = 0, m_tile: int = 0):
+    """mla_decode on the library's own per-device workspace (no workspace
+    argument, no allocation by the library): the caller passes out and lse.
+    Calls that overlap on one device race (include/mla.h)."""
+    prob, out, lse, dev = _decode_args(q, kv_cache, block_table, seqlens, out, lse, kv_scales,
+                                       None, max_seqlen, num_parts, m_tile)
+    with torch.cuda.device(dev):
+        _check(lib().mla_decode_noalloc(ctypes.byref(prob), _ptr(q), _ptr(kv_cache),
+                                        _ptr(kv_scales), _ptr(block_table), _ptr(seqlens),
+                                        float(softmax_scale), _ptr(out), _ptr(lse),
+                                        _stream(dev)))
     return out, lse
 
 

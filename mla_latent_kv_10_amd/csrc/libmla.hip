@@ -3062,6 +3062,61 @@ hipError_t launch_rows(const DecodeParams& dp, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Host-side checks shared by the decode entry points; fills *pl.
+mla_status check_decode_args(const mla_problem* p, const void* q, const void* kv_cache,
+                             const void* kv_scales, const int32_t* block_table,
+                             const int32_t* seqlens, float softmax_scale, const void* out,
+                             const float* lse, Plan* pl) {
+  mla_status s = validate_problem(p);
+  if (s != MLA_OK) return s;
+  if (p->batch == 0) return ok();
+  if (!q || !kv_cache || !block_table || !seqlens || !out || !lse)
+    return fail(MLA_ERR_INVALID_ARG, "null array argument");
+  if (p->kv_dtype == MLA_KV_Q8_0 && !kv_scales)
+    return fail(MLA_ERR_INVALID_ARG, "kv_scales is required for MLA_KV_Q8_0");
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
+    return fail(MLA_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seqlens, 4))
+    return fail(MLA_ERR_INVALID_ARG, "lse, block_table and seqlens must be 4-byte aligned");
+  if (p->kv_dtype == MLA_KV_Q8_0 && !aligned(kv_scales, 16))
+    return fail(MLA_ERR_INVALID_ARG, "kv_scales must be 16-byte aligned");
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
+    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  return make_plan(p, pl);
+}
+
+mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* q,
+                              const void* kv_cache, const void* kv_scales,
+                              const int32_t* block_table, const int32_t* seqlens,
+                              float softmax_scale, void* out, float* lse, void* workspace,
+                              hipStream_t stream);
+
+// Workspace of mla_decode_noalloc: one array per device, held until the
+// process ends. In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is taken once per device with
+// hipGetSymbolAddress and only that address is used.
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+mla_status scratch_of_current_device(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MLA_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !a)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -3102,31 +3157,49 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
                       const int32_t* seqlens, float softmax_scale, void* out, float* lse,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   // everything checkable on the host, before any HIP call
-  mla_status s = validate_problem(p);
-  if (s != MLA_OK) return s;
-  if (p->batch == 0) return ok();
-  if (!q || !kv_cache || !block_table || !seqlens || !out || !lse)
-    return fail(MLA_ERR_INVALID_ARG, "null array argument");
-  if (p->kv_dtype == MLA_KV_Q8_0 && !kv_scales)
-    return fail(MLA_ERR_INVALID_ARG, "kv_scales is required for MLA_KV_Q8_0");
-  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
-    return fail(MLA_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
-  if (!aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seqlens, 4))
-    return fail(MLA_ERR_INVALID_ARG, "lse, block_table and seqlens must be 4-byte aligned");
-  if (p->kv_dtype == MLA_KV_Q8_0 && !aligned(kv_scales, 16))
-    return fail(MLA_ERR_INVALID_ARG, "kv_scales must be 16-byte aligned");
-  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
-    return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  Plan pl;
+  mla_status s = check_decode_args(p, q, kv_cache, kv_scales, block_table, seqlens,
+                                   softmax_scale, out, lse, &pl);
+  if (s != MLA_OK || p->batch == 0) return s;
   if (workspace && !aligned(workspace, 16))
     return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  Plan pl;
-  s = make_plan(p, &pl);
-  if (s != MLA_OK) return s;
   if (workspace_bytes < pl.bytes)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.bytes,
                 workspace_bytes);
   if (!workspace) return fail(MLA_ERR_INVALID_ARG, "workspace is NULL");
+  return launch_decode_step(p, pl, q, kv_cache, kv_scales, block_table, seqlens, softmax_scale,
+                            out, lse, workspace, stream);
+}
 
+mla_status mla_decode_noalloc(const mla_problem* p, const void* q, const void* kv_cache,
+                              const void* kv_scales, const int32_t* block_table,
+                              const int32_t* seqlens, float softmax_scale, void* out,
+                              float* lse, hipStream_t stream) {
+  Plan pl;
+  mla_status s = check_decode_args(p, q, kv_cache, kv_scales, block_table, seqlens,
+                                   softmax_scale, out, lse, &pl);
+  if (s != MLA_OK || p->batch == 0) return s;
+  if (pl.bytes > kScratchBytes)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "this problem needs %zu bytes of workspace; mla_decode_noalloc holds at most "
+                "%zu (MLA_NOALLOC_SCRATCH_BYTES): use mla_decode with a workspace",
+                pl.bytes, (size_t)kScratchBytes);
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != MLA_OK) return s;
+  return launch_decode_step(p, pl, q, kv_cache, kv_scales, block_table, seqlens, softmax_scale,
+                            out, lse, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* q,
+                              const void* kv_cache, const void* kv_scales,
+                              const int32_t* block_table, const int32_t* seqlens,
+                              float softmax_scale, void* out, float* lse, void* workspace,
+                              hipStream_t stream) {
   DecodeParams dp;
   dp.q = (const uint16_t*)q;
   dp.kv = (const uint8_t*)kv_cache;
@@ -3183,6 +3256,10 @@ mla_status mla_decode(const mla_problem* p, const void* q, const void* kv_cache,
   }
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 mla_status mla_combine(int32_t num_splits, int64_t rows, const float* partial_out,
                        const float* partial_lse, void* out, float* lse, hipStream_t stream) {
