@@ -71,6 +71,7 @@ extern "C" {
 #define MLA_D_LATENT 512
 #define MLA_D_ROPE 64
 #define MLA_D_K 576
+#define MLA_D_HEAD 128       /* per-head no-RoPE query width and value width */
 #define MLA_BLOCK_TOKENS 64
 #define MLA_Q8_GROUP 32
 #define MLA_MAX_BATCH 2048   /* sequences per call */
@@ -182,6 +183,56 @@ mla_status mla_combine(int32_t num_splits, int64_t rows, const float* partial_ou
  */
 mla_status mla_plan(const mla_problem* p, const int32_t* seqlens, int32_t* plan_out,
                     int64_t plan_capacity, hipStream_t stream);
+
+/*
+ * The steps either side of mla_decode (a decoder layer's MLA attention in
+ * absorbed form). MLA rebuilds per-head keys and values from the cached
+ * latent as k = W_UK c and v = W_UV c ("MLA: Multi-Head Latent Attention --
+ * DeepSeek-AI Explained", section Method); absorbing W_UK into the query and
+ * W_UV into the output (nnets.ru article, section on the essence of MLA;
+ * snowgate.dev forum thread 35, last reply) turns them into these two
+ * per-head products. Rows are query rows r = (b * s_q + i) * H + h, as in
+ * mla_decode; bf16 in and out, fp32 accumulation on the matrix cores.
+ * Deterministic; errors are returned before anything is enqueued.
+ */
+
+/* q_abs[r] = [ W_UK[h]^T q_nope[r] ; q_rope[r] ]: the absorbed query mla_decode takes.
+ *   q_nope bf16 [rows, 128], q_rope bf16 [rows, 64] (already rotated)
+ *   w_uk_t bf16 [H, 512, 128]: W_UK[h] transposed, i.e. w_uk_t[h][d][j] = W_UK[h][j][d]
+ *          where the per-head key is k_j = sum_d W_UK[h][j][d] c_d
+ *   q_abs  bf16 [rows, 576]
+ * rows a multiple of num_heads; all arrays 16-byte aligned. */
+mla_status mla_absorb_query(int64_t rows, int32_t num_heads, const void* q_nope,
+                            const void* q_rope, const void* w_uk_t, void* q_abs,
+                            hipStream_t stream);
+
+/* o[r] = W_UV[h] o_lat[r]: the per-head attention output from mla_decode's
+ * latent-space output.
+ *   o_lat bf16 [rows, 512], w_uv bf16 [H, 128, 512] (v_j = sum_d W_UV[h][j][d] c_d),
+ *   o     bf16 [rows, 128]
+ * rows a multiple of num_heads; all arrays 16-byte aligned. */
+mla_status mla_project_output(int64_t rows, int32_t num_heads, const void* o_lat,
+                              const void* w_uv, void* o, hipStream_t stream);
+
+/* Append the s_q new tokens of a decode step to the paged cache, before
+ * mla_decode reads it: row i of sequence b (rows bf16 [B, s_q, 576], the new
+ * [c_KV | k_rope] with k_rope already rotated) is token t = seqlens[b] - s_q + i
+ * and goes to row t % 64 of block block_table[b][t / 64]. Rows whose position
+ * falls outside [0, 64 * max_blocks_per_seq) or whose block id lies outside
+ * [0, num_blocks) are skipped.
+ *   MLA_KV_BF16: kv_cache bf16 [num_blocks, 64, 576], the row copied as is;
+ *   MLA_KV_Q8_0: kv_cache int8 [num_blocks, 64, 576] + kv_scales fp16
+ *     [num_blocks, 64, 18], written by the q8_0 rule (FlashMLA page of the
+ *     ik_llama.cpp docs, "KV cache with MLA"): per group g of 32 columns,
+ *     d = max |x| / 127 in fp32, scale = fp16(d) rounded to nearest even,
+ *     code = x / d rounded half away from zero, clamped to [-127, 127]
+ *     (max |x| = 0 gives scale 0 and codes 0); rows must be finite.
+ * rows and kv_cache 16-byte aligned, the other arrays 4-byte. Two new rows
+ * aimed at the same slot race. */
+mla_status mla_cache_append(int32_t batch, int32_t seqlen_q, const void* rows,
+                            const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* seqlens, int64_t num_blocks, int32_t kv_dtype,
+                            void* kv_cache, void* kv_scales, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* mla_status_str(mla_status s);

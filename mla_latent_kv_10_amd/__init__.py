@@ -25,7 +25,9 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
 
 # Entry points declared in include/mla.h
 EXPORTS = ("mla_workspace_size", "mla_num_parts", "mla_decode", "mla_decode_noalloc",
-           "mla_combine", "mla_plan", "mla_status_str", "mla_last_error")
+           "mla_combine", "mla_plan", "mla_absorb_query", "mla_project_output",
+           "mla_cache_append", "mla_status_str", "mla_last_error")
+D_HEAD = 128
 NOALLOC_SCRATCH_BYTES = 72 << 20
 
 
@@ -62,8 +64,12 @@ def lib():
         L.mla_decode_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, f32, vp, vp, vp]
         L.mla_combine.argtypes = [i32, i64, vp, vp, vp, vp, vp]
         L.mla_plan.argtypes = [pp, vp, vp, i64, vp]
+        L.mla_absorb_query.argtypes = [i64, i32, vp, vp, vp, vp, vp]
+        L.mla_project_output.argtypes = [i64, i32, vp, vp, vp, vp]
+        L.mla_cache_append.argtypes = [i32, i32, vp, vp, i32, vp, i64, i32, vp, vp, vp]
         for name in ("mla_workspace_size", "mla_num_parts", "mla_decode", "mla_decode_noalloc",
-                     "mla_combine", "mla_plan"):
+                     "mla_combine", "mla_plan", "mla_absorb_query", "mla_project_output",
+                     "mla_cache_append"):
             getattr(L, name).restype = ctypes.c_int
         L.mla_status_str.argtypes = [ctypes.c_int]
         L.mla_status_str.restype = ctypes.c_char_p
@@ -252,3 +258,103 @@ def mla_plan(seqlens: torch.Tensor, *, batch: int, seqlen_q: int, num_heads: int
     return dict(P=P, seq_prefix=buf[:B + 1], part_start=buf[B + 1:B + P + 2],
                 seq_first_part=buf[B + P + 2:2 * B + P + 2],
                 seq_last_part=buf[2 * B + P + 2:3 * B + P + 2])
+
+
+def _on_device(name: str, t: torch.Tensor, dev):
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def mla_absorb_query(q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk_t: torch.Tensor,
+                     q_abs: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q_abs = [W_UK[h]^T q_nope ; q_rope] per query row (include/mla.h).
+
+    q_nope bf16 [..., H, 128], q_rope bf16 [..., H, 64], w_uk_t bf16 [H, 512, 128]
+    (W_UK transposed per head) -> q_abs bf16 [..., H, 576]."""
+    _require(w_uk_t, "w_uk_t", torch.bfloat16, 3)
+    H = w_uk_t.shape[0]
+    if tuple(w_uk_t.shape[1:]) != (D_LATENT, D_HEAD):
+        raise ValueError("w_uk_t must be [H, 512, 128]")
+    if q_nope.dtype != torch.bfloat16 or q_rope.dtype != torch.bfloat16:
+        raise TypeError("q_nope and q_rope must be bfloat16")
+    if not (q_nope.is_contiguous() and q_rope.is_contiguous()):
+        raise ValueError("q_nope and q_rope must be contiguous")
+    if q_nope.shape[-2:] != (H, D_HEAD) or q_rope.shape[-2:] != (H, D_ROPE) \
+            or q_nope.shape[:-1] != q_rope.shape[:-1]:
+        raise ValueError("q_nope must be [..., H, 128] and q_rope [..., H, 64]")
+    dev = q_nope.device
+    if dev.type != "cuda":
+        raise ValueError("libmla runs on the GPU only")
+    for name, t in (("q_rope", q_rope), ("w_uk_t", w_uk_t)):
+        _on_device(name, t, dev)
+    rows = q_nope.numel() // D_HEAD
+    if q_abs is None:
+        q_abs = torch.empty(q_nope.shape[:-1] + (D_K,), dtype=torch.bfloat16, device=dev)
+    if q_abs.dtype != torch.bfloat16 or not q_abs.is_contiguous() or q_abs.numel() != rows * D_K:
+        raise ValueError("q_abs must be contiguous bf16 [..., H, 576]")
+    _on_device("q_abs", q_abs, dev)
+    with torch.cuda.device(dev):
+        _check(lib().mla_absorb_query(rows, H, _ptr(q_nope), _ptr(q_rope), _ptr(w_uk_t),
+                                      _ptr(q_abs), _stream(dev)))
+    return q_abs
+
+
+def mla_project_output(o_lat: torch.Tensor, w_uv: torch.Tensor,
+                       o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """o = W_UV[h] o_lat per query row: o_lat bf16 [..., H, 512], w_uv bf16
+    [H, 128, 512] -> o bf16 [..., H, 128]."""
+    _require(w_uv, "w_uv", torch.bfloat16, 3)
+    H = w_uv.shape[0]
+    if tuple(w_uv.shape[1:]) != (D_HEAD, D_LATENT):
+        raise ValueError("w_uv must be [H, 128, 512]")
+    if o_lat.dtype != torch.bfloat16 or not o_lat.is_contiguous() or o_lat.shape[-2:] != (H, D_LATENT):
+        raise ValueError("o_lat must be contiguous bf16 [..., H, 512]")
+    dev = o_lat.device
+    if dev.type != "cuda":
+        raise ValueError("libmla runs on the GPU only")
+    _on_device("w_uv", w_uv, dev)
+    rows = o_lat.numel() // D_LATENT
+    if o is None:
+        o = torch.empty(o_lat.shape[:-1] + (D_HEAD,), dtype=torch.bfloat16, device=dev)
+    if o.dtype != torch.bfloat16 or not o.is_contiguous() or o.numel() != rows * D_HEAD:
+        raise ValueError("o must be contiguous bf16 [..., H, 128]")
+    _on_device("o", o, dev)
+    with torch.cuda.device(dev):
+        _check(lib().mla_project_output(rows, H, _ptr(o_lat), _ptr(w_uv), _ptr(o),
+                                        _stream(dev)))
+    return o
+
+
+def mla_cache_append(rows: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor,
+                     kv_cache: torch.Tensor, kv_scales: Optional[torch.Tensor] = None) -> None:
+    """Write the new rows (bf16 [B, s_q, 576]) of a decode step into the paged
+    cache in place: bf16 [nb, 64, 576], or int8 q8_0 with kv_scales float16
+    [nb, 64, 18] (include/mla.h)."""
+    _require(rows, "rows", torch.bfloat16, 3)
+    if rows.shape[-1] != D_K:
+        raise ValueError("rows must be [B, s_q, 576]")
+    B, s_q, _ = rows.shape
+    _require(block_table, "block_table", torch.int32, 2)
+    _require(seqlens, "seqlens", torch.int32, 1)
+    q8 = kv_cache.dtype == torch.int8
+    _require(kv_cache, "kv_cache", torch.int8 if q8 else torch.bfloat16, 3)
+    if tuple(kv_cache.shape[1:]) != (BLOCK_TOKENS, D_K):
+        raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    if q8:
+        if kv_scales is None:
+            raise ValueError("kv_scales is required for an int8 (q8_0) cache")
+        _require(kv_scales, "kv_scales", torch.float16, 3)
+    if block_table.shape[0] != B or seqlens.shape[0] != B:
+        raise ValueError("block_table and seqlens must have B rows")
+    dev = rows.device
+    if dev.type != "cuda":
+        raise ValueError("libmla runs on the GPU only")
+    for name, t in (("block_table", block_table), ("seqlens", seqlens), ("kv_cache", kv_cache),
+                    ("kv_scales", kv_scales)):
+        if t is not None:
+            _on_device(name, t, dev)
+    with torch.cuda.device(dev):
+        _check(lib().mla_cache_append(B, s_q, _ptr(rows), _ptr(block_table),
+                                      block_table.shape[1], _ptr(seqlens), kv_cache.shape[0],
+                                      KV_Q8_0 if q8 else KV_BF16, _ptr(kv_cache), _ptr(kv_scales),
+                                      _stream(dev)))

@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB_PATH = os.path.join(PKG, "libmla.so")
-SOURCES = [os.path.join(PKG, "csrc", "libmla.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "libmla.hip"), os.path.join(PKG, "csrc", "mla_proj.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -2911,6 +2911,15 @@ mla_status ok() {
   return MLA_OK;
 }
 
+}  // namespace
+
+namespace mla_internal {
+// error string of the other entry points of the library (csrc/mla_proj.hip)
+__attribute__((visibility("hidden"))) void set_last_error(const char* msg) { g_last_error = msg; }
+}  // namespace mla_internal
+
+namespace {
+
 int device_cus() {
   static std::mutex mu;
   static int cache[64] = {0};

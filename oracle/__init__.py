@@ -67,6 +67,12 @@ def _load():
         lib.oracle_combine.restype = None
         lib.oracle_plan.argtypes = [i32, vp, i32, i32, vp, vp, vp, vp]
         lib.oracle_plan.restype = ctypes.c_int
+        lib.oracle_fp16_bits.argtypes = [ctypes.c_float]
+        lib.oracle_fp16_bits.restype = u16
+        lib.oracle_quantize_q8_0_row.argtypes = [vp, vp, vp]
+        lib.oracle_quantize_q8_0_row.restype = None
+        lib.oracle_cache_append.argtypes = [i32, i32, i32, vp, vp, i32, vp, i64, vp, vp]
+        lib.oracle_cache_append.restype = i64
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -195,6 +201,38 @@ def project_output(o_lat, w_uv):
     out = np.empty(o_lat.shape[:-1] + (D_HEAD,), np.float64)
     _load().oracle_project_output(rows, H, _p(o_lat), _p(_c(w_uv, np.float64)), _p(out))
     return out
+
+
+def fp16_bits(x: float) -> int:
+    """IEEE binary16 bits of float32 x, round to nearest even."""
+    return int(_load().oracle_fp16_bits(float(np.float32(x))))
+
+
+def quantize_q8_0(x):
+    """q8_0 cache writer on float32 rows of 576 -> (int8 codes, fp16 scale bits [.., 18])."""
+    x = _c(x, np.float32)
+    rows = x.size // D_K
+    flat = x.reshape(rows, D_K)
+    q = np.empty((rows, D_K), np.int8)
+    sc = np.empty((rows, D_K // 32), np.uint16)
+    for r in range(rows):
+        _load().oracle_quantize_q8_0_row(_p(flat[r]), _p(q[r]), _p(sc[r]))
+    return q.reshape(x.shape), sc.reshape(x.shape[:-1] + (D_K // 32,))
+
+
+def cache_append(rows, block_table, seqlens, kv, kv_scales=None):
+    """Write the new rows (bf16 bits [B, s_q, 576]) into the paged cache kv
+    (bf16 bits or int8 with kv_scales), in place. Returns rows written."""
+    rows = _c(rows, np.uint16)
+    B, s_q, dk = rows.shape
+    assert dk == D_K and kv.flags["C_CONTIGUOUS"]
+    kind = 0 if kv.dtype == np.uint16 else 1
+    if kind == 1:
+        assert kv_scales is not None and kv_scales.flags["C_CONTIGUOUS"]
+    bt = _c(block_table, np.int32)
+    sl = _c(seqlens, np.int32)
+    return int(_load().oracle_cache_append(B, s_q, kind, _p(rows), _p(bt), bt.shape[1], _p(sl),
+                                           kv.shape[0], _p(kv), _p(kv_scales)))
 
 
 def combine(part_out, part_lse):

@@ -85,6 +85,61 @@ double oracle_q8_value(int8_t qv, uint16_t scale_bits) {
 int oracle_max_threads(void) { return omp_get_max_threads(); }
 void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 
+/* IEEE 754 binary16 bits of a float, rounded to nearest (ties to even):
+ * overflow to infinity from 65520 up (65504 plus half a unit in the last
+ * place), subnormals below 2^-14 in steps of 2^-24. NaN gives 0x7E00. */
+uint16_t oracle_fp16_bits(float f) {
+  const double v0 = (double)f;
+  if (isnan(v0)) return 0x7E00;
+  const uint16_t sign = signbit(v0) ? 0x8000 : 0;
+  const double v = fabs(v0);
+  if (v >= 65520.0) return sign | 0x7C00;
+  if (v < ldexp(1.0, -14)) {
+    /* subnormal (or zero): v = m * 2^-24, m rounded to nearest even; m = 1024
+     * is the smallest normal, whose bits are 0x0400 as well */
+    const double m = rint(ldexp(v, 24));
+    return sign | (uint16_t)m;
+  }
+  int ex;
+  frexp(v, &ex);                     /* v = f * 2^ex, f in [0.5, 1) */
+  int E = ex - 1;                    /* v = 1.x * 2^E */
+  double sig = rint(ldexp(v, 10 - E));   /* in [1024, 2048] */
+  if (sig >= 2048.0) {
+    sig = 1024.0;
+    ++E;
+  }
+  if (E + 15 >= 31) return sign | 0x7C00;
+  return sign | (uint16_t)((E + 15) << 10) | (uint16_t)(sig - 1024.0);
+}
+
+/* q8_0 cache writer for one row of 576 values, the quantisation behind the
+ * q8_0 cache type (FlashMLA page, "KV cache with MLA"): per group g of 32
+ * columns, a = max |x|, d = a / 127 in fp32, stored scale fp16(d) (nearest
+ * even), code = x / d (fp32) rounded half away from zero and clamped to
+ * [-127, 127]; a = 0 gives scale 0 and codes 0. A cached value is then
+ * fp16(d) * code. */
+void oracle_quantize_q8_0_row(const float* x, int8_t* q, uint16_t* scales) {
+  for (int g = 0; g < Q8_GROUPS; ++g) {
+    const float* xs = x + g * Q8_GROUP;
+    float amax = 0.0f;
+    for (int k = 0; k < Q8_GROUP; ++k)
+      if (fabsf(xs[k]) > amax) amax = fabsf(xs[k]);
+    const float d = amax / 127.0f;
+    scales[g] = oracle_fp16_bits(d);
+    for (int k = 0; k < Q8_GROUP; ++k) {
+      float c = 0.0f;
+      if (d > 0.0f) {
+        const float r = xs[k] / d;
+        const float t = truncf(r);
+        c = fabsf(r - t) >= 0.5f ? t + (r > 0.0f ? 1.0f : -1.0f) : t;
+      }
+      if (c > 127.0f) c = 127.0f;
+      if (c < -127.0f) c = -127.0f;
+      q[g * Q8_GROUP + k] = (int8_t)c;
+    }
+  }
+}
+
 /* ------------------------------------------------------------ paged cache */
 
 typedef struct {
@@ -275,6 +330,46 @@ int oracle_decode_absorbed_f64q(int32_t B, int32_t s_q, int32_t H, const double*
   cache_view c = {kv_kind, kv, kv_scales, num_blocks, block_table, max_blocks};
   return decode_absorbed_core(B, s_q, H, NULL, q, &c, seqlens, softmax_scale, NULL, 0, out,
                               lse, NULL);
+}
+
+/* ------------------------------------------------------------ cache append */
+
+/*
+ * Appending the new tokens of a decode step to the paged cache: the s_q new
+ * rows of sequence b are its last s_q tokens, so new row i lands at position
+ * t = L_b - s_q + i (L_b = seqlens[b], which already counts them), i.e. in row
+ * t % 64 of physical block block_table[b][t / 64]. Positions outside
+ * [0, 64 * max_blocks) and blocks outside [0, num_blocks) are skipped.
+ *   rows   bf16 bits [B, s_q, 576]: the new [c_KV | k_rope] rows
+ *   kind 0: kv bf16 bits [num_blocks, 64, 576], written as given;
+ *   kind 1: kv int8 [num_blocks, 64, 576] + scales fp16 bits [num_blocks, 64, 18],
+ *           written by the q8_0 cache writer above.
+ * Returns the number of rows written.
+ */
+int64_t oracle_cache_append(int32_t B, int32_t s_q, int32_t kind, const uint16_t* rows,
+                            const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seqlens, int64_t num_blocks, void* kv,
+                            uint16_t* scales) {
+  int64_t written = 0;
+  float x[D_K];
+  for (int32_t b = 0; b < B; ++b) {
+    for (int32_t i = 0; i < s_q; ++i) {
+      const int64_t t = (int64_t)seqlens[b] - s_q + i;
+      if (t < 0 || t >= (int64_t)max_blocks * BLOCK_TOKENS) continue;
+      const int32_t blk = block_table[(int64_t)b * max_blocks + t / BLOCK_TOKENS];
+      if (blk < 0 || (int64_t)blk >= num_blocks) continue;
+      const int64_t dst = (int64_t)blk * BLOCK_TOKENS + t % BLOCK_TOKENS;
+      const uint16_t* src = rows + ((int64_t)b * s_q + i) * D_K;
+      if (kind == 0) {
+        memcpy((uint16_t*)kv + dst * D_K, src, sizeof(uint16_t) * D_K);
+      } else {
+        for (int d = 0; d < D_K; ++d) x[d] = (float)oracle_bf16_value(src[d]);
+        oracle_quantize_q8_0_row(x, (int8_t*)kv + dst * D_K, scales + dst * Q8_GROUPS);
+      }
+      ++written;
+    }
+  }
+  return written;
 }
 
 /* ------------------------------------------ decompressed (non-absorbed) form */
