@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=WORKLOAD_CFG, help="workload index 1..5")
+    ap.add_argument("--config", type=int, default=WORKLOAD_CFG,
+                    help="workload index 1..5 (6: the bench shape over an fp8 cache)")
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--m-tile", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -177,16 +178,21 @@ def main():
     if w.kv_dtype == "bf16":
         kv0 = torch.from_numpy(w.kv.view(np.int16)).view(torch.bfloat16).to(dev)
         sc0 = None
+    elif w.kv_dtype == "fp8":
+        kv0 = torch.from_numpy(w.kv).to(dev)
+        sc0 = torch.from_numpy(w.kv_scales).to(dev)
     else:
         kv0 = torch.from_numpy(w.kv).to(dev)
         sc0 = torch.from_numpy(w.kv_scales.view(np.int16)).view(torch.float16).to(dev)
-    cache_bytes = kv0.numel() * kv0.element_size() + (0 if sc0 is None else sc0.numel() * 2)
+    cache_bytes = kv0.numel() * kv0.element_size() + (
+        0 if sc0 is None else sc0.numel() * sc0.element_size())
     copies = max(1, int(np.ceil(3 * 256e6 / cache_bytes)) + 1)
     kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
     scs = [sc0] + [None if sc0 is None else sc0.clone() for _ in range(copies - 1)]
     out = torch.empty((w.B, w.s_q, w.H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.s_q, w.H), dtype=torch.float32, device=dev)
-    prob = mla.make_problem(q, kv0, bt, kv_dtype=mla.KV_Q8_0 if sc0 is not None else mla.KV_BF16,
+    prob = mla.make_problem(q, kv0, bt, kv_dtype={"bf16": mla.KV_BF16, "q8_0": mla.KV_Q8_0,
+                                                  "fp8": mla.KV_FP8}[w.kv_dtype],
                             max_seqlen=w.max_seqlen, num_parts=args.num_parts,
                             m_tile=args.m_tile)
     ws = torch.empty(max(16, mla.workspace_size(prob)), dtype=torch.uint8, device=dev)
@@ -263,7 +269,8 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w.kv_dtype == "bf16" else "q8_0 cache, bf16 MFMA",
+        "dtype": {"bf16": "bf16", "q8_0": "q8_0 cache, bf16 MFMA",
+                  "fp8": "fp8 (e4m3) cache, bf16 MFMA"}[w.kv_dtype],
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seqlen": seqlen_desc,
                    "seqlen_q": w.s_q, "kv_cache": f"{w.kv_dtype}, paged 64-token blocks, "

@@ -31,6 +31,9 @@
  *                int8  [num_blocks, 64, 576]   (MLA_KV_Q8_0) with
  *   kv_scales    fp16  [num_blocks, 64, 18]    scale g covers columns 32g .. 32g+31;
  *                                              a cached value is scale * int8
+ *                uint8 [num_blocks, 64, 576]   (MLA_KV_FP8: OCP e4m3, 1-4-3, bias 7) with
+ *   kv_scales    fp32  [num_blocks, 64]        one scale per token; a cached value
+ *                                              is scale * e4m3 (576 + 4 bytes a token)
  *   block_table  int32 [B, max_blocks_per_seq] token t of sequence b is row t % 64
  *                                              of block block_table[b][t / 64]
  *   seqlens      int32 [B]                     cached tokens of sequence b,
@@ -89,7 +92,7 @@ typedef enum {
   MLA_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
 } mla_status;
 
-typedef enum { MLA_KV_BF16 = 0, MLA_KV_Q8_0 = 1 } mla_kv_dtype;
+typedef enum { MLA_KV_BF16 = 0, MLA_KV_Q8_0 = 1, MLA_KV_FP8 = 2 } mla_kv_dtype;
 
 /* Problem descriptor (host struct, read during a call only). */
 typedef struct {
@@ -104,10 +107,10 @@ typedef struct {
   int32_t kv_dtype;           /* mla_kv_dtype */
   int32_t num_parts;          /* 0: automatic; else P >= 1 KV partitions (see mla_plan) */
   int32_t m_tile;             /* 0: automatic; else 16, 32, 64 or 128 query rows
-                                 per workgroup (16: bf16 cache only).
-                                 Automatic picks the smallest tile that holds
-                                 seqlen_q * num_heads rows (16 only for bf16),
-                                 else 128. */
+                                 per workgroup (16: bf16 cache only; fp8 cache:
+                                 128 only). Automatic picks the smallest tile
+                                 that holds seqlen_q * num_heads rows (16 only
+                                 for bf16), else 128; always 128 for fp8. */
 } mla_problem;
 
 /* Bytes of device workspace mla_decode needs for *p (written to *bytes, host).
@@ -226,7 +229,12 @@ mla_status mla_project_output(int64_t rows, int32_t num_heads, const void* o_lat
  *     ik_llama.cpp docs, "KV cache with MLA"): per group g of 32 columns,
  *     d = max |x| / 127 in fp32, scale = fp16(d) rounded to nearest even,
  *     code = x / d rounded half away from zero, clamped to [-127, 127]
- *     (max |x| = 0 gives scale 0 and codes 0); rows must be finite.
+ *     (max |x| = 0 gives scale 0 and codes 0);
+ *   MLA_KV_FP8: kv_cache uint8 [num_blocks, 64, 576] + kv_scales fp32 [num_blocks, 64]:
+ *     one scale per token, d = max |x| / 448 (fp32, stored as is), code = OCP E4M3
+ *     of x / d, nearest even, saturated to +-448 (the forum's fp8 KV cache,
+ *     snowgate.dev thread 35); max |x| = 0 gives scale 0 and codes 0.
+ * rows must be finite.
  * rows and kv_cache 16-byte aligned, the other arrays 4-byte. Two new rows
  * aimed at the same slot race. */
 mla_status mla_cache_append(int32_t batch, int32_t seqlen_q, const void* rows,

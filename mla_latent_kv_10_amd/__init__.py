@@ -17,7 +17,7 @@ import torch
 from ._build import LIB_PATH, build  # noqa: F401
 
 D_LATENT, D_ROPE, D_K, BLOCK_TOKENS = 512, 64, 576, 64
-KV_BF16, KV_Q8_0 = 0, 1
+KV_BF16, KV_Q8_0, KV_FP8 = 0, 1, 2
 MAX_BATCH, MAX_ROWS = 2048, 4096
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
@@ -124,22 +124,40 @@ def _require(t: torch.Tensor, name: str, dtype, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _cache_kind(kv_cache: torch.Tensor) -> int:
+    """bf16 -> KV_BF16, int8 -> KV_Q8_0, uint8 -> KV_FP8 (E4M3 bytes)."""
+    kinds = {torch.bfloat16: KV_BF16, torch.int8: KV_Q8_0, torch.uint8: KV_FP8}
+    if not isinstance(kv_cache, torch.Tensor) or kv_cache.dtype not in kinds:
+        raise TypeError("kv_cache must be a bfloat16, int8 (q8_0) or uint8 (fp8 E4M3) tensor")
+    _require(kv_cache, "kv_cache", kv_cache.dtype, 3)
+    return kinds[kv_cache.dtype]
+
+
+def _check_scales(kind: int, kv_cache: torch.Tensor, kv_scales):
+    if kind == KV_BF16:
+        return
+    if kv_scales is None:
+        raise ValueError("kv_scales is required for a quantised (q8_0 or fp8) cache")
+    if kind == KV_Q8_0:
+        _require(kv_scales, "kv_scales", torch.float16, 3)
+        if tuple(kv_scales.shape) != (kv_cache.shape[0], BLOCK_TOKENS, D_K // 32):
+            raise ValueError("kv_scales must be [num_blocks, 64, 18]")
+    else:
+        _require(kv_scales, "kv_scales", torch.float32, 2)
+        if tuple(kv_scales.shape) != (kv_cache.shape[0], BLOCK_TOKENS):
+            raise ValueError("kv_scales must be [num_blocks, 64] (fp32, one per token)")
+
+
 def _decode_args(q, kv_cache, block_table, seqlens, out, lse, kv_scales, workspace,
                  max_seqlen, num_parts, m_tile):
     """Check the decode arguments -> (problem, out, lse, device)."""
     _require(q, "q", torch.bfloat16, 4)
     if q.shape[-1] != D_K:
         raise ValueError("q rows must be 576 wide")
-    q8 = kv_cache.dtype == torch.int8
-    _require(kv_cache, "kv_cache", torch.int8 if q8 else torch.bfloat16, 3)
+    kind = _cache_kind(kv_cache)
     if tuple(kv_cache.shape[1:]) != (BLOCK_TOKENS, D_K):
         raise ValueError("kv_cache must be [num_blocks, 64, 576]")
-    if q8:
-        if kv_scales is None:
-            raise ValueError("kv_scales is required for an int8 (q8_0) cache")
-        _require(kv_scales, "kv_scales", torch.float16, 3)
-        if tuple(kv_scales.shape) != (kv_cache.shape[0], BLOCK_TOKENS, D_K // 32):
-            raise ValueError("kv_scales must be [num_blocks, 64, 18]")
+    _check_scales(kind, kv_cache, kv_scales)
     _require(block_table, "block_table", torch.int32, 2)
     _require(seqlens, "seqlens", torch.int32, 1)
     B, s_q, H, _ = q.shape
@@ -161,7 +179,7 @@ def _decode_args(q, kv_cache, block_table, seqlens, out, lse, kv_scales, workspa
     _require(lse, "lse", torch.float32, 3)
     if tuple(out.shape) != (B, s_q, H, D_LATENT) or tuple(lse.shape) != (B, s_q, H):
         raise ValueError("out must be [B, s_q, H, 512] and lse [B, s_q, H]")
-    prob = make_problem(q, kv_cache, block_table, kv_dtype=KV_Q8_0 if q8 else KV_BF16,
+    prob = make_problem(q, kv_cache, block_table, kv_dtype=kind,
                         max_seqlen=max_seqlen, num_parts=num_parts, m_tile=m_tile)
     return prob, out, lse, dev
 
@@ -174,8 +192,9 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
                workspace: Optional[torch.Tensor] = None):
     """Decode step over a paged latent cache (see include/mla.h).
 
-    q bf16 [B, s_q, H, 576]; kv_cache bf16 [nb, 64, 576] or int8 (q8_0, with
-    kv_scales float16 [nb, 64, 18]); block_table int32 [B, max_blocks];
+    q bf16 [B, s_q, H, 576]; kv_cache bf16 [nb, 64, 576], int8 (q8_0, with
+    kv_scales float16 [nb, 64, 18]) or uint8 (fp8 E4M3, with kv_scales
+    float32 [nb, 64]); block_table int32 [B, max_blocks];
     seqlens int32 [B] (device). Returns (out bf16 [B, s_q, H, 512],
     lse float32 [B, s_q, H]). Runs on the current stream; never synchronises.
     """
@@ -328,22 +347,18 @@ def mla_project_output(o_lat: torch.Tensor, w_uv: torch.Tensor,
 def mla_cache_append(rows: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor,
                      kv_cache: torch.Tensor, kv_scales: Optional[torch.Tensor] = None) -> None:
     """Write the new rows (bf16 [B, s_q, 576]) of a decode step into the paged
-    cache in place: bf16 [nb, 64, 576], or int8 q8_0 with kv_scales float16
-    [nb, 64, 18] (include/mla.h)."""
+    cache in place: bf16 [nb, 64, 576], int8 q8_0 with kv_scales float16
+    [nb, 64, 18], or uint8 fp8 with kv_scales float32 [nb, 64] (include/mla.h)."""
     _require(rows, "rows", torch.bfloat16, 3)
     if rows.shape[-1] != D_K:
         raise ValueError("rows must be [B, s_q, 576]")
     B, s_q, _ = rows.shape
     _require(block_table, "block_table", torch.int32, 2)
     _require(seqlens, "seqlens", torch.int32, 1)
-    q8 = kv_cache.dtype == torch.int8
-    _require(kv_cache, "kv_cache", torch.int8 if q8 else torch.bfloat16, 3)
+    kind = _cache_kind(kv_cache)
     if tuple(kv_cache.shape[1:]) != (BLOCK_TOKENS, D_K):
         raise ValueError("kv_cache must be [num_blocks, 64, 576]")
-    if q8:
-        if kv_scales is None:
-            raise ValueError("kv_scales is required for an int8 (q8_0) cache")
-        _require(kv_scales, "kv_scales", torch.float16, 3)
+    _check_scales(kind, kv_cache, kv_scales)
     if block_table.shape[0] != B or seqlens.shape[0] != B:
         raise ValueError("block_table and seqlens must have B rows")
     dev = rows.device
@@ -356,5 +371,5 @@ def mla_cache_append(rows: torch.Tensor, block_table: torch.Tensor, seqlens: tor
     with torch.cuda.device(dev):
         _check(lib().mla_cache_append(B, s_q, _ptr(rows), _ptr(block_table),
                                       block_table.shape[1], _ptr(seqlens), kv_cache.shape[0],
-                                      KV_Q8_0 if q8 else KV_BF16, _ptr(kv_cache), _ptr(kv_scales),
+                                      kind, _ptr(kv_cache), _ptr(kv_scales),
                                       _stream(dev)))

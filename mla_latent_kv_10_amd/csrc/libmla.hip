@@ -59,6 +59,9 @@ constexpr int kQ8ScaleRowBytes = 36;
 constexpr int kQ8TileBytes = kTile * kQ8RowBytes;               // 18432
 constexpr int kQ8ScaleTileBytes = kTile * kQ8ScaleRowBytes;     // 1152
 constexpr int kQ8StageBytes = kQ8TileBytes + 2048;              // int8 + scales, padded
+// fp8 (e4m3) tiles: 32 rows x 576 bytes plus 32 fp32 per-token scales
+constexpr int kFp8TileBytes = kTile * kDK;                      // 18432
+constexpr int kFp8StageBytes = kFp8TileBytes + 1024;            // fp8 + scales, padded
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
@@ -2225,38 +2228,47 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   }
 }
 
-// --------------------------------- q8_0 decode kernel (128-row tile)
+// ------------------- q8_0 / fp8 decode kernel (128-row tile, converted tiles)
 
-// q8_0 cache, 128 query rows per workgroup, 4 waves; wave w computes the
-// scores and the softmax of rows 32w..32w+31 and the value product of all 128
-// rows for output columns 128w..128w+127 (the division of the 128-row bf16
-// kernel). Per 32-token tile, in four phases separated by barriers:
-//  1. the int8 tile (18 KiB) and its scales (1152 B), copied by LDS-DMA into a
-//     3-stage ring, are converted once by all threads into two bf16 tiles in
-//     the row-group layout: hi = bf16(scale * value) and
-//     lo = bf16(scale * value - hi). The product of an fp16 scale and an int8
-//     value is exact in fp32 and hi + lo equals it to within 2^-17 relative,
-//     so scores over hi and lo are the exact dequantised scores up to fp32
-//     accumulation; tokens past the end of the sequence convert to zero;
-//  2. scores S^T = K q~^T over hi and lo (two MFMA chains of 36 steps);
+// Quantised cache (q8_0 or fp8), 128 query rows per workgroup, 4 waves; wave w
+// computes the scores and the softmax of rows 32w..32w+31 and the value
+// product of all 128 rows for output columns 128w..128w+127 (the division of
+// the 128-row bf16 kernel). Per 32-token tile, in four phases separated by
+// barriers:
+//  1. the quantised tile (18 KiB of int8 or E4M3 bytes) and its scales,
+//     copied by LDS-DMA into a 3-stage ring, are converted once by all threads
+//     into bf16 tiles in the row-group layout.
+//     q8_0: hi = bf16(scale * value) and lo = bf16(scale * value - hi). The
+//     product of an fp16 scale and an int8 value is exact in fp32 and hi + lo
+//     equals it to within 2^-17 relative, so scores over hi and lo are the
+//     exact dequantised scores up to fp32 accumulation.
+//     fp8: hi = the E4M3 value itself, which bf16 holds exactly; the token's
+//     fp32 scale multiplies its score and its probability instead (one scale
+//     per token, so it factors out of both products).
+//     Tokens past the end of the sequence convert to zero;
+//  2. scores S^T = K q~^T over hi and lo (two MFMA chains of 36 steps; one for
+//     fp8);
 //  3. online softmax of the wave's rows (lazy reference maximum), P published
 //     through LDS with the rescale requests;
-//  4. value product O^T += V^T P^T with V = hi, the dequantised value rounded
-//     to bf16.
+//  4. value product O^T += V^T P^T with V = hi (q8_0: the dequantised value
+//     rounded to bf16; fp8: exact, the scale rides on P).
 // Compared with converting the int8 operands in every wave and scaling each
 // 32-column group's partial score (the 32/64-row q8_0 kernel), the conversion
 // work is done once per tile for all 128 rows and the scores are pure MFMA
 // work.
-template <bool NT>
-__global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) {
+template <bool NT, int KV>
+__global__ __launch_bounds__(256, 1) void mla_decode_cvt_kernel(DecodeParams a) {
+  static_assert(KV == MLA_KV_Q8_0 || KV == MLA_KV_FP8, "cache type");
+  constexpr bool FP8 = KV == MLA_KV_FP8;
   constexpr int NW = 4;
   constexpr int NTH = 64 * NW;
   constexpr int MT = 128;
-  constexpr int NST = 3;                  // int8 ring stages
+  constexpr int NST = 3;                  // ring stages of the quantised tiles
   constexpr int KPF = 2;                  // score k-steps in flight (hi and lo each)
-  constexpr int CPW = 5;                  // 1 KiB copies per wave per tile (20 per tile)
+  constexpr int CPW = 5;                  // 1 KiB copies per wave per tile (at most 20 per tile)
+  constexpr int STAGE = FP8 ? kFp8StageBytes : kQ8StageBytes;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NST][kQ8StageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NST][STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t s_hl[2][kTileBytes];   // hi, lo
   __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];   // P, B-operand layout
   __shared__ float s_alpha[MT];
@@ -2383,10 +2395,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
       bad = bad || __any(inval && bt_base + lane < seg_len);
       bt_lane = inval ? 0 : bt_lane;
     };
-    // Copies of int8 tile idx into ring stage idx % 3: copy k = wave + 4 j
-    // (k < 18: int8 bytes 1024 k .. of the tile, contiguous; k = 18, 19: the
-    // 1152 bytes of scales, the tail of copy 19 reading the first bytes again
-    // into the stage's padding).
+    // Copies of quantised tile idx into ring stage idx % 3: copy k = wave + 4 j
+    // (k < 18: bytes 1024 k .. of the tile's 32 rows, contiguous (int8 or
+    // fp8); q8_0: k = 18, 19: the 1152 bytes of scales, the tail of copy 19
+    // reading the first bytes again into the stage's padding; fp8: k = 18:
+    // the 128 bytes of per-token scales, lanes past them re-reading the
+    // first bytes into the padding).
     auto issue = [&](int idx) {
       int rel = (idx >> 1) - bt_base;   // lane of the segment's id window
       if (rel >= 64) {
@@ -2399,17 +2413,31 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
       const int64_t phys = uniform(__builtin_amdgcn_readlane(bt_lane, rel));
       const int64_t row0 = phys * kBT + ((t_begin + idx) & 1) * kTile;
       const uint8_t* src = a.kv + row0 * kQ8RowBytes;
-      const uint8_t* ssrc = a.kv_scales + row0 * kQ8ScaleRowBytes;
       const uint32_t dst = lds_addr_of(s_ring[idx % NST]);
+      if constexpr (FP8) {
+        const uint8_t* ssrc = a.kv_scales + row0 * 4;
 #pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        const int k = wave + 4 * j;
-        if (k < 18) {
-          copy(src + 1024 * k, 16 * lane, dst + 1024 * k);
-        } else {
-          // scales: default policy (the tail lanes re-read a partial line)
-          const int off = 1024 * (k - 18) + 16 * lane;
-          dma16_sbase(ssrc, off < kQ8ScaleTileBytes ? off : 0, dst + kQ8TileBytes + 1024 * (k - 18));
+        for (int j = 0; j < CPW; ++j) {
+          const int k = wave + 4 * j;
+          if (k < 18) {
+            copy(src + 1024 * k, 16 * lane, dst + 1024 * k);
+          } else if (k == 18) {
+            const int off = 16 * lane;
+            dma16_sbase(ssrc, off < 4 * kTile ? off : 0, dst + kFp8TileBytes);
+          }
+        }
+      } else {
+        const uint8_t* ssrc = a.kv_scales + row0 * kQ8ScaleRowBytes;
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+          const int k = wave + 4 * j;
+          if (k < 18) {
+            copy(src + 1024 * k, 16 * lane, dst + 1024 * k);
+          } else {
+            // scales: default policy (the tail lanes re-read a partial line)
+            const int off = 1024 * (k - 18) + 16 * lane;
+            dma16_sbase(ssrc, off < kQ8ScaleTileBytes ? off : 0, dst + kQ8TileBytes + 1024 * (k - 18));
+          }
         }
       }
     };
@@ -2436,8 +2464,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
     for (int it = 0; it < n_run; ++it) {
       // ---- 1. int8 tile it landed (tile it+1 may be in flight); everyone is
       // done with the previous tile's hi / lo / P
-      if (it + 1 < n_run) wait_vmcnt<CPW>();
-      else wait_vmcnt<0>();
+      // copies this wave issued per tile: q8_0 5; fp8 5, or 4 in wave 3
+      if (it + 1 < n_run) {
+        if (FP8 && wave == 3)
+          wait_vmcnt<CPW - 1>();
+        else
+          wait_vmcnt<CPW>();
+      } else {
+        wait_vmcnt<0>();
+      }
       lds_barrier();
       if (it + 2 < n_run) issue(it + 2);
       {
@@ -2455,40 +2490,59 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
         const int t = 8 * wave + rr;
         const uint32_t keep = t < valid ? 0xffffffffu : 0u;
         const LDS_AS uint8_t* srow = st + kQ8RowBytes * t + 8 * cc;
-        const LDS_AS uint32_t* scl =
-            reinterpret_cast<const LDS_AS uint32_t*>(st + kQ8TileBytes + kQ8ScaleRowBytes * t);
-        uint64_t raw[9];
-        uint32_t sc2[9];
+        if constexpr (FP8) {
+          // fp8 (e4m3) to bf16 is exact (3 mantissa bits fit in 7, and every
+          // e4m3 exponent, subnormals included, is a normal bf16 one); the
+          // per-token scale is applied to the scores and probabilities
+          uint64_t raw[9];
 #pragma unroll
-        for (int i = 0; i < 9; ++i) {
-          raw[i] = *reinterpret_cast<const LDS_AS uint64_t*>(srow + 64 * i);
-          sc2[i] = scl[i];   // scales of groups 2i, 2i+1; chunk 8i + cc is group 2i + (cc >> 2)
-        }
-        const int sh16 = 16 * (cc >> 2);
+          for (int i = 0; i < 9; ++i) raw[i] = *reinterpret_cast<const LDS_AS uint64_t*>(srow + 64 * i);
 #pragma unroll
-        for (int i = 0; i < 9; ++i) {
-          // the scale is zeroed too: a NaN or infinite scale in an unused
-          // slot would otherwise reach the value product as 0 * inf
-          const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)((sc2[i] & keep) >> sh16));
-          const uint32_t wv[2] = {(uint32_t)raw[i] & keep, (uint32_t)(raw[i] >> 32) & keep};
-          u32x4 whi, wlo;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const uint32_t word = wv[e2 >> 1];
-            const float x0 = d * (float)(int8_t)(word >> (16 * (e2 & 1)));
-            const float x1 = d * (float)(int8_t)(word >> (16 * (e2 & 1) + 8));
-            const uint32_t h = pack_bf16x2(x0, x1);
-            const float h0 = __builtin_bit_cast(float, h << 16);
-            const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
-            whi[e2] = h;
-            wlo[e2] = pack_bf16x2(x0 - h0, x1 - h1);
+          for (int i = 0; i < 9; ++i) {
+            const uint32_t w0 = (uint32_t)raw[i] & keep, w1 = (uint32_t)(raw[i] >> 32) & keep;
+            u32x4 whi;
+            whi[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+            whi[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+            whi[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+            whi[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+            *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[0] + 16 * (tid + NTH * i)) = whi;
           }
-          const int U = tid + NTH * i;
-          *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[0] + 16 * U) = whi;
-          *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[1] + 16 * U) = wlo;
+        } else {
+          const LDS_AS uint32_t* scl =
+              reinterpret_cast<const LDS_AS uint32_t*>(st + kQ8TileBytes + kQ8ScaleRowBytes * t);
+          uint64_t raw[9];
+          uint32_t sc2[9];
+#pragma unroll
+          for (int i = 0; i < 9; ++i) {
+            raw[i] = *reinterpret_cast<const LDS_AS uint64_t*>(srow + 64 * i);
+            sc2[i] = scl[i];   // scales of groups 2i, 2i+1; chunk 8i + cc is group 2i + (cc >> 2)
+          }
+          const int sh16 = 16 * (cc >> 2);
+#pragma unroll
+          for (int i = 0; i < 9; ++i) {
+            // the scale is zeroed too: a NaN or infinite scale in an unused
+            // slot would otherwise reach the value product as 0 * inf
+            const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)((sc2[i] & keep) >> sh16));
+            const uint32_t wv[2] = {(uint32_t)raw[i] & keep, (uint32_t)(raw[i] >> 32) & keep};
+            u32x4 whi, wlo;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const uint32_t word = wv[e2 >> 1];
+              const float x0 = d * (float)(int8_t)(word >> (16 * (e2 & 1)));
+              const float x1 = d * (float)(int8_t)(word >> (16 * (e2 & 1) + 8));
+              const uint32_t h = pack_bf16x2(x0, x1);
+              const float h0 = __builtin_bit_cast(float, h << 16);
+              const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+              whi[e2] = h;
+              wlo[e2] = pack_bf16x2(x0 - h0, x1 - h1);
+            }
+            const int U = tid + NTH * i;
+            *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[0] + 16 * U) = whi;
+            *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[1] + 16 * U) = wlo;
+          }
         }
       }
-      lds_barrier();   // hi and lo of tile it visible
+      lds_barrier();   // hi (and lo) of tile it visible
 
       // ---- 2. scores of the wave's 32 rows over hi and lo (two chains)
       const LDS_AS uint8_t* khi = (const LDS_AS uint8_t*)s_hl[0];
@@ -2498,24 +2552,40 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
       };
       f32x16 sh, sl;
       bf16x8 kh[KPF], kl[KPF];
+      if constexpr (FP8) {
+        // one chain: the converted values are exact
+        constexpr int KF = 2 * KPF;
+        bf16x8 kf8[KF];
 #pragma unroll
-      for (int j2 = 0; j2 < KPF; ++j2) {
-        kh[j2] = rd(khi, j2);
-        kl[j2] = rd(klo, j2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      unroll<36>([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        mfma_score(sh, kh[k % KPF], qf[k], k == 0);
-        mfma_score(sl, kl[k % KPF], qf[k], k == 0);
-        if constexpr (k + KPF < 36) {
-          kh[k % KPF] = rd(khi, k + KPF);
-          kl[k % KPF] = rd(klo, k + KPF);
+        for (int j2 = 0; j2 < KF; ++j2) kf8[j2] = rd(khi, j2);
+        __builtin_amdgcn_sched_barrier(0);
+        unroll<36>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          mfma_score(sh, kf8[k % KF], qf[k], k == 0);
+          if constexpr (k + KF < 36) kf8[k % KF] = rd(khi, k + KF);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        mfma_vgpr_drain(sh);
+      } else {
+#pragma unroll
+        for (int j2 = 0; j2 < KPF; ++j2) {
+          kh[j2] = rd(khi, j2);
+          kl[j2] = rd(klo, j2);
         }
         __builtin_amdgcn_sched_barrier(0);
-      });
-      mfma_vgpr_drain(sh);
-      mfma_vgpr_drain(sl);
+        unroll<36>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          mfma_score(sh, kh[k % KPF], qf[k], k == 0);
+          mfma_score(sl, kl[k % KPF], qf[k], k == 0);
+          if constexpr (k + KPF < 36) {
+            kh[k % KPF] = rd(khi, k + KPF);
+            kl[k % KPF] = rd(klo, k + KPF);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        mfma_vgpr_drain(sh);
+        mfma_vgpr_drain(sl);
+      }
 
       // ---- 3. online softmax of the wave's rows (log2 domain); element i of
       // the lane is token 8 (i >> 2) + 4 hi + (i & 3) of row l32
@@ -2524,10 +2594,29 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
       const bool masked = !__all(t0 + kTile <= n_vis);
       const int limx = masked ? n_vis - t0 - 4 * hi : kTile;
       float x[16];
+      // fp8: per-token scales of the lane's 16 tokens 8 j + 4 hi + (0..3);
+      // a masked token's scale is zeroed (an unused slot may hold NaN)
+      float tsc[16];
+      if constexpr (FP8) {
+        const LDS_AS uint8_t* sst = (const LDS_AS uint8_t*)s_ring[it % NST] + kFp8TileBytes;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v4 = *reinterpret_cast<const LDS_AS f32x4*>(sst + 4 * (8 * j + 4 * hi));
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) tsc[4 * j + r4] = v4[r4];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float sv = (sh[i] + sl[i]) * cs;
-        x[i] = (!masked || 8 * (i >> 2) + (i & 3) < limx) ? sv : -INFINITY;
+        const bool vis = !masked || 8 * (i >> 2) + (i & 3) < limx;
+        float sv;
+        if constexpr (FP8) {
+          tsc[i] = vis ? tsc[i] : 0.f;
+          sv = sh[i] * (cs * tsc[i]);
+        } else {
+          sv = (sh[i] + sl[i]) * cs;
+        }
+        x[i] = vis ? sv : -INFINITY;
       }
       float lmax = max3f(x[0], x[1], x[2]);
       lmax = max3f(lmax, x[3], x[4]);
@@ -2551,7 +2640,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
         const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
         const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
         psum += p0 + p1;
-        pw[j] = pack_bf16x2(p0, p1);
+        // fp8: V is scale * value; the scale rides on the probability
+        if constexpr (FP8)
+          pw[j] = pack_bf16x2(p0 * tsc[2 * j], p1 * tsc[2 * j + 1]);
+        else
+          pw[j] = pack_bf16x2(p0, p1);
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
@@ -2938,7 +3031,7 @@ int device_cus() {
 
 struct Plan {
   bool narrow;   // 16-row tile (bf16 cache)
-  bool q8w;      // 128-row tile (q8_0 cache)
+  bool q8w;      // 128-row tile converted to bf16 in LDS (q8_0 or fp8 cache)
   int HG, CG, MT, m_tiles, P, M;
   size_t off_prefix, off_lse, off_o, bytes;
 };
@@ -2960,7 +3053,7 @@ mla_status validate_problem(const mla_problem* p) {
     return fail(MLA_ERR_UNSUPPORTED, "block table too large");
   if (p->num_blocks < 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks must be >= 0");
   if (p->max_seqlen < 0) return fail(MLA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
-  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_Q8_0)
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_Q8_0 && p->kv_dtype != MLA_KV_FP8)
     return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);
   if (p->num_parts < 0) return fail(MLA_ERR_INVALID_ARG, "num_parts must be >= 0");
   if (p->m_tile != 0 && p->m_tile != 16 && p->m_tile != 32 && p->m_tile != 64 &&
@@ -2985,17 +3078,23 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   // rows than one tile holds take several row tiles per KV part, placed on
   // the same XCD so the second read of each cache tile hits L2.
   const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
+  const bool fp8 = p->kv_dtype == MLA_KV_FP8;
   if (q8 && p->m_tile == 16)
     return fail(MLA_ERR_UNSUPPORTED, "m_tile %d is not available for the q8_0 cache", p->m_tile);
-  pl->narrow = !q8 && (p->m_tile == 16 || (p->m_tile == 0 && M <= 16));
+  if (fp8 && p->m_tile != 0 && p->m_tile != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "the fp8 cache takes 128-row tiles only (m_tile %d)",
+                p->m_tile);
+  pl->narrow = !q8 && !fp8 && (p->m_tile == 16 || (p->m_tile == 0 && M <= 16));
   if (pl->narrow) {
     pl->HG = 1;
+  } else if (fp8) {
+    pl->HG = 4;
   } else if (p->m_tile) {
     pl->HG = p->m_tile / 32;
   } else {
     pl->HG = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   }
-  pl->q8w = q8 && pl->HG == 4;
+  pl->q8w = (q8 || fp8) && pl->HG == 4;
   pl->CG = q8 ? (pl->q8w ? 1 : 4) : 4 / pl->HG;
   pl->MT = pl->narrow ? 16 : 32 * pl->HG;
   pl->m_tiles = (M + pl->MT - 1) / pl->MT;
@@ -3049,11 +3148,12 @@ hipError_t launch_pipe(const DecodeParams& dp, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_q8w(const DecodeParams& dp, int grid, hipStream_t stream) {
+template <int KV>
+hipError_t launch_cvt(const DecodeParams& dp, int grid, hipStream_t stream) {
   if (dp.m_tiles == 1)
-    hipLaunchKernelGGL(mla_decode_q8w_kernel<true>, dim3(grid), dim3(256), 0, stream, dp);
+    hipLaunchKernelGGL((mla_decode_cvt_kernel<true, KV>), dim3(grid), dim3(256), 0, stream, dp);
   else
-    hipLaunchKernelGGL(mla_decode_q8w_kernel<false>, dim3(grid), dim3(256), 0, stream, dp);
+    hipLaunchKernelGGL((mla_decode_cvt_kernel<false, KV>), dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -3081,13 +3181,13 @@ mla_status check_decode_args(const mla_problem* p, const void* q, const void* kv
   if (p->batch == 0) return ok();
   if (!q || !kv_cache || !block_table || !seqlens || !out || !lse)
     return fail(MLA_ERR_INVALID_ARG, "null array argument");
-  if (p->kv_dtype == MLA_KV_Q8_0 && !kv_scales)
-    return fail(MLA_ERR_INVALID_ARG, "kv_scales is required for MLA_KV_Q8_0");
+  if (p->kv_dtype != MLA_KV_BF16 && !kv_scales)
+    return fail(MLA_ERR_INVALID_ARG, "kv_scales is required for a quantised cache");
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16))
     return fail(MLA_ERR_INVALID_ARG, "q, kv_cache and out must be 16-byte aligned");
   if (!aligned(lse, 4) || !aligned(block_table, 4) || !aligned(seqlens, 4))
     return fail(MLA_ERR_INVALID_ARG, "lse, block_table and seqlens must be 4-byte aligned");
-  if (p->kv_dtype == MLA_KV_Q8_0 && !aligned(kv_scales, 16))
+  if (p->kv_dtype != MLA_KV_BF16 && !aligned(kv_scales, 16))
     return fail(MLA_ERR_INVALID_ARG, "kv_scales must be 16-byte aligned");
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
@@ -3235,22 +3335,37 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
 
   const int grid = pl.P * pl.m_tiles;
   hipError_t e;
-  const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
-  if (pl.narrow) {
-    e = launch_narrow(dp, grid, stream);
-  } else if (!q8) {
-    switch (pl.HG) {
-      case 1: e = launch_rows<1>(dp, grid, stream); break;
-      case 2: e = launch_rows<2>(dp, grid, stream); break;
-      case 4: e = launch_pipe(dp, grid, stream); break;
-      default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
-    }
-  } else if (pl.q8w) {
-    e = launch_q8w(dp, grid, stream);
-  } else if (pl.HG == 2) {
-    e = launch_decode<2, 4, true>(dp, grid, stream);
-  } else {
-    e = launch_decode<1, 4, true>(dp, grid, stream);
+  // every cache type has its own kernels: a kernel reads the cache in its
+  // own row size (1152 B bf16, 576 B int8 or E4M3)
+  switch (p->kv_dtype) {
+    case MLA_KV_BF16:
+      if (pl.narrow) {
+        e = launch_narrow(dp, grid, stream);
+      } else {
+        switch (pl.HG) {
+          case 1: e = launch_rows<1>(dp, grid, stream); break;
+          case 2: e = launch_rows<2>(dp, grid, stream); break;
+          case 4: e = launch_pipe(dp, grid, stream); break;
+          default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
+        }
+      }
+      break;
+    case MLA_KV_Q8_0:
+      if (pl.q8w)
+        e = launch_cvt<MLA_KV_Q8_0>(dp, grid, stream);
+      else if (pl.HG == 2)
+        e = launch_decode<2, 4, true>(dp, grid, stream);
+      else if (pl.HG == 1)
+        e = launch_decode<1, 4, true>(dp, grid, stream);
+      else
+        return fail(MLA_ERR_UNSUPPORTED, "no q8_0 kernel for this row tile");
+      break;
+    case MLA_KV_FP8:
+      if (!pl.q8w) return fail(MLA_ERR_UNSUPPORTED, "no fp8 kernel for this row tile");
+      e = launch_cvt<MLA_KV_FP8>(dp, grid, stream);
+      break;
+    default:
+      return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);
   }
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   if (pl.P > 1) {

@@ -2,7 +2,7 @@
 //  * query absorption   q~ = [W_UK[h]^T q_nope ; q_rope]     (128 -> 512 per head)
 //  * output projection  o  = W_UV[h] o_lat                    (512 -> 128 per head)
 //  * cache append       the new [c_KV | k_rope] rows of a decode step written
-//                       into the paged cache (bf16, or q8_0-quantised)
+//                       into the paged cache (bf16, q8_0- or fp8-quantised)
 // MLA recovers per-head keys and values from the cached latent through
 // k = W_UK c and v = W_UV c ("MLA: Multi-Head Latent Attention -- DeepSeek-AI
 // Explained", section Method); folding W_UK into the query and W_UV into the
@@ -144,6 +144,26 @@ __global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict
   }
 }
 
+// OCP E4M3 encoding of a finite float (1 sign, 4 exponent bits with bias 7,
+// 3 fraction bits, no infinities, S.1111.111 = NaN): nearest, ties to even,
+// saturated to +-448. Below 2^-6 the values are subnormal, steps of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_rne(float f) {
+  const uint32_t sign = f < 0.0f || (f == 0.0f && signbit(f)) ? 0x80u : 0u;
+  const float a = fabsf(f);
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
+  int ex;
+  frexpf(a, &ex);
+  int e = ex - 1;
+  float m = rintf(ldexpf(a, 3 - e));   // 8 .. 16
+  if (m >= 16.0f) {
+    m = 8.0f;
+    ++e;
+  }
+  if (e > 8) return sign | 0x7Eu;
+  const uint32_t code = (uint32_t)(((e + 7) << 3) | ((int)m - 8));
+  return sign | (code == 0x7Fu ? 0x7Eu : code);
+}
+
 // Cache append: one wave per new row. Row i of sequence b is token
 // t = seqlens[b] - s_q + i; positions outside the block table and block ids
 // outside the pool are skipped (nothing is written for that row).
@@ -170,6 +190,42 @@ __global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__
     u32x4* d = reinterpret_cast<u32x4*>(kv + dst * kDK * 2);
     const u32x4* s = reinterpret_cast<const u32x4*>(src);
     for (int u = lane; u < kDK * 2 / 16; u += 64) d[u] = s[u];
+    return;
+  }
+  if (kind == MLA_KV_FP8) {
+    // one fp32 scale per token, d = max |x| / 448, code = E4M3(x / d): lane
+    // l < 36 holds values 16 l .. 16 l + 15
+    const bool act = lane < kDK / 16;
+    float x[16];
+    float amax = 0.0f;
+    if (act) {
+      const u32x4* s = reinterpret_cast<const u32x4*>(src + 16 * lane);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 w = s[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
+          x[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) amax = fabsf(x[k]) > amax ? fabsf(x[k]) : amax;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const float d = amax / 448.0f;
+    if (act) {
+      uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t code = d > 0.0f ? e4m3_rne(x[k] / d) : 0u;
+        packed[k >> 2] |= code << (8 * (k & 3));
+      }
+      *reinterpret_cast<u32x4*>(kv + dst * kDK + 16 * lane) =
+          u32x4{packed[0], packed[1], packed[2], packed[3]};
+      if (lane == 0) reinterpret_cast<float*>(scales)[dst] = d;
+    }
     return;
   }
   // q8_0
@@ -289,7 +345,7 @@ mla_status mla_cache_append(int32_t batch, int32_t seqlen_q, const void* rows,
     mla_set_last_error("batch >= 0, seqlen_q >= 1, max_blocks_per_seq >= 1, num_blocks >= 0");
     return MLA_ERR_INVALID_ARG;
   }
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_Q8_0) {
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_Q8_0 && kv_dtype != MLA_KV_FP8) {
     mla_set_last_error("unknown kv_dtype");
     return MLA_ERR_INVALID_ARG;
   }
@@ -298,7 +354,7 @@ mla_status mla_cache_append(int32_t batch, int32_t seqlen_q, const void* rows,
     return MLA_ERR_UNSUPPORTED;
   }
   if (batch == 0) return MLA_OK;
-  if (!rows || !block_table || !seqlens || !kv_cache || (kv_dtype == MLA_KV_Q8_0 && !kv_scales)) {
+  if (!rows || !block_table || !seqlens || !kv_cache || (kv_dtype != MLA_KV_BF16 && !kv_scales)) {
     mla_set_last_error("null array argument");
     return MLA_ERR_INVALID_ARG;
   }

@@ -67,6 +67,12 @@ def _load():
         lib.oracle_combine.restype = None
         lib.oracle_plan.argtypes = [i32, vp, i32, i32, vp, vp, vp, vp]
         lib.oracle_plan.restype = ctypes.c_int
+        lib.oracle_fp8_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp8_value.restype = dbl
+        lib.oracle_fp8_bits.argtypes = [ctypes.c_float]
+        lib.oracle_fp8_bits.restype = ctypes.c_uint8
+        lib.oracle_quantize_fp8_row.argtypes = [vp, vp, vp]
+        lib.oracle_quantize_fp8_row.restype = None
         lib.oracle_fp16_bits.argtypes = [ctypes.c_float]
         lib.oracle_fp16_bits.restype = u16
         lib.oracle_quantize_q8_0_row.argtypes = [vp, vp, vp]
@@ -110,11 +116,34 @@ def q8_value(q: int, scale_bits: int) -> float:
     return _load().oracle_q8_value(q, scale_bits)
 
 
+def fp8_value(bits: int) -> float:
+    """OCP E4M3 byte -> its value (exact)."""
+    return _load().oracle_fp8_value(bits)
+
+
+def fp8_bits(x: float) -> int:
+    """float32 -> OCP E4M3 byte, nearest even, saturated to +-448."""
+    return int(_load().oracle_fp8_bits(float(np.float32(x))))
+
+
+def quantize_fp8(x):
+    """fp8 cache writer on float32 rows of 576 -> (uint8 codes, float32 scale per row)."""
+    x = _c(x, np.float32)
+    rows = x.size // D_K
+    flat = x.reshape(rows, D_K)
+    q = np.empty((rows, D_K), np.uint8)
+    sc = np.empty(rows, np.float32)
+    for r in range(rows):
+        _load().oracle_quantize_fp8_row(_p(flat[r]), _p(q[r]), sc[r:].ctypes.data)
+    return q.reshape(x.shape), sc.reshape(x.shape[:-1])
+
+
 def decode_absorbed(q, kv, block_table, seqlens, softmax_scale, *, kv_scales=None, rows=None,
                     with_abs=False):
     """Absorbed-form decode (fp64). q: uint16 [B, s_q, H, 576] bf16 bits.
 
-    kv: uint16 bf16 bits or int8 (with kv_scales uint16 fp16 bits [nb, 64, 18]).
+    kv: uint16 bf16 bits, int8 (with kv_scales uint16 fp16 bits [nb, 64, 18]) or
+    uint8 fp8 E4M3 (with kv_scales float32 [nb, 64]).
     rows: optional int64 row ids r = (b * s_q + i) * H + h.
     Returns (out float64 [n, 512], lse float64 [n]); all rows -> shaped [B, s_q, H, ...].
     with_abs: also return out_abs = sum_t p_t |row_t| (same shape as out).
@@ -122,9 +151,9 @@ def decode_absorbed(q, kv, block_table, seqlens, softmax_scale, *, kv_scales=Non
     q = _c(q, np.uint16)
     B, s_q, H, dk = q.shape
     assert dk == D_K
-    kind = 0 if kv.dtype == np.uint16 else 1
-    kv = _c(kv, np.uint16 if kind == 0 else np.int8)
-    sc = None if kind == 0 else _c(kv_scales, np.uint16)
+    kind = {np.dtype(np.uint16): 0, np.dtype(np.int8): 1, np.dtype(np.uint8): 2}[kv.dtype]
+    kv = _c(kv, kv.dtype)
+    sc = None if kind == 0 else _c(kv_scales, np.uint16 if kind == 1 else np.float32)
     bt = _c(block_table, np.int32)
     sl = _c(seqlens, np.int32)
     rr = None if rows is None else _c(rows, np.int64)
@@ -226,8 +255,8 @@ def cache_append(rows, block_table, seqlens, kv, kv_scales=None):
     rows = _c(rows, np.uint16)
     B, s_q, dk = rows.shape
     assert dk == D_K and kv.flags["C_CONTIGUOUS"]
-    kind = 0 if kv.dtype == np.uint16 else 1
-    if kind == 1:
+    kind = {np.dtype(np.uint16): 0, np.dtype(np.int8): 1, np.dtype(np.uint8): 2}[kv.dtype]
+    if kind:
         assert kv_scales is not None and kv_scales.flags["C_CONTIGUOUS"]
     bt = _c(block_table, np.int32)
     sl = _c(seqlens, np.int32)

@@ -80,6 +80,57 @@ double oracle_q8_value(int8_t qv, uint16_t scale_bits) {
   return oracle_fp16_value(scale_bits) * (double)qv;
 }
 
+/* OCP 8-bit float E4M3 (the "fp8" of the forum's fp8 KV cache; 1 sign, 4
+ * exponent bits with bias 7, 3 fraction bits, no infinities): exponent 0 is
+ * subnormal (m/8 * 2^-6), S.1111.111 is NaN, the largest finite value is
+ * 1.75 * 2^8 = 448. Exact in double. */
+double oracle_fp8_value(uint8_t bits) {
+  const int s = bits >> 7, e = (bits >> 3) & 0xF, m = bits & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10);
+  return s ? -v : v;
+}
+
+/* E4M3 encoding of a finite float, rounded to nearest (ties to even) and
+ * saturated to +-448 (the NaN code is never produced for a finite input). */
+uint8_t oracle_fp8_bits(float f) {
+  const uint8_t sign = signbit(f) ? 0x80 : 0;
+  const double a = fabs((double)f);
+  if (a < ldexp(1.0, -6)) {                  /* subnormal range: steps of 2^-9 */
+    const double m = rint(ldexp(a, 9));      /* 0 .. 8; 8 is the smallest normal */
+    return sign | (uint8_t)m;
+  }
+  int ex;
+  frexp(a, &ex);                             /* a = f * 2^ex, f in [0.5, 1) */
+  int E = ex - 1;
+  double sig = rint(ldexp(a, 3 - E));        /* 8 .. 16 */
+  if (sig >= 16.0) {
+    sig = 8.0;
+    ++E;
+  }
+  if (E > 8) return sign | 0x7E;
+  uint8_t code = (uint8_t)(((E + 7) << 3) | (int)(sig - 8.0));
+  if (code == 0x7F) code = 0x7E;             /* above 448: saturate */
+  return sign | code;
+}
+
+/* fp8 cache writer for one row of 576 values: one fp32 scale per token,
+ * d = max |x| / 448, stored as is; code = E4M3(x / d) (fp32 division); a row
+ * of zeros gives d = 0 and codes 0. A cached value is d * E4M3 value. */
+void oracle_quantize_fp8_row(const float* x, uint8_t* q, float* scale) {
+  float amax = 0.0f;
+  for (int d = 0; d < D_K; ++d)
+    if (fabsf(x[d]) > amax) amax = fabsf(x[d]);
+  const float dsc = amax / 448.0f;
+  *scale = dsc;
+  for (int d = 0; d < D_K; ++d) q[d] = dsc > 0.0f ? oracle_fp8_bits(x[d] / dsc) : 0;
+}
+
 /* Host threads the parallel loops below use (OpenMP), and a way to change it
  * (timing a single core). */
 int oracle_max_threads(void) { return omp_get_max_threads(); }
@@ -143,9 +194,9 @@ void oracle_quantize_q8_0_row(const float* x, int8_t* q, uint16_t* scales) {
 /* ------------------------------------------------------------ paged cache */
 
 typedef struct {
-  int kind; /* 0: bf16 bits, 1: q8_0 */
+  int kind; /* 0: bf16 bits, 1: q8_0, 2: fp8 with per-token fp32 scales */
   const void* kv;
-  const uint16_t* scales;
+  const void* scales;
   int64_t num_blocks;
   const int32_t* block_table;
   int32_t max_blocks;
@@ -159,10 +210,14 @@ static void cache_row(const cache_view* c, int32_t b, int64_t t, double* dst) {
   if (c->kind == 0) {
     const uint16_t* r = (const uint16_t*)c->kv + row * D_K;
     for (int d = 0; d < D_K; ++d) dst[d] = oracle_bf16_value(r[d]);
-  } else {
+  } else if (c->kind == 1) {
     const int8_t* r = (const int8_t*)c->kv + row * D_K;
-    const uint16_t* s = c->scales + row * Q8_GROUPS;
+    const uint16_t* s = (const uint16_t*)c->scales + row * Q8_GROUPS;
     for (int d = 0; d < D_K; ++d) dst[d] = oracle_q8_value(r[d], s[d / Q8_GROUP]);
+  } else {
+    const uint8_t* r = (const uint8_t*)c->kv + row * D_K;
+    const double s = (double)((const float*)c->scales)[row];
+    for (int d = 0; d < D_K; ++d) dst[d] = s * oracle_fp8_value(r[d]);
   }
 }
 
@@ -288,15 +343,16 @@ static int decode_absorbed_core(int32_t B, int32_t s_q, int32_t H, const uint16_
 /*
  * Absorbed-form decode, the contract of the GPU kernel.
  *   q          bf16 bits [B, s_q, H, 576], row r = (b * s_q + i) * H + h
- *   kv         bf16 bits or int8 [num_blocks, 64, 576] (kv_kind 0 / 1)
- *   kv_scales  fp16 bits [num_blocks, 64, 18] for q8_0, else NULL
+ *   kv         bf16 bits, int8 or fp8 [num_blocks, 64, 576] (kv_kind 0 / 1 / 2)
+ *   kv_scales  fp16 bits [num_blocks, 64, 18] for q8_0, fp32 [num_blocks, 64]
+ *              for fp8, else NULL
  *   block_table int32 [B, max_blocks]; seqlens int32 [B] (new tokens included)
  *   rows       optional list of row ids to compute (NULL = all, in order)
  *   out        double [n_rows, 512];  lse double [n_rows] (natural log)
  * Returns 0, or -1 if a row id is out of range.
  */
 int oracle_decode_absorbed(int32_t B, int32_t s_q, int32_t H, const uint16_t* q,
-                           int32_t kv_kind, const void* kv, const uint16_t* kv_scales,
+                           int32_t kv_kind, const void* kv, const void* kv_scales,
                            int64_t num_blocks, const int32_t* block_table, int32_t max_blocks,
                            const int32_t* seqlens, double softmax_scale, const int64_t* rows,
                            int64_t n_rows, double* out, double* lse) {
@@ -311,7 +367,7 @@ int oracle_decode_absorbed(int32_t B, int32_t s_q, int32_t H, const uint16_t* q,
  * u * out_abs[e], which is what an error bound for such arithmetic scales
  * with; out_abs >= |out| always, with equality when all terms share a sign. */
 int oracle_decode_absorbed_abs(int32_t B, int32_t s_q, int32_t H, const uint16_t* q,
-                               int32_t kv_kind, const void* kv, const uint16_t* kv_scales,
+                               int32_t kv_kind, const void* kv, const void* kv_scales,
                                int64_t num_blocks, const int32_t* block_table,
                                int32_t max_blocks, const int32_t* seqlens, double softmax_scale,
                                const int64_t* rows, int64_t n_rows, double* out, double* lse,
@@ -323,7 +379,7 @@ int oracle_decode_absorbed_abs(int32_t B, int32_t s_q, int32_t H, const uint16_t
 
 /* Same, with an fp64 query [B, s_q, H, 576] (used for the absorption check). */
 int oracle_decode_absorbed_f64q(int32_t B, int32_t s_q, int32_t H, const double* q,
-                                int32_t kv_kind, const void* kv, const uint16_t* kv_scales,
+                                int32_t kv_kind, const void* kv, const void* kv_scales,
                                 int64_t num_blocks, const int32_t* block_table,
                                 int32_t max_blocks, const int32_t* seqlens,
                                 double softmax_scale, double* out, double* lse) {
@@ -343,13 +399,15 @@ int oracle_decode_absorbed_f64q(int32_t B, int32_t s_q, int32_t H, const double*
  *   rows   bf16 bits [B, s_q, 576]: the new [c_KV | k_rope] rows
  *   kind 0: kv bf16 bits [num_blocks, 64, 576], written as given;
  *   kind 1: kv int8 [num_blocks, 64, 576] + scales fp16 bits [num_blocks, 64, 18],
- *           written by the q8_0 cache writer above.
+ *           written by the q8_0 cache writer above;
+ *   kind 2: kv fp8 [num_blocks, 64, 576] + scales fp32 [num_blocks, 64], written by
+ *           the fp8 cache writer above.
  * Returns the number of rows written.
  */
 int64_t oracle_cache_append(int32_t B, int32_t s_q, int32_t kind, const uint16_t* rows,
                             const int32_t* block_table, int32_t max_blocks,
                             const int32_t* seqlens, int64_t num_blocks, void* kv,
-                            uint16_t* scales) {
+                            void* scales) {
   int64_t written = 0;
   float x[D_K];
   for (int32_t b = 0; b < B; ++b) {
@@ -364,7 +422,10 @@ int64_t oracle_cache_append(int32_t B, int32_t s_q, int32_t kind, const uint16_t
         memcpy((uint16_t*)kv + dst * D_K, src, sizeof(uint16_t) * D_K);
       } else {
         for (int d = 0; d < D_K; ++d) x[d] = (float)oracle_bf16_value(src[d]);
-        oracle_quantize_q8_0_row(x, (int8_t*)kv + dst * D_K, scales + dst * Q8_GROUPS);
+        if (kind == 1)
+          oracle_quantize_q8_0_row(x, (int8_t*)kv + dst * D_K, (uint16_t*)scales + dst * Q8_GROUPS);
+        else
+          oracle_quantize_fp8_row(x, (uint8_t*)kv + dst * D_K, (float*)scales + dst);
       }
       ++written;
     }

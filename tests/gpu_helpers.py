@@ -31,8 +31,11 @@ import workload as wl
 #   4. a q8_0 cache: the dequantised value scale * int8 (exact in fp32) is
 #      rounded to bf16 for the value product (the scores use it unrounded).
 # So k = 3 for a bf16 cache and 4 for a q8_0 cache (the split case bounds the
-# unsplit one). The 2e-2 term absorbs what is left: fp32 accumulation, the
-# exp2 approximation and score rounding, all orders of magnitude smaller.
+# unsplit one). An fp8 (E4M3) cache converts to bf16 exactly and its
+# per-token scale multiplies the score and the probability in fp32 before
+# rounding (1), so k = 3 as for bf16. The 2e-2 term absorbs what is left:
+# fp32 accumulation, the exp2 approximation and score rounding, all orders of
+# magnitude smaller.
 # A flat 2e-2 cannot hold in general: bf16 cannot hold values above 8 to
 # within 2e-2, and the long-context workload's x8 rows reach |out| = 30.
 # Where the workload keeps A_e small enough for the flat bound to be
@@ -41,7 +44,7 @@ import workload as wl
 #   |lse_gpu - lse_ref| <= 1e-3 (absolute).
 OUT_ABS_TOL = 2e-2
 BF16_U = 2.0 ** -8
-ROUNDINGS = {"bf16": 3, "q8_0": 4}
+ROUNDINGS = {"bf16": 3, "q8_0": 4, "fp8": 3}
 OUT_REL_TOL = 1e-2
 LSE_ABS_TOL = 1e-3
 
@@ -71,6 +74,9 @@ def device_inputs(w: wl.Workload, dev="cuda"):
     if w.kv_dtype == "bf16":
         t["kv"] = torch.from_numpy(w.kv.view(np.int16)).view(torch.bfloat16).to(dev)
         t["kv_scales"] = None
+    elif w.kv_dtype == "fp8":
+        t["kv"] = torch.from_numpy(w.kv).to(dev)
+        t["kv_scales"] = torch.from_numpy(w.kv_scales).to(dev)
     else:
         t["kv"] = torch.from_numpy(w.kv).to(dev)
         t["kv_scales"] = torch.from_numpy(w.kv_scales.view(np.int16)).view(torch.float16).to(dev)

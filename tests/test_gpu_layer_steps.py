@@ -91,7 +91,7 @@ def test_project_output_matches_the_oracle(B, s_q, H):
     assert np.all(err <= _product_bar(ref, mag, 512))
 
 
-@pytest.mark.parametrize("kvd", ["bf16", "q8_0"])
+@pytest.mark.parametrize("kvd", ["bf16", "q8_0", "fp8"])
 def test_cache_append_is_bit_exact(kvd):
     """Every byte of the cache after an append equals the oracle's: the new
     rows land at their positions (q8_0: quantised by the same rule), rows
@@ -109,12 +109,15 @@ def test_cache_append_is_bit_exact(kvd):
     assert n == 2 + 1 + 2 + 2 + 0
     if kvd == "bf16":
         assert np.array_equal(_bits_of(t["kv"]), kv_ref)
+    elif kvd == "fp8":
+        assert np.array_equal(t["kv"].cpu().numpy(), kv_ref)
+        assert np.array_equal(t["kv_scales"].cpu().numpy().view(np.uint32), sc_ref.view(np.uint32))
     else:
         assert np.array_equal(t["kv"].cpu().numpy(), kv_ref)
         assert np.array_equal(t["kv_scales"].view(torch.int16).cpu().numpy().view(np.uint16), sc_ref)
 
 
-@pytest.mark.parametrize("kvd", ["bf16", "q8_0"])
+@pytest.mark.parametrize("kvd", ["bf16", "q8_0", "fp8"])
 def test_append_then_decode(kvd):
     """A decode step after the append reads the appended rows: it matches the
     oracle's decode of the oracle-appended cache."""

@@ -52,6 +52,14 @@ SMALL = [
     ("h128_q8_many", 12, 1, 128, [1, 0, 31, 33, 64, 65, 130, 0, 2, 300, 97, 5000],
      "permuted", "q8_0", 0),
     ("h128_pair_q8", 2, 2, 128, [300, 4500], "permuted", "q8_0", 0),
+    # fp8 (E4M3, per-token scale): the 128-row converting kernel, also for
+    # few heads (padded rows), causal pairs, many segments, long segments
+    ("h128_fp8", 2, 1, 128, [700, 129], "permuted", "fp8", 0),
+    ("h16_fp8", 3, 1, 16, [64, 1, 999], "permuted", "fp8", 0),
+    ("h128_pair_fp8", 2, 2, 128, [300, 4500], "permuted", "fp8", 0),
+    ("h256_fp8", 2, 2, 128, [77, 1300], "sequential", "fp8", 0),
+    ("h128_fp8_many", 12, 1, 128, [1, 0, 31, 33, 64, 65, 130, 0, 2, 300, 97, 5000],
+     "permuted", "fp8", 0),
 ]
 
 
@@ -72,7 +80,7 @@ def test_tiny_config_all_rows():
     compare(out, lse, *oracle_rows(w), what="tiny", flat=True)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
 def test_full_size_config_all_rows(cfg):
     """Every row of each large workload, in the launch configuration the
     benchmark uses, against the fp64 oracle."""
@@ -143,7 +151,7 @@ def test_one_hot_probe_returns_the_exact_row(H):
 
 
 @pytest.mark.parametrize("H,kvd", [(16, "bf16"), (40, "bf16"), (128, "bf16"),
-                                   (40, "q8_0"), (128, "q8_0")])
+                                   (40, "q8_0"), (128, "q8_0"), (128, "fp8")])
 def test_unused_cache_slots_never_reach_the_result(H, kvd):
     """The slots of a sequence's last block past its length hold NaN (bf16
     rows; q8_0 scales): every kernel gives the oracle's result, which never
@@ -155,6 +163,9 @@ def test_unused_cache_slots_never_reach_the_result(H, kvd):
             blk = w.block_table[b, L // 64]
             if kvd == "bf16":
                 w.kv[blk, L % 64:, :] = 0x7FC0        # bf16 NaN
+            elif kvd == "fp8":
+                w.kv[blk, L % 64:, :] = 0x7F          # E4M3 NaN
+                w.kv_scales[blk, L % 64:] = np.nan
             else:
                 w.kv_scales[blk, L % 64:, :] = 0x7E00  # fp16 NaN
     ref = oracle_rows(w)
@@ -197,7 +208,8 @@ def test_invalid_block_id_in_a_later_id_window():
         assert np.all(np.isfinite(lse[[0, 2]]))
 
 
-@pytest.mark.parametrize("H,kvd", [(16, "bf16"), (40, "bf16"), (128, "bf16"), (16, "q8_0")])
+@pytest.mark.parametrize("H,kvd", [(16, "bf16"), (40, "bf16"), (128, "bf16"), (16, "q8_0"),
+                                   (128, "fp8")])
 def test_empty_pool_poisons_every_nonempty_sequence(H, kvd):
     """num_blocks = 0: no block id is valid, so every sequence with tokens is
     poisoned and nothing is read from the cache; empty sequences stay empty."""
@@ -206,8 +218,10 @@ def test_empty_pool_poisons_every_nonempty_sequence(H, kvd):
     t = device_inputs(w)
     out = torch.empty((w.B, 1, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, 1, H), dtype=torch.float32, device="cuda")
-    prob = mla.make_problem(t["q"], t["kv"], t["bt"], kv_dtype=mla.KV_BF16 if kvd == "bf16"
-                            else mla.KV_Q8_0, max_seqlen=w.max_seqlen, num_parts=2)
+    prob = mla.make_problem(t["q"], t["kv"], t["bt"],
+                            kv_dtype={"bf16": mla.KV_BF16, "q8_0": mla.KV_Q8_0,
+                                      "fp8": mla.KV_FP8}[kvd],
+                            max_seqlen=w.max_seqlen, num_parts=2)
     prob.num_blocks = 0
     ws = torch.empty(max(16, mla.workspace_size(prob)), dtype=torch.uint8, device="cuda")
     vp = ctypes.c_void_p
@@ -359,3 +373,38 @@ def test_absorbed_query_end_to_end():
     # bf16 rounding of q~ and of out bounds the gap
     assert np.abs(o_gpu - o_ref).max() <= 5e-2 * max(1.0, np.abs(o_ref).max())
     assert np.abs(lse - lse_ref).max() <= 5e-2
+
+
+def test_fp8_codes_convert_exactly():
+    """One-hot probe over an fp8 cache: the target token's latent columns hold
+    every finite E4M3 code; with scale 1 and probability 1 the output is each
+    code's value, which bf16 holds exactly, so it must match bit for bit."""
+    w = wl.make_workload("fp8codes", 2, 1, 128, [300, 70], seed=15, table="permuted",
+                         kv_dtype="fp8")
+    # every finite code but -0 (0x80): the value product accumulates from +0,
+    # and +0 + (-0) is +0
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], np.uint8)
+    w.kv[:, :, 512:] = 0
+    w.kv_scales[:] = 1.0
+    w.q[:] = 0
+    d = 9
+    w.q[..., 512 + d] = int(wl.f32_to_bf16_bits(np.float32([64.0]))[0])
+    expect, rows = {}, {}
+    for b, t in ((0, 123), (1, 69)):
+        blk, pos = w.block_table[b, t // 64], t % 64
+        row = np.resize(np.roll(codes, 37 * b), 512)
+        rows[b] = row
+        w.kv[blk, pos, :512] = row
+        w.kv[blk, pos, 512 + d] = 0x68          # E4M3 of 64: logit 64 * 64 = 4096
+        vals = np.array([oracle.fp8_value(int(c)) for c in row], np.float32)
+        expect[b] = wl.f32_to_bf16_bits(vals)
+    w.softmax_scale = 1.0
+    for parts in (1, 0):
+        out, lse, bits = run_gpu(w, num_parts=parts)
+        for b in (0, 1):
+            for h in range(128):
+                bad = np.nonzero(bits[b, 0, h] != expect[b])[0]
+                assert bad.size == 0, (b, h, parts, [(int(c), hex(int(rows[b][c])),
+                                                     hex(int(bits[b, 0, h, c])),
+                                                     hex(int(expect[b][c]))) for c in bad[:6]])
+        assert np.abs(lse[:, 0] - 4096.0).max() <= 1e-3

@@ -115,3 +115,62 @@ def test_cache_append_q8_0_is_the_quantiser_on_the_new_rows():
         blk = w.block_table[b, t // 64]
         assert np.array_equal(kv[blk, t % 64], q_ref[b])
         assert np.array_equal(sc[blk, t % 64], s_ref[b])
+
+
+# ------------------------------------------------------------ fp8 (E4M3)
+
+def test_fp8_decoder_fixed_points():
+    # OCP E4M3: bias 7, 3 fraction bits, subnormals below 2^-6, max 448, one NaN pattern
+    assert oracle.fp8_value(0x00) == 0.0
+    assert oracle.fp8_value(0x01) == 2.0 ** -9            # smallest subnormal
+    assert oracle.fp8_value(0x07) == 7 * 2.0 ** -9        # largest subnormal
+    assert oracle.fp8_value(0x08) == 2.0 ** -6            # smallest normal
+    assert oracle.fp8_value(0x38) == 1.0
+    assert oracle.fp8_value(0x39) == 1.125
+    assert oracle.fp8_value(0x7E) == 448.0
+    assert oracle.fp8_value(0xFE) == -448.0
+    assert oracle.fp8_value(0xC0) == -2.0
+    assert np.isnan(oracle.fp8_value(0x7F)) and np.isnan(oracle.fp8_value(0xFF))
+    vals = [oracle.fp8_value(b) for b in range(0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))   # codes 0..126 increase
+
+
+def test_fp8_encoder_round_trips_and_rounds_to_even():
+    for b in range(256):
+        if b in (0x7F, 0xFF):
+            continue
+        assert oracle.fp8_bits(oracle.fp8_value(b)) == b, hex(b)
+    assert oracle.fp8_bits(1.0625) == 0x38      # halfway 1 .. 1.125 -> even (1)
+    assert oracle.fp8_bits(1.1875) == 0x3A      # halfway 1.125 .. 1.25 -> even (1.25)
+    assert oracle.fp8_bits(2.0 ** -10) == 0x00  # halfway 0 .. 2^-9 -> even (0)
+    assert oracle.fp8_bits(3 * 2.0 ** -10) == 0x02
+    assert oracle.fp8_bits(460.0) == 0x7E       # saturates at 448
+    assert oracle.fp8_bits(1e30) == 0x7E and oracle.fp8_bits(-1e30) == 0xFE
+
+
+def test_fp8_writer_matches_the_generators_independent_writer_and_bounds():
+    x = wl.normal_f32(576 * 100, 11, 2).reshape(100, 576) * np.float32(3.0)
+    x[7] = 0.0
+    q, sc = oracle.quantize_fp8(x)
+    q2, sc2 = wl.quantize_fp8(x)
+    assert np.array_equal(q, q2) and np.array_equal(sc, sc2)
+    assert sc[7] == 0 and np.all(q[7] == 0)
+    dec = np.array([oracle.fp8_value(b) for b in range(256)])
+    xh = dec[q] * sc[:, None]
+    # relative spacing of E4M3 normals is 2^-3, so rounding moves a value by at
+    # most 2^-4 of itself; subnormals (below 2^-6 d) by at most 2^-10 d
+    bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sc[:, None]) + 1e-12
+    assert np.all(np.abs(x - xh) <= bound)
+    assert np.all(np.abs(dec[q]).max(1)[sc > 0] == 448.0)   # the largest value maps to +-448
+
+
+def test_cache_append_fp8_is_the_writer_on_the_new_rows():
+    w = wl.make_workload("app4", 2, 1, 16, [100, 64], seed=34, table="permuted", kv_dtype="fp8")
+    new = wl.normal_bf16(2 * 576, 34, 40).reshape(2, 1, 576)
+    kv, sc = w.kv.copy(), w.kv_scales.copy()
+    assert oracle.cache_append(new, w.block_table, w.seqlens, kv, sc) == 2
+    q_ref, s_ref = oracle.quantize_fp8(wl.bf16_bits_to_f32(new.reshape(2, 576)))
+    for b in range(2):
+        t = int(w.seqlens[b]) - 1
+        blk = w.block_table[b, t // 64]
+        assert np.array_equal(kv[blk, t % 64], q_ref[b]) and sc[blk, t % 64] == s_ref[b]

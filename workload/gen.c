@@ -212,3 +212,39 @@ void gen_quantize_q8_0(const float* x, int64_t rows, int32_t cols, int8_t* q, ui
     }
   }
 }
+
+/*
+ * fp8 cache writer: each row of 576 floats gets one fp32 scale
+ * d = max |x| / 448 and codes E4M3(x / d), OCP E4M3 (bias 7, 3 fraction bits,
+ * largest finite 448, no infinities) rounded to nearest even and saturated;
+ * d = 0 for a row of zeros (codes 0).
+ */
+static uint8_t f32_to_e4m3_rne(float f) {
+  const uint8_t sign = signbit(f) ? 0x80 : 0;
+  const float a = fabsf(f);
+  if (a < 0.015625f) return sign | (uint8_t)rintf(a * 512.0f);   /* steps of 2^-9 */
+  int ex;
+  frexpf(a, &ex);
+  int e = ex - 1;
+  float m = rintf(ldexpf(a, 3 - e));
+  if (m >= 16.0f) {
+    m = 8.0f;
+    ++e;
+  }
+  if (e > 8) return sign | 0x7E;
+  uint8_t code = (uint8_t)(((e + 7) << 3) | ((int)m - 8));
+  return sign | (code == 0x7F ? 0x7E : code);
+}
+
+void gen_quantize_fp8(const float* x, int64_t rows, int32_t cols, uint8_t* q, float* scale) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xs = x + r * cols;
+    float amax = 0.0f;
+    for (int32_t k = 0; k < cols; ++k)
+      if (fabsf(xs[k]) > amax) amax = fabsf(xs[k]);
+    const float d = amax / 448.0f;
+    scale[r] = d;
+    for (int32_t k = 0; k < cols; ++k) q[r * cols + k] = d > 0.0f ? f32_to_e4m3_rne(xs[k] / d) : 0;
+  }
+}
