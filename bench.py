@@ -38,7 +38,7 @@ WORKLOAD_CFG = 2                 # 64 x 128 heads x 4096 tokens, bf16 cache
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for rel in ("mla_latent_kv_10_amd/csrc/libmla.hip", "include/mla.h"):
+    for rel in ("mla_latent_kv_10_amd/csrc/libmla.hip", "include/mla.h"):   # the decode kernels
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -58,20 +58,63 @@ def parse():
                     help="replay the steps from HIP graphs instead of launching each from Python")
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
+                    help="run only a plain 1 GiB device copy (HBM counter calibration and "
+                         "measured copy bandwidth)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="run only the MFMA probe kernel (sustained dense bf16 MFMA rate; "
+                         "the MFMA-busy counter calibration)")
     return ap.parse_args()
 
 
 def copy_calibration():
+    """A plain 1 GiB device-to-device copy, three times: the reference the HBM
+    counters are scaled by, and the copy bandwidth the chip sustains."""
     import torch
     n = 1 << 30
     x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     y = torch.empty_like(x)
     torch.cuda.synchronize()
-    for _ in range(3):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    y.copy_(x)
+    e0.record()
+    for _ in range(2):
         y.copy_(x)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": n, "launches": 3}))
+    ms = e0.elapsed_time(e1) / 2
+    print(json.dumps({"copy_bytes": n, "launches": 3, "copy_ms": round(ms, 4),
+                      "read_plus_write_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
+
+
+def mfma_probe():
+    """Independent bf16 MFMAs on every SIMD (mla_latent_kv_10_amd/csrc/mla_probe.hip):
+    the dense bf16 MFMA rate the chip sustains, next to the 2.5 PFLOP/s peak."""
+    import ctypes
+    import torch
+    from mla_latent_kv_10_amd._build import PROBE_PATH
+    lib = ctypes.CDLL(PROBE_PATH)
+    lib.mla_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.mla_probe_mfma.restype = ctypes.c_int
+    wgs = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 20000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.mla_probe_mfma(ctypes.c_void_p(out.data_ptr()), wgs, 200, stream) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    assert lib.mla_probe_mfma(ctypes.c_void_p(out.data_ptr()), wgs, iters, stream) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = wgs * 4 * iters * 8 * 32768
+    tfs = flops / (ms * 1e-3) / 1e12
+    # each SIMD retires one 32x32x16 MFMA per 32 cycles at full rate
+    clock_ghz = wgs * 4 * iters * 8 * 32 / (ms * 1e-3) / wgs / 4 / 1e9
+    print(json.dumps({"probe": "mfma_bf16_32x32x16", "workgroups": wgs, "iters": iters,
+                      "ms": round(ms, 4), "tflops": round(tfs, 1),
+                      "frac_of_peak": round(tfs / BF16_MFMA_PEAK_TFLOPS, 4),
+                      "implied_clock_ghz": round(clock_ghz, 3)}))
 
 
 def _cpu_model() -> str:
@@ -162,6 +205,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.mfma_probe:
+        mfma_probe()
         return
     import torch
     import mla_latent_kv_10_amd as mla

@@ -3,6 +3,7 @@
   python bench_profile.py trace  <kernel-trace dir> <out.md> "<command that made it>"
   python bench_profile.py traffic <fetch dir> <write dir> <copy-fetch dir> <copy-write dir> \
                           <out.json> "<commands>"
+  python bench_profile.py mfma <pmc dir> <probe pmc dir> <out.json> "<commands>" [extra json]
 
 trace: per-kernel calls / average / total duration from a
   `rocprofv3 --kernel-trace --stats --output-format csv` run.
@@ -95,10 +96,69 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_json, command) -> 
     print(json.dumps(rec, indent=1))
 
 
+def _counters(d: str):
+    """-> {kernel: {counter: [(value, duration ns) per dispatch]}}"""
+    vals = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        vals[_short(r["Kernel_Name"])][r["Counter_Name"]].append((float(r["Counter_Value"]), dur))
+    return vals
+
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def mfma(pmc_dir, probe_dir, out_json, command, extra=None) -> None:
+    """Per kernel, medians over its dispatches:
+      mfma_busy_frac  (SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE) of the kernel
+                      divided by the same ratio of the probe, which keeps every
+                      matrix core busy: the share of the kernel's time the matrix
+                      cores are busy, at the kernel's own clock;
+      executed_bf16_flops  SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 (padding and
+                      idle-step MFMAs included);
+      executed_tflops  those flops over the dispatch's duration under the
+                      profiler, next to the probe's sustained rate."""
+    probe = _counters(probe_dir)
+    pk = [k for k in probe if "mfma_probe" in k]
+    if not pk:
+        raise RuntimeError(f"no probe kernel in {probe_dir}")
+    pc = probe[pk[0]]
+    # the probe's long dispatch (the short first one only warms it up)
+    i = max(range(len(pc["GRBM_GUI_ACTIVE"])), key=lambda j: pc["GRBM_GUI_ACTIVE"][j][0])
+    probe_ratio = pc["SQ_VALU_MFMA_BUSY_CYCLES"][i][0] / pc["GRBM_GUI_ACTIVE"][i][0]
+    probe_tflops = pc["SQ_INSTS_VALU_MFMA_MOPS_BF16"][i][0] * 512 / (pc["GRBM_GUI_ACTIVE"][i][1] * 1e-9) / 1e12
+    per = {}
+    for k, c in _counters(pmc_dir).items():
+        if not any(t in k for t in LIB_KERNELS) or not c.get("GRBM_GUI_ACTIVE"):
+            continue
+        n = len(c["GRBM_GUI_ACTIVE"])
+        ratios = [b[0] / g[0] for b, g in zip(c["SQ_VALU_MFMA_BUSY_CYCLES"], c["GRBM_GUI_ACTIVE"]) if g[0] > 0]
+        rec = {"dispatches": n, "mfma_busy_frac": round(_median(ratios) / probe_ratio, 4)}
+        if c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+            fl = [m[0] * 512 for m in c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]]
+            rates = [m[0] * 512 / (m[1] * 1e-9) / 1e12 for m in c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] if m[1] > 0]
+            rec["executed_bf16_flops"] = _median(fl)
+            rec["executed_tflops"] = round(_median(rates), 1)
+            rec["executed_frac_of_probe"] = round(_median(rates) / probe_tflops, 4)
+        rec["median_duration_us"] = round(_median([g[1] for g in c["GRBM_GUI_ACTIVE"]]) / 1e3, 2)
+        per[k] = rec
+    out = {"source_hash": bench.source_hash(), "command": command,
+           "probe_busy_ratio": round(probe_ratio, 3), "probe_tflops": round(probe_tflops, 1),
+           "per_kernel": per}
+    if extra:
+        out.update(json.loads(extra))
+    json.dump(out, open(out_json, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:8])
+    elif sys.argv[1] == "mfma":
+        mfma(*sys.argv[2:7])
     else:
         raise SystemExit(__doc__)
