@@ -1745,14 +1745,19 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
 // when a row's does, its owner publishes the factor and every wave rescales
 // that row's accumulators. The plan prefix and the epilogue's scratch live in
 // ring space that is idle at those times, which keeps LDS under 160 KiB.
-template <bool NT>
+template <bool NT, bool FP8>
 __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a) {
   constexpr int NW = 4;
   constexpr int NTH = 64 * NW;
   constexpr int MT = 128;
-  constexpr int NST = 4;                  // ring stages
-  constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile
+  constexpr int NST = FP8 ? 3 : 4;        // ring stages of bf16 tiles
+  constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile (bf16)
   constexpr int KPF = 3;                  // score operands in flight
+  // fp8: the E4M3 tiles (18 KiB + 128 B of scales) stream into two slots of
+  // their own; each is converted to bf16 into a ring stage one iteration
+  // before its scores, so the score and value steps are those of bf16
+  constexpr int RING = FP8 ? NST * kTileBytes + 2 * kFp8StageBytes : NST * kTileBytes;
+  static_assert(RING >= 4 * kTileBytes, "the query is transposed through 4 x 36 KiB of the ring");
   // LDS-DMA copy of one block (NT: non-temporal, when no other workgroup
   // reads the same tiles)
   auto copy = [](const void* src, uint32_t off, uint32_t dst) {
@@ -1762,15 +1767,19 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       dma16_sbase(src, off, dst);
   };
 
-  __shared__ __attribute__((aligned(1024))) uint8_t s_stage[NST][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_ring[RING];
   __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];   // P, B-operand layout
   __shared__ float s_alpha[MT];
   __shared__ __attribute__((aligned(16))) int s_flag[NW];
-  // aliases inside ring stage 3, which is idle before the first tile and
-  // after the last one
-  int* s_pre = reinterpret_cast<int*>(s_stage[3]);                  // [B+1]
-  int* s_misc = reinterpret_cast<int*>(s_stage[3] + 4 * (kMaxBatch + 8));
-  float* s_lsum = reinterpret_cast<float*>(s_stage[3]);            // epilogue
+  // fp8: per-token scales of the tiles in the bf16 stages
+  __shared__ __attribute__((aligned(16))) float s_tsc[FP8 ? NST : 1][kTile];
+  auto s_stage = [&](int i) { return s_ring + kTileBytes * i; };
+  auto s_f8 = [&](int j) { return s_ring + NST * kTileBytes + kFp8StageBytes * j; };
+  // aliases inside the last ring stage, which is idle before the first tile
+  // and after the last one
+  int* s_pre = reinterpret_cast<int*>(s_stage(NST - 1));                   // [B+1]
+  int* s_misc = reinterpret_cast<int*>(s_stage(NST - 1) + 4 * (kMaxBatch + 8));
+  float* s_lsum = reinterpret_cast<float*>(s_stage(NST - 1));             // epilogue
 
   const int tid = threadIdx.x, wave = uniform(tid >> 6);
 
@@ -1889,7 +1898,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       bad = bad || __any(inval && bt_base + lane < seg_len);
       bt_lane = inval ? 0 : bt_lane;
     };
-    auto tile_src = [&](int idx) {
+    // first cache row of tile idx (clamped to the segment's last tile)
+    auto tile_row0 = [&](int idx) {
       idx = min(idx, n_run - 1);
       int rel = (idx >> 1) - bt_base;
       if (rel >= 64) {
@@ -1900,15 +1910,90 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         check_ids();
       }
       const int64_t phys = uniform(__builtin_amdgcn_readlane(bt_lane, rel));
-      return a.kv + (phys * kBT + ((t_begin + idx) & 1) * kTile) * kRowBytes;
+      return phys * kBT + ((t_begin + idx) & 1) * kTile;
+    };
+    auto tile_src = [&](int idx) {
+      if constexpr (FP8)
+        return a.kv + tile_row0(idx) * kDK;
+      else
+        return a.kv + tile_row0(idx) * kRowBytes;
+    };
+    // fp8 copies of one tile: copy k = wave + 4 j (k < 18: bytes 1024 k .. of
+    // the tile's 32 contiguous rows; k = 18: its 128 bytes of scales, lanes
+    // past them re-reading the first bytes into the slot's padding). Waves
+    // 0..2 issue 5 copies per tile, wave 3 four.
+    auto copy8 = [&](const uint8_t* src, const uint8_t* ssrc, uint32_t dst, int j) {
+      const int kk = wave + 4 * j;
+      if (kk < 18) {
+        copy(src + 1024 * kk, 16 * lane, dst + 1024 * kk);
+      } else if (kk == 18) {
+        const int off = 16 * lane;
+        dma16_sbase(ssrc, off < 4 * kTile ? off : 0, dst + kFp8TileBytes);
+      }
     };
     auto issue = [&](int idx) {
-      const uint32_t dst = lds_addr_of(s_stage[idx % NST]) + 1024 * wave;
-      const uint8_t* src = tile_src(idx);
+      if constexpr (FP8) {
+        const int64_t row0 = tile_row0(idx);
+        const uint8_t* src = a.kv + row0 * kDK;
+        const uint8_t* ssrc = a.kv_scales + row0 * 4;
+        const uint32_t dst = lds_addr_of(s_f8(idx & 1));
 #pragma unroll
-      for (int j = 0; j < LPW; ++j) copy(src + 128 * j, doff, dst + 4096 * j);
+        for (int j = 0; j < 5; ++j) copy8(src, ssrc, dst, j);
+      } else {
+        const uint32_t dst = lds_addr_of(s_stage(idx % NST)) + 1024 * wave;
+        const uint8_t* src = tile_src(idx);
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) copy(src + 128 * j, doff, dst + 4096 * j);
+      }
     };
-    auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {
+    // copies this wave issues per tile
+    auto wait_tile = [&]() {
+      if constexpr (FP8) {
+        if (wave == 3)
+          wait_vmcnt<4>();
+        else
+          wait_vmcnt<5>();
+      } else {
+        wait_vmcnt<LPW>();
+      }
+    };
+    // fp8: convert tile idx (landed in its slot, visible to every wave) into
+    // the row-group layout of ring stage idx % NST, exactly (E4M3 values are
+    // bf16 values), and its per-token scales into s_tsc; tokens past the end
+    // of the sequence convert to zero with scale zero
+    auto convert8 = [&](int idx) {
+      const LDS_AS uint8_t* sl = (const LDS_AS uint8_t*)s_f8(idx & 1);
+      LDS_AS uint8_t* dstt = (LDS_AS uint8_t*)s_stage(idx % NST);
+      const int valid = L - (t_begin + idx) * kTile;
+      const int c0 = (lane >> 4) & 1;
+      const int rr = (lane & 3) | ((((lane >> 2) & 1) ^ c0) << 2);
+      const int cc = c0 | ((((lane >> 3) ^ wave) & 1) << 1) | (((lane >> 5) & 1) << 2);
+      const int t = 8 * wave + rr;
+      const uint32_t keep = t < valid ? 0xffffffffu : 0u;
+      const LDS_AS uint8_t* srow = sl + kDK * t + 8 * cc;
+#pragma unroll
+      for (int i0 = 0; i0 < 9; i0 += 3) {
+        uint64_t raw[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) raw[i] = *reinterpret_cast<const LDS_AS uint64_t*>(srow + 64 * (i0 + i));
+#pragma unroll
+        for (int i1 = 0; i1 < 3; ++i1) {
+        const int i = i0 + i1;
+        const uint32_t w0 = (uint32_t)raw[i1] & keep, w1 = (uint32_t)(raw[i1] >> 32) & keep;
+        u32x4 wv;
+        wv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+        wv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+        wv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+        wv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+        *reinterpret_cast<LDS_AS u32x4*>(dstt + 16 * (tid + NTH * i)) = wv;
+        }
+      }
+      if (tid < kTile) {
+        const float sc = reinterpret_cast<const LDS_AS float*>(sl + kFp8TileBytes)[tid];
+        s_tsc[idx % NST][tid] = tid < valid ? sc : 0.f;
+      }
+    };
+    auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {   // bf16 only
       for (int u = tid; u < kTile * 72; u += NTH) {
         const int c0 = (u >> 4) & 1;
         const int token = 8 * ((u >> 6) & 3) + ((u & 3) | ((((u >> 2) & 1) ^ c0) << 2));
@@ -1947,7 +2032,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         }
       }
       {
-        LDS_AS uint8_t* stq = (LDS_AS uint8_t*)s_stage[wave];
+        LDS_AS uint8_t* stq = (LDS_AS uint8_t*)s_stage(wave);
         int t = 0, c = lane;
 #pragma unroll
         for (int j = 0; j < 36; ++j) {
@@ -1966,10 +2051,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       lds_barrier();   // every wave holds its query rows; the ring is free
       issue(0);
       issue(1);
-      // "tile -1" (value product before the first tile) reads stage 3 with
-      // P = 0: both are zero-filled so that it adds exact zeros
+      // "tile -1" (value product before the first tile) reads the last
+      // stage with P = 0: both are zero-filled so that it adds exact zeros
       for (int u = tid; u < kTileBytes / 16; u += NTH)
-        *reinterpret_cast<LDS_AS f32x4*>((LDS_AS uint8_t*)s_stage[3] + 16 * u) =
+        *reinterpret_cast<LDS_AS f32x4*>((LDS_AS uint8_t*)s_stage(NST - 1) + 16 * u) =
             f32x4{0.f, 0.f, 0.f, 0.f};
       s_p[wave][0][lane] = u32x4{0u, 0u, 0u, 0u};
       s_p[wave][1][lane] = u32x4{0u, 0u, 0u, 0u};
@@ -1985,11 +2070,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     // latency is not exposed at the start of the score chain.
     bf16x8 kf[KPF];
     auto rd_at = [&](int t, int k) {
-      return lds_read_b128((const LDS_AS uint8_t*)s_stage[t % NST] + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0));
+      return lds_read_b128((const LDS_AS uint8_t*)s_stage(t % NST) + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0));
     };
     if (n_run > 0) {
-      wait_vmcnt<LPW>();          // tile 0 landed; tile 1 may be in flight
-      lds_barrier();              // ... in every wave's part; stage 3 and P zeroed
+      wait_tile();                // tile 0 landed; tile 1 may be in flight
+      lds_barrier();              // ... in every wave's part; the last stage and P zeroed
+      if constexpr (FP8) {
+        convert8(0);
+        lds_barrier();
+      }
 #pragma unroll
       for (int j2 = 0; j2 < KPF; ++j2) kf[j2] = rd_at(0, j2);
     }
@@ -1997,15 +2086,20 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       // P(it-1), alpha and flags of every wave are visible: their writes were
       // issued before the KPF score reads now in flight, and LDS operations
       // of a wave complete in order
-      if (it > 0) asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KPF) : "memory");
+      // (fp8: the barrier after the conversion at the end of the previous
+      // iteration already made them visible)
+      if (!FP8 && it > 0) asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KPF) : "memory");
       const bool has_s = it < n_run;
-      const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage[it % NST];
-      const LDS_AS uint8_t* sp = (const LDS_AS uint8_t*)s_stage[(it + NST - 1) % NST];
+      const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage(it % NST);
+      const LDS_AS uint8_t* sp = (const LDS_AS uint8_t*)s_stage((it + NST - 1) % NST);
       const int t0 = (t_begin + it) * kTile;
       // rescale requests of tile it-1, read now and acted on after phase A
       const u32x4 flg = *reinterpret_cast<const u32x4*>(s_flag);
-      const uint8_t* nsrc = tile_src(it + 2);
-      const uint32_t ndst = lds_addr_of(s_stage[(it + 2) % NST]) + 1024 * wave;
+      const int64_t nrow0 = tile_row0(it + 2);
+      const uint8_t* nsrc = a.kv + nrow0 * (FP8 ? kDK : kRowBytes);
+      const uint8_t* nssrc = a.kv_scales + nrow0 * 4;   // fp8 only
+      const uint32_t ndst = FP8 ? lds_addr_of(s_f8((it + 2) & 1))
+                                : lds_addr_of(s_stage((it + 2) % NST)) + 1024 * wave;
 
       // value step q = (kk, cb, rb) with kk = q / 16, cb = (q / 4) % 4,
       // rb = q % 4: O^T block (rb, cb) += V^T (column block cb, token half kk)
@@ -2046,7 +2140,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         if constexpr (k >= 24 && k < 28) pf[k - 24] = __builtin_bit_cast(bf16x8, s_p[k - 24][0][lane]);
         if constexpr (k == 29) va[0] = vread(0, 0);
         if constexpr (k == 31) va[1] = vread(0, 1);
-        if constexpr ((k & 3) == 1) copy(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
+        if constexpr (FP8) {
+          if constexpr ((k & 7) == 1) copy8(nsrc, nssrc, ndst, k >> 3);
+        } else {
+          if constexpr ((k & 3) == 1) copy(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
+        }
         __builtin_amdgcn_sched_barrier(0);
       });
       mfma_vgpr_drain(s);
@@ -2078,6 +2176,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       // more than the threshold.
       const float c = a.scale_mag_log2;
       float x[16];
+      f32x4 tsc4[4];   // fp8: per-token scales of the lane's tokens 8 g + 4 hi + (0..3)
       float m01 = 0.f, m02 = 0.f, m03 = 0.f, m04 = 0.f, m05 = 0.f, m06 = 0.f, lmax = 0.f, rmax = 0.f;
       float m_new = m_run, alpha = 1.f, neg_m = 0.f, psum = 0.f, pprev = 0.f;
       bool raise = false;
@@ -2086,8 +2185,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       auto sm_step = [&](auto jc) {
         constexpr int st_ = decltype(jc)::value;
         if constexpr (st_ < 4) {
+          if constexpr (FP8) {
+            // tokens 8 st_ + 4 hi + (0..3); a token's score is scale * <q, row>
+            const f32x4 v4 = *(const LDS_AS f32x4*)(&s_tsc[it % NST][8 * st_ + 4 * hi]);
 #pragma unroll
-          for (int i2 = 4 * st_; i2 < 4 * st_ + 4; ++i2) x[i2] = s[i2] * c;
+            for (int r4 = 0; r4 < 4; ++r4) x[4 * st_ + r4] = s[4 * st_ + r4] * (c * v4[r4]);
+          } else {
+#pragma unroll
+            for (int i2 = 4 * st_; i2 < 4 * st_ + 4; ++i2) x[i2] = s[i2] * c;
+          }
           if constexpr (st_ == 3) {
             if (masked) {
 #pragma unroll
@@ -2114,6 +2220,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
           m_new = raise ? rmax + kRefHeadroom : m_run;
           asm volatile("" : "+v"(m_new));
         } else if constexpr (st_ == 10) {
+          if constexpr (FP8) tsc4[0] = *(const LDS_AS f32x4*)(&s_tsc[it % NST][4 * hi]);
           alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
           asm volatile("" : "+v"(alpha));
         } else if constexpr (st_ == 11) {
@@ -2121,10 +2228,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
           asm volatile("" : "+v"(neg_m));
         } else {
           constexpr int j2 = st_ - 12;
+          if constexpr (FP8 && (j2 & 3) == 2 && j2 + 2 < 16)   // scales of the next 4 tokens
+            tsc4[(j2 + 2) >> 2] = *(const LDS_AS f32x4*)(&s_tsc[it % NST][8 * ((j2 + 2) >> 2) + 4 * hi]);
           const float p = __builtin_amdgcn_exp2f(x[j2] + neg_m);
           psum += p;
           if constexpr (j2 & 1) {
-            pw[j2 >> 1] = pack_bf16x2(pprev, p);
+            // fp8: V is scale * value, the scale rides on the probability
+            if constexpr (FP8)
+              pw[j2 >> 1] = pack_bf16x2(pprev * tsc4[j2 >> 2][(j2 - 1) & 3], p * tsc4[j2 >> 2][j2 & 3]);
+            else
+              pw[j2 >> 1] = pack_bf16x2(pprev, p);
             asm volatile("" : "+v"(psum), "+v"(pw[j2 >> 1]));
           } else {
             pprev = p;
@@ -2147,9 +2260,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         l_run = l_run * alpha + psum;
         m_run = m_new;
         // last tile: zero rows past the end; its V serves the next iteration
-        if (L - t0 < kTile) clear_tail((LDS_AS uint8_t*)s_stage[it % NST], L - t0);
+        // (fp8: the conversion zeroed them)
+        if (!FP8 && L - t0 < kTile) clear_tail((LDS_AS uint8_t*)s_stage(it % NST), L - t0);
       }
-      wait_vmcnt<LPW>();          // tile it+1 landed (this wave's part); tile it+2 in flight
+      wait_tile();                // tile it+1 landed (this wave's part); tile it+2 in flight
       lds_barrier();              // every wave has read P(it-1) and tile it-1; tile it+1 visible
       if (has_s) {
         s_p[wave][0][lane] = u32x4{pw[0], pw[1], pw[2], pw[3]};
@@ -2157,6 +2271,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         if (raise_any && hi == 0) s_alpha[32 * wave + l32] = alpha;
       }
       if (lane == 0) s_flag[wave] = raise_any ? 1 : 0;
+      if constexpr (FP8) {
+        // tile it+1 into its bf16 stage (it held tile it-2, whose value
+        // product ran in the previous iteration), then make it and P visible
+        if (it + 1 < n_run) convert8(it + 1);
+        lds_barrier();
+      }
       asm volatile("" ::: "memory");   // the writes above are issued before the reads below
 #pragma unroll
       for (int j2 = 0; j2 < KPF; ++j2) kf[j2] = rd_at(it + 1, j2);
@@ -2174,7 +2294,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     constexpr int kStageRow = 272;
     uint16_t* dst_base = split ? a.part_o + ((int64_t)slot * a.M) * kDL
                                : a.out + ((int64_t)b * a.M) * kDL;
-    LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_stage[0] + wave * (64 * kStageRow);
+    LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_stage(0) + wave * (64 * kStageRow);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -3140,11 +3260,12 @@ hipError_t launch_decode(const DecodeParams& dp, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool FP8>
 hipError_t launch_pipe(const DecodeParams& dp, int grid, hipStream_t stream) {
   if (dp.m_tiles == 1)
-    hipLaunchKernelGGL(mla_decode_pipe_kernel<true>, dim3(grid), dim3(256), 0, stream, dp);
+    hipLaunchKernelGGL((mla_decode_pipe_kernel<true, FP8>), dim3(grid), dim3(256), 0, stream, dp);
   else
-    hipLaunchKernelGGL(mla_decode_pipe_kernel<false>, dim3(grid), dim3(256), 0, stream, dp);
+    hipLaunchKernelGGL((mla_decode_pipe_kernel<false, FP8>), dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -3345,7 +3466,7 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
         switch (pl.HG) {
           case 1: e = launch_rows<1>(dp, grid, stream); break;
           case 2: e = launch_rows<2>(dp, grid, stream); break;
-          case 4: e = launch_pipe(dp, grid, stream); break;
+          case 4: e = launch_pipe<false>(dp, grid, stream); break;
           default: return fail(MLA_ERR_UNSUPPORTED, "no kernel for this row tile");
         }
       }
@@ -3362,7 +3483,7 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
       break;
     case MLA_KV_FP8:
       if (!pl.q8w) return fail(MLA_ERR_UNSUPPORTED, "no fp8 kernel for this row tile");
-      e = launch_cvt<MLA_KV_FP8>(dp, grid, stream);
+      e = launch_pipe<true>(dp, grid, stream);
       break;
     default:
       return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);
