@@ -68,6 +68,19 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Eight OCP E4M3 codes (byte i = element i) to bf16, exactly: every finite
+// E4M3 value, subnormals included, is a bf16 value.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true));
+  return __builtin_bit_cast(bf16x8, r);
+}
 
 #define LDS_AS __attribute__((address_space(3)))
 // Read-only for the whole kernel: loads through this address space with a
@@ -160,6 +173,14 @@ __device__ __forceinline__ bf16x8 vt_fragment(const LDS_AS uint8_t* p0, const LD
   typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
   i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// The same operand from an fp8 (E4M3) tile, as codes: one transposing
+// 64-bit read (in each 16-lane group, lane 2s+h points at columns 8h..8h+7
+// of token s and lane i receives column i of tokens s = 0..7).
+__device__ __forceinline__ u32x2 vt_codes8(const LDS_AS uint8_t* p) {
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(p));
+  return u32x2{(uint32_t)v[0], (uint32_t)v[1]};
 }
 
 // LDS tile layout of the 32/64-row and q8_0 kernels (bf16, 32 tokens x 576
@@ -1715,6 +1736,19 @@ __device__ __forceinline__ void mfma_score(f32x16& acc, const bf16x8& a, const b
   else
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+// The same with an A operand that VALU code has just written (an fp8 tile
+// converted in registers): a VALU write of a VGPR that an MFMA then reads as
+// SrcA/B needs 2 wait states, which the compiler does not insert ahead of
+// an asm statement. `other` (the operand being converted for the next step)
+// is held live across the MFMA, so that the conversions never write the
+// registers an MFMA in flight is reading.
+__device__ __forceinline__ void mfma_score_valu_a(f32x16& acc, const bf16x8& a, const bf16x8& b, bool first,
+                                                  const bf16x8& other) {
+  if (first)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b), "v"(other));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b), "v"(other));
+}
 // max of three floats in one v_max3_f32; the asm also pins the result where
 // it stands (no sinking into later conditional code).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -1750,14 +1784,19 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   constexpr int NW = 4;
   constexpr int NTH = 64 * NW;
   constexpr int MT = 128;
-  constexpr int NST = FP8 ? 3 : 4;        // ring stages of bf16 tiles
+  constexpr int NST = 4;                  // ring stages
   constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile (bf16)
-  constexpr int KPF = 3;                  // score operands in flight
-  // fp8: the E4M3 tiles (18 KiB + 128 B of scales) stream into two slots of
-  // their own; each is converted to bf16 into a ring stage one iteration
-  // before its scores, so the score and value steps are those of bf16
-  constexpr int RING = FP8 ? NST * kTileBytes + 2 * kFp8StageBytes : NST * kTileBytes;
-  static_assert(RING >= 4 * kTileBytes, "the query is transposed through 4 x 36 KiB of the ring");
+  // score operands in flight (fp8: each is converted one step before its
+  // MFMA, so one more is read ahead)
+  constexpr int KPF = FP8 ? 4 : 3;
+  // fp8: the E4M3 tiles (18 KiB of codes + 128 B of scales) stream into
+  // 19 KiB stages and are read as MFMA operands directly, converted to bf16
+  // in registers (exact: every E4M3 value is a bf16 value), which halves the
+  // LDS traffic of both products
+  constexpr int STB = FP8 ? kFp8StageBytes : kTileBytes;   // bytes per ring stage
+  constexpr int RING = 4 * kTileBytes;    // the query is transposed through 4 x 36 KiB
+  static_assert(NST * STB <= RING, "ring stages");
+  using KOp = std::conditional_t<FP8, u32x2, bf16x8>;       // score operand as read
   // LDS-DMA copy of one block (NT: non-temporal, when no other workgroup
   // reads the same tiles)
   auto copy = [](const void* src, uint32_t off, uint32_t dst) {
@@ -1771,15 +1810,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   __shared__ __attribute__((aligned(16))) u32x4 s_p[NW][2][64];   // P, B-operand layout
   __shared__ float s_alpha[MT];
   __shared__ __attribute__((aligned(16))) int s_flag[NW];
-  // fp8: per-token scales of the tiles in the bf16 stages
-  __shared__ __attribute__((aligned(16))) float s_tsc[FP8 ? NST : 1][kTile];
-  auto s_stage = [&](int i) { return s_ring + kTileBytes * i; };
-  auto s_f8 = [&](int j) { return s_ring + NST * kTileBytes + kFp8StageBytes * j; };
-  // aliases inside the last ring stage, which is idle before the first tile
-  // and after the last one
-  int* s_pre = reinterpret_cast<int*>(s_stage(NST - 1));                   // [B+1]
-  int* s_misc = reinterpret_cast<int*>(s_stage(NST - 1) + 4 * (kMaxBatch + 8));
-  float* s_lsum = reinterpret_cast<float*>(s_stage(NST - 1));             // epilogue
+  auto s_stage = [&](int i) { return s_ring + STB * i; };
+  // aliases in the ring's last 36 KiB, which is idle before the first tile
+  // and after the last one (fp8: never reached by the stages)
+  uint8_t* const s_idle = s_ring + 3 * kTileBytes;
+  int* s_pre = reinterpret_cast<int*>(s_idle);                    // [B+1]
+  int* s_misc = reinterpret_cast<int*>(s_idle + 4 * (kMaxBatch + 8));
+  float* s_lsum = reinterpret_cast<float*>(s_idle);               // epilogue
 
   const int tid = threadIdx.x, wave = uniform(tid >> 6);
 
@@ -1853,6 +1890,23 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     const int dr = (lane & 3) | ((((lane >> 2) & 1) ^ dc0) << 2);
     const int dcc = dc0 | ((((lane >> 3) ^ wave) & 1) << 1) | (((lane >> 5) & 1) << 2);
     const uint32_t doff = (uint32_t)((8 * wave + dr) * kRowBytes + 16 * dcc);
+    // fp8 stage: chunk k (16 codes, columns 16k..16k+15) of the 32 tokens
+    // fills bytes 512 k .. 512 k + 511, token t in slot t ^ 4 (k & 1). A
+    // score operand (8 codes of one token) is then one 8-byte read out of a
+    // 512-byte run; the XOR puts the two chunks of a value read (transposing
+    // read of 8 tokens x 16 columns per 16-lane group) in opposite halves of
+    // the bank window. LDS-DMA copy m fills chunks 2m, 2m+1: lane l takes
+    // chunk 2m + (l >> 5) of token (l & 31) ^ 4 (l >> 5).
+    const uint32_t doff8 = (uint32_t)(kDK * ((lane & 31) ^ (4 * hi)) + 16 * hi);
+    const int kofs8_0 = 16 * l32 + 8 * hi;
+    const int kofs8_1 = 16 * (l32 ^ 4) + 8 * hi;
+    // value read: group g16 covers columns 16 (g16 & 1) + 0..15 of the column
+    // block (chunk 8 w + 2 cb + (g16 & 1)); lane i16 = 2 s + h points at
+    // codes 8h..8h+7 of the chunk for token 4 vh + (s & 3) + 8 (s >> 2) and
+    // receives column i16 of those 8 tokens
+    const int vs8 = i16 >> 1;
+    const int vofs8 = 512 * (8 * wave + (g16 & 1)) +
+                      16 * ((4 * vh + (vs8 & 3) + 8 * (vs8 >> 2)) ^ (4 * (g16 & 1))) + 8 * (i16 & 1);
 
     const int L = uniform(clamp_len(((const CONST_AS int32_t*)a.seqlens)[b], a.max_blocks));
     const int pre_e = pre_b + (L + kBT - 1) / kBT;
@@ -1918,15 +1972,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       else
         return a.kv + tile_row0(idx) * kRowBytes;
     };
-    // fp8 copies of one tile: copy k = wave + 4 j (k < 18: bytes 1024 k .. of
-    // the tile's 32 contiguous rows; k = 18: its 128 bytes of scales, lanes
-    // past them re-reading the first bytes into the slot's padding). Waves
+    // fp8 copy j of this wave: copy m = wave + 4 j (m < 18: chunks 2m, 2m+1
+    // of the tile's 32 rows, 32 bytes of each, the lines shared by copies
+    // m..m+3 read from cache; m = 18: the tile's 128 bytes of scales, lanes
+    // past them re-reading the first bytes into the stage's padding). Waves
     // 0..2 issue 5 copies per tile, wave 3 four.
     auto copy8 = [&](const uint8_t* src, const uint8_t* ssrc, uint32_t dst, int j) {
-      const int kk = wave + 4 * j;
-      if (kk < 18) {
-        copy(src + 1024 * kk, 16 * lane, dst + 1024 * kk);
-      } else if (kk == 18) {
+      const int m = wave + 4 * j;
+      if (m < 18) {
+        dma16_sbase(src + 32 * m, doff8, dst + 1024 * m);
+      } else if (m == 18) {
         const int off = 16 * lane;
         dma16_sbase(ssrc, off < 4 * kTile ? off : 0, dst + kFp8TileBytes);
       }
@@ -1936,7 +1991,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         const int64_t row0 = tile_row0(idx);
         const uint8_t* src = a.kv + row0 * kDK;
         const uint8_t* ssrc = a.kv_scales + row0 * 4;
-        const uint32_t dst = lds_addr_of(s_f8(idx & 1));
+        const uint32_t dst = lds_addr_of(s_stage(idx % NST));
 #pragma unroll
         for (int j = 0; j < 5; ++j) copy8(src, ssrc, dst, j);
       } else {
@@ -1957,41 +2012,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         wait_vmcnt<LPW>();
       }
     };
-    // fp8: convert tile idx (landed in its slot, visible to every wave) into
-    // the row-group layout of ring stage idx % NST, exactly (E4M3 values are
-    // bf16 values), and its per-token scales into s_tsc; tokens past the end
-    // of the sequence convert to zero with scale zero
-    auto convert8 = [&](int idx) {
-      const LDS_AS uint8_t* sl = (const LDS_AS uint8_t*)s_f8(idx & 1);
-      LDS_AS uint8_t* dstt = (LDS_AS uint8_t*)s_stage(idx % NST);
-      const int valid = L - (t_begin + idx) * kTile;
-      const int c0 = (lane >> 4) & 1;
-      const int rr = (lane & 3) | ((((lane >> 2) & 1) ^ c0) << 2);
-      const int cc = c0 | ((((lane >> 3) ^ wave) & 1) << 1) | (((lane >> 5) & 1) << 2);
-      const int t = 8 * wave + rr;
-      const uint32_t keep = t < valid ? 0xffffffffu : 0u;
-      const LDS_AS uint8_t* srow = sl + kDK * t + 8 * cc;
-#pragma unroll
-      for (int i0 = 0; i0 < 9; i0 += 3) {
-        uint64_t raw[3];
-#pragma unroll
-        for (int i = 0; i < 3; ++i) raw[i] = *reinterpret_cast<const LDS_AS uint64_t*>(srow + 64 * (i0 + i));
-#pragma unroll
-        for (int i1 = 0; i1 < 3; ++i1) {
-        const int i = i0 + i1;
-        const uint32_t w0 = (uint32_t)raw[i1] & keep, w1 = (uint32_t)(raw[i1] >> 32) & keep;
-        u32x4 wv;
-        wv[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
-        wv[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
-        wv[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
-        wv[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
-        *reinterpret_cast<LDS_AS u32x4*>(dstt + 16 * (tid + NTH * i)) = wv;
-        }
+    // fp8, last tile: codes and scales of the tokens past the end are zeroed
+    // (they may hold anything, NaN included; the value product multiplies
+    // them by zero probabilities)
+    auto clear_tail8 = [&](LDS_AS uint8_t* st, int valid) {
+      for (int u = tid; u < 36 * kTile; u += NTH) {
+        const int token = (u & 31) ^ (4 * ((u >> 5) & 1));
+        if (token >= valid) *reinterpret_cast<LDS_AS u32x4*>(st + 16 * u) = u32x4{0u, 0u, 0u, 0u};
       }
-      if (tid < kTile) {
-        const float sc = reinterpret_cast<const LDS_AS float*>(sl + kFp8TileBytes)[tid];
-        s_tsc[idx % NST][tid] = tid < valid ? sc : 0.f;
-      }
+      if (tid < kTile && tid >= valid) reinterpret_cast<LDS_AS float*>(st + kFp8TileBytes)[tid] = 0.f;
     };
     auto clear_tail = [&](LDS_AS uint8_t* st, int valid) {   // bf16 only
       for (int u = tid; u < kTile * 72; u += NTH) {
@@ -2032,7 +2061,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         }
       }
       {
-        LDS_AS uint8_t* stq = (LDS_AS uint8_t*)s_stage(wave);
+        LDS_AS uint8_t* stq = (LDS_AS uint8_t*)(s_ring + kTileBytes * wave);
         int t = 0, c = lane;
 #pragma unroll
         for (int j = 0; j < 36; ++j) {
@@ -2053,7 +2082,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       issue(1);
       // "tile -1" (value product before the first tile) reads the last
       // stage with P = 0: both are zero-filled so that it adds exact zeros
-      for (int u = tid; u < kTileBytes / 16; u += NTH)
+      for (int u = tid; u < STB / 16; u += NTH)
         *reinterpret_cast<LDS_AS f32x4*>((LDS_AS uint8_t*)s_stage(NST - 1) + 16 * u) =
             f32x4{0.f, 0.f, 0.f, 0.f};
       s_p[wave][0][lane] = u32x4{0u, 0u, 0u, 0u};
@@ -2068,16 +2097,23 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     // The first score operands of tile it are read at the end of iteration
     // it-1, before the barrier that publishes P(it-1), so that their LDS
     // latency is not exposed at the start of the score chain.
-    bf16x8 kf[KPF];
+    KOp kf[KPF];
     auto rd_at = [&](int t, int k) {
-      return lds_read_b128((const LDS_AS uint8_t*)s_stage(t % NST) + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0));
+      const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage(t % NST);
+      if constexpr (FP8)
+        return *reinterpret_cast<const LDS_AS u32x2*>(st + 512 * k + ((k & 1) ? kofs8_1 : kofs8_0));
+      else
+        return lds_read_b128(st + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0));
     };
     if (n_run > 0) {
       wait_tile();                // tile 0 landed; tile 1 may be in flight
       lds_barrier();              // ... in every wave's part; the last stage and P zeroed
       if constexpr (FP8) {
-        convert8(0);
-        lds_barrier();
+        const int v0 = L - t_begin * kTile;
+        if (v0 < kTile) {
+          clear_tail8((LDS_AS uint8_t*)s_stage(0), v0);
+          lds_barrier();
+        }
       }
 #pragma unroll
       for (int j2 = 0; j2 < KPF; ++j2) kf[j2] = rd_at(0, j2);
@@ -2086,9 +2122,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       // P(it-1), alpha and flags of every wave are visible: their writes were
       // issued before the KPF score reads now in flight, and LDS operations
       // of a wave complete in order
-      // (fp8: the barrier after the conversion at the end of the previous
-      // iteration already made them visible)
-      if (!FP8 && it > 0) asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KPF) : "memory");
+      if (it > 0) asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KPF) : "memory");
       const bool has_s = it < n_run;
       const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage(it % NST);
       const LDS_AS uint8_t* sp = (const LDS_AS uint8_t*)s_stage((it + NST - 1) % NST);
@@ -2098,26 +2132,45 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       const int64_t nrow0 = tile_row0(it + 2);
       const uint8_t* nsrc = a.kv + nrow0 * (FP8 ? kDK : kRowBytes);
       const uint8_t* nssrc = a.kv_scales + nrow0 * 4;   // fp8 only
-      const uint32_t ndst = FP8 ? lds_addr_of(s_f8((it + 2) & 1))
-                                : lds_addr_of(s_stage((it + 2) % NST)) + 1024 * wave;
+      const uint32_t ndst = lds_addr_of(s_stage((it + 2) % NST)) + (FP8 ? 0 : 1024 * wave);
 
       // value step q = (kk, cb, rb) with kk = q / 16, cb = (q / 4) % 4,
       // rb = q % 4: O^T block (rb, cb) += V^T (column block cb, token half kk)
       // x P^T (rows of wave rb, token half kk)
       f32x16 s;
-      auto rd = [&](int k) { return lds_read_b128(st + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0)); };
-      auto vread = [&](int kk, int cb) {
-        const int o = 4096 * (cb >> 1) + 512 * (cb & 1) + 2048 * kk;
-        return vt_fragment(sp + vofs0 + o, sp + vofs1 + o);
+      auto rd = [&](int k) -> KOp {
+        if constexpr (FP8)
+          return *reinterpret_cast<const LDS_AS u32x2*>(st + 512 * k + ((k & 1) ? kofs8_1 : kofs8_0));
+        else
+          return lds_read_b128(st + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0));
       };
-      bf16x8 pf[4], va[2];   // value operands, loaded in phase A's last third
+      auto vread = [&](int kk, int cb) {
+        if constexpr (FP8) {
+          return vt_codes8(sp + vofs8 + 1024 * cb + 256 * kk);
+        } else {
+          const int o = 4096 * (cb >> 1) + 512 * (cb & 1) + 2048 * kk;
+          return vt_fragment(sp + vofs0 + o, sp + vofs1 + o);
+        }
+      };
+      // value operands, loaded in phase A's last third (fp8: va holds codes;
+      // vb the current column block's operand, converted at the end of the
+      // previous block)
+      using VOp = std::conditional_t<FP8, u32x2, bf16x8>;
+      bf16x8 pf[4], vb;
+      VOp va[2];
       auto pv_step = [&](auto qc) {
         constexpr int q = decltype(qc)::value, cb = (q >> 2) & 3, rb = q & 3;
-        o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb & 1], pf[rb], o[4 * rb + cb], 0, 0, 0);
+        if constexpr (FP8)
+          o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pf[rb], o[4 * rb + cb], 0, 0, 0);
+        else
+          o[4 * rb + cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cb & 1], pf[rb], o[4 * rb + cb], 0, 0, 0);
         if constexpr (rb == 3 && q + 5 < 32) {
           // next V^T operand two column blocks ahead (token half changes at 16)
           constexpr int nq = q + 5;
           va[cb & 1] = vread(nq >> 4, (nq >> 2) & 3);
+        }
+        if constexpr (FP8) {
+          if constexpr (rb == 3 && q + 1 < 32) vb = fp8x8_to_bf16(va[(cb + 1) & 1]);
         }
         // P^T of the second token half: each row block right after its last
         // use in the first half, four steps ahead of its first use
@@ -2133,13 +2186,28 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       // ---- phase A: the dependent score chain of tile it (36 MFMAs) and the
       // copy of tile it+2; in its last third the first value operands of
       // tile it-1 are read
+      // fp8: converted score operands, alternating: step k reads kb[k & 1]
+      // while the operand of step k+1 is converted into kb[(k + 1) & 1]
+      bf16x8 kb[2];
+      if constexpr (FP8) {
+        kb[0] = fp8x8_to_bf16(kf[0]);
+        kb[1] = kb[0];
+      }
       unroll<36>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
-        mfma_score(s, kf[k % KPF], qf[k], k == 0);
+        if constexpr (FP8) {
+          mfma_score_valu_a(s, kb[k & 1], qf[k], k == 0, kb[(k + 1) & 1]);
+          if constexpr (k + 1 < 36) kb[(k + 1) & 1] = fp8x8_to_bf16(kf[(k + 1) % KPF]);
+        } else {
+          mfma_score(s, kf[k % KPF], qf[k], k == 0);
+        }
         if constexpr (k + KPF < 36) kf[k % KPF] = rd(k + KPF);
         if constexpr (k >= 24 && k < 28) pf[k - 24] = __builtin_bit_cast(bf16x8, s_p[k - 24][0][lane]);
         if constexpr (k == 29) va[0] = vread(0, 0);
         if constexpr (k == 31) va[1] = vread(0, 1);
+        if constexpr (FP8) {
+          if constexpr (k == 34) vb = fp8x8_to_bf16(va[0]);
+        }
         if constexpr (FP8) {
           if constexpr ((k & 7) == 1) copy8(nsrc, nssrc, ndst, k >> 3);
         } else {
@@ -2177,6 +2245,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       const float c = a.scale_mag_log2;
       float x[16];
       f32x4 tsc4[4];   // fp8: per-token scales of the lane's tokens 8 g + 4 hi + (0..3)
+      const LDS_AS float* tscp = reinterpret_cast<const LDS_AS float*>(st + kFp8TileBytes) + 4 * hi;
       float m01 = 0.f, m02 = 0.f, m03 = 0.f, m04 = 0.f, m05 = 0.f, m06 = 0.f, lmax = 0.f, rmax = 0.f;
       float m_new = m_run, alpha = 1.f, neg_m = 0.f, psum = 0.f, pprev = 0.f;
       bool raise = false;
@@ -2187,7 +2256,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         if constexpr (st_ < 4) {
           if constexpr (FP8) {
             // tokens 8 st_ + 4 hi + (0..3); a token's score is scale * <q, row>
-            const f32x4 v4 = *(const LDS_AS f32x4*)(&s_tsc[it % NST][8 * st_ + 4 * hi]);
+            const f32x4 v4 = *reinterpret_cast<const LDS_AS f32x4*>(tscp + 8 * st_);
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) x[4 * st_ + r4] = s[4 * st_ + r4] * (c * v4[r4]);
           } else {
@@ -2220,7 +2289,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
           m_new = raise ? rmax + kRefHeadroom : m_run;
           asm volatile("" : "+v"(m_new));
         } else if constexpr (st_ == 10) {
-          if constexpr (FP8) tsc4[0] = *(const LDS_AS f32x4*)(&s_tsc[it % NST][4 * hi]);
+          if constexpr (FP8) tsc4[0] = *reinterpret_cast<const LDS_AS f32x4*>(tscp);
           alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
           asm volatile("" : "+v"(alpha));
         } else if constexpr (st_ == 11) {
@@ -2229,7 +2298,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         } else {
           constexpr int j2 = st_ - 12;
           if constexpr (FP8 && (j2 & 3) == 2 && j2 + 2 < 16)   // scales of the next 4 tokens
-            tsc4[(j2 + 2) >> 2] = *(const LDS_AS f32x4*)(&s_tsc[it % NST][8 * ((j2 + 2) >> 2) + 4 * hi]);
+            tsc4[(j2 + 2) >> 2] = *reinterpret_cast<const LDS_AS f32x4*>(tscp + 8 * ((j2 + 2) >> 2));
           const float p = __builtin_amdgcn_exp2f(x[j2] + neg_m);
           psum += p;
           if constexpr (j2 & 1) {
@@ -2260,7 +2329,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         l_run = l_run * alpha + psum;
         m_run = m_new;
         // last tile: zero rows past the end; its V serves the next iteration
-        // (fp8: the conversion zeroed them)
+        // (fp8: zeroed before its scores)
         if (!FP8 && L - t0 < kTile) clear_tail((LDS_AS uint8_t*)s_stage(it % NST), L - t0);
       }
       wait_tile();                // tile it+1 landed (this wave's part); tile it+2 in flight
@@ -2272,10 +2341,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       }
       if (lane == 0) s_flag[wave] = raise_any ? 1 : 0;
       if constexpr (FP8) {
-        // tile it+1 into its bf16 stage (it held tile it-2, whose value
-        // product ran in the previous iteration), then make it and P visible
-        if (it + 1 < n_run) convert8(it + 1);
-        lds_barrier();
+        // tile it+1 is the last: zero its tail before its scales are read
+        // (the next barrier publishes it; a score read racing with it only
+        // meets tokens that the mask drops)
+        const int vn = L - (t0 + kTile);
+        if (it + 1 < n_run && vn < kTile) clear_tail8((LDS_AS uint8_t*)s_stage((it + 1) % NST), vn);
       }
       asm volatile("" ::: "memory");   // the writes above are issued before the reads below
 #pragma unroll
@@ -2294,7 +2364,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     constexpr int kStageRow = 272;
     uint16_t* dst_base = split ? a.part_o + ((int64_t)slot * a.M) * kDL
                                : a.out + ((int64_t)b * a.M) * kDL;
-    LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_stage(0) + wave * (64 * kStageRow);
+    LDS_AS uint8_t* stg = (LDS_AS uint8_t*)s_ring + wave * (64 * kStageRow);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -2355,38 +2425,31 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
 // product of all 128 rows for output columns 128w..128w+127 (the division of
 // the 128-row bf16 kernel). Per 32-token tile, in four phases separated by
 // barriers:
-//  1. the quantised tile (18 KiB of int8 or E4M3 bytes) and its scales,
-//     copied by LDS-DMA into a 3-stage ring, are converted once by all threads
-//     into bf16 tiles in the row-group layout.
-//     q8_0: hi = bf16(scale * value) and lo = bf16(scale * value - hi). The
-//     product of an fp16 scale and an int8 value is exact in fp32 and hi + lo
-//     equals it to within 2^-17 relative, so scores over hi and lo are the
-//     exact dequantised scores up to fp32 accumulation.
-//     fp8: hi = the E4M3 value itself, which bf16 holds exactly; the token's
-//     fp32 scale multiplies its score and its probability instead (one scale
-//     per token, so it factors out of both products).
-//     Tokens past the end of the sequence convert to zero;
-//  2. scores S^T = K q~^T over hi and lo (two MFMA chains of 36 steps; one for
-//     fp8);
+//  1. the int8 tile (18 KiB) and its scales (1152 B), copied by LDS-DMA into a
+//     3-stage ring, are converted once by all threads into two bf16 tiles in
+//     the row-group layout: hi = bf16(scale * value) and
+//     lo = bf16(scale * value - hi). The product of an fp16 scale and an int8
+//     value is exact in fp32 and hi + lo equals it to within 2^-17 relative,
+//     so scores over hi and lo are the exact dequantised scores up to fp32
+//     accumulation; tokens past the end of the sequence convert to zero;
+//  2. scores S^T = K q~^T over hi and lo (two MFMA chains of 36 steps);
 //  3. online softmax of the wave's rows (lazy reference maximum), P published
 //     through LDS with the rescale requests;
-//  4. value product O^T += V^T P^T with V = hi (q8_0: the dequantised value
-//     rounded to bf16; fp8: exact, the scale rides on P).
+//  4. value product O^T += V^T P^T with V = hi, the dequantised value rounded
+//     to bf16.
 // Compared with converting the int8 operands in every wave and scaling each
 // 32-column group's partial score (the 32/64-row q8_0 kernel), the conversion
 // work is done once per tile for all 128 rows and the scores are pure MFMA
 // work.
-template <bool NT, int KV>
-__global__ __launch_bounds__(256, 1) void mla_decode_cvt_kernel(DecodeParams a) {
-  static_assert(KV == MLA_KV_Q8_0 || KV == MLA_KV_FP8, "cache type");
-  constexpr bool FP8 = KV == MLA_KV_FP8;
+template <bool NT>
+__global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) {
   constexpr int NW = 4;
   constexpr int NTH = 64 * NW;
   constexpr int MT = 128;
   constexpr int NST = 3;                  // ring stages of the quantised tiles
   constexpr int KPF = 2;                  // score k-steps in flight (hi and lo each)
   constexpr int CPW = 5;                  // 1 KiB copies per wave per tile (at most 20 per tile)
-  constexpr int STAGE = FP8 ? kFp8StageBytes : kQ8StageBytes;
+  constexpr int STAGE = kQ8StageBytes;
 
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NST][STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t s_hl[2][kTileBytes];   // hi, lo
@@ -2515,12 +2578,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_cvt_kernel(DecodeParams a) 
       bad = bad || __any(inval && bt_base + lane < seg_len);
       bt_lane = inval ? 0 : bt_lane;
     };
-    // Copies of quantised tile idx into ring stage idx % 3: copy k = wave + 4 j
-    // (k < 18: bytes 1024 k .. of the tile's 32 rows, contiguous (int8 or
-    // fp8); q8_0: k = 18, 19: the 1152 bytes of scales, the tail of copy 19
-    // reading the first bytes again into the stage's padding; fp8: k = 18:
-    // the 128 bytes of per-token scales, lanes past them re-reading the
-    // first bytes into the padding).
+    // Copies of int8 tile idx into ring stage idx % 3: copy k = wave + 4 j
+    // (k < 18: bytes 1024 k .. of the tile's 32 rows, contiguous; k = 18, 19:
+    // the 1152 bytes of scales, the tail of copy 19 reading the first bytes
+    // again into the stage's padding).
     auto issue = [&](int idx) {
       int rel = (idx >> 1) - bt_base;   // lane of the segment's id window
       if (rel >= 64) {
@@ -2534,30 +2595,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_cvt_kernel(DecodeParams a) 
       const int64_t row0 = phys * kBT + ((t_begin + idx) & 1) * kTile;
       const uint8_t* src = a.kv + row0 * kQ8RowBytes;
       const uint32_t dst = lds_addr_of(s_ring[idx % NST]);
-      if constexpr (FP8) {
-        const uint8_t* ssrc = a.kv_scales + row0 * 4;
+      const uint8_t* ssrc = a.kv_scales + row0 * kQ8ScaleRowBytes;
 #pragma unroll
-        for (int j = 0; j < CPW; ++j) {
-          const int k = wave + 4 * j;
-          if (k < 18) {
-            copy(src + 1024 * k, 16 * lane, dst + 1024 * k);
-          } else if (k == 18) {
-            const int off = 16 * lane;
-            dma16_sbase(ssrc, off < 4 * kTile ? off : 0, dst + kFp8TileBytes);
-          }
-        }
-      } else {
-        const uint8_t* ssrc = a.kv_scales + row0 * kQ8ScaleRowBytes;
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) {
-          const int k = wave + 4 * j;
-          if (k < 18) {
-            copy(src + 1024 * k, 16 * lane, dst + 1024 * k);
-          } else {
-            // scales: default policy (the tail lanes re-read a partial line)
-            const int off = 1024 * (k - 18) + 16 * lane;
-            dma16_sbase(ssrc, off < kQ8ScaleTileBytes ? off : 0, dst + kQ8TileBytes + 1024 * (k - 18));
-          }
+      for (int j = 0; j < CPW; ++j) {
+        const int k = wave + 4 * j;
+        if (k < 18) {
+          copy(src + 1024 * k, 16 * lane, dst + 1024 * k);
+        } else {
+          // scales: default policy (the tail lanes re-read a partial line)
+          const int off = 1024 * (k - 18) + 16 * lane;
+          dma16_sbase(ssrc, off < kQ8ScaleTileBytes ? off : 0, dst + kQ8TileBytes + 1024 * (k - 18));
         }
       }
     };
@@ -2584,12 +2631,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_cvt_kernel(DecodeParams a) 
     for (int it = 0; it < n_run; ++it) {
       // ---- 1. int8 tile it landed (tile it+1 may be in flight); everyone is
       // done with the previous tile's hi / lo / P
-      // copies this wave issued per tile: q8_0 5; fp8 5, or 4 in wave 3
       if (it + 1 < n_run) {
-        if (FP8 && wave == 3)
-          wait_vmcnt<CPW - 1>();
-        else
-          wait_vmcnt<CPW>();
+        wait_vmcnt<CPW>();
       } else {
         wait_vmcnt<0>();
       }
@@ -2610,56 +2653,37 @@ __global__ __launch_bounds__(256, 1) void mla_decode_cvt_kernel(DecodeParams a) 
         const int t = 8 * wave + rr;
         const uint32_t keep = t < valid ? 0xffffffffu : 0u;
         const LDS_AS uint8_t* srow = st + kQ8RowBytes * t + 8 * cc;
-        if constexpr (FP8) {
-          // fp8 (e4m3) to bf16 is exact (3 mantissa bits fit in 7, and every
-          // e4m3 exponent, subnormals included, is a normal bf16 one); the
-          // per-token scale is applied to the scores and probabilities
-          uint64_t raw[9];
+        const LDS_AS uint32_t* scl =
+            reinterpret_cast<const LDS_AS uint32_t*>(st + kQ8TileBytes + kQ8ScaleRowBytes * t);
+        uint64_t raw[9];
+        uint32_t sc2[9];
 #pragma unroll
-          for (int i = 0; i < 9; ++i) raw[i] = *reinterpret_cast<const LDS_AS uint64_t*>(srow + 64 * i);
+        for (int i = 0; i < 9; ++i) {
+          raw[i] = *reinterpret_cast<const LDS_AS uint64_t*>(srow + 64 * i);
+          sc2[i] = scl[i];   // scales of groups 2i, 2i+1; chunk 8i + cc is group 2i + (cc >> 2)
+        }
+        const int sh16 = 16 * (cc >> 2);
 #pragma unroll
-          for (int i = 0; i < 9; ++i) {
-            const uint32_t w0 = (uint32_t)raw[i] & keep, w1 = (uint32_t)(raw[i] >> 32) & keep;
-            u32x4 whi;
-            whi[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
-            whi[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
-            whi[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
-            whi[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
-            *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[0] + 16 * (tid + NTH * i)) = whi;
+        for (int i = 0; i < 9; ++i) {
+          // the scale is zeroed too: a NaN or infinite scale in an unused
+          // slot would otherwise reach the value product as 0 * inf
+          const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)((sc2[i] & keep) >> sh16));
+          const uint32_t wv[2] = {(uint32_t)raw[i] & keep, (uint32_t)(raw[i] >> 32) & keep};
+          u32x4 whi, wlo;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const uint32_t word = wv[e2 >> 1];
+            const float x0 = d * (float)(int8_t)(word >> (16 * (e2 & 1)));
+            const float x1 = d * (float)(int8_t)(word >> (16 * (e2 & 1) + 8));
+            const uint32_t h = pack_bf16x2(x0, x1);
+            const float h0 = __builtin_bit_cast(float, h << 16);
+            const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+            whi[e2] = h;
+            wlo[e2] = pack_bf16x2(x0 - h0, x1 - h1);
           }
-        } else {
-          const LDS_AS uint32_t* scl =
-              reinterpret_cast<const LDS_AS uint32_t*>(st + kQ8TileBytes + kQ8ScaleRowBytes * t);
-          uint64_t raw[9];
-          uint32_t sc2[9];
-#pragma unroll
-          for (int i = 0; i < 9; ++i) {
-            raw[i] = *reinterpret_cast<const LDS_AS uint64_t*>(srow + 64 * i);
-            sc2[i] = scl[i];   // scales of groups 2i, 2i+1; chunk 8i + cc is group 2i + (cc >> 2)
-          }
-          const int sh16 = 16 * (cc >> 2);
-#pragma unroll
-          for (int i = 0; i < 9; ++i) {
-            // the scale is zeroed too: a NaN or infinite scale in an unused
-            // slot would otherwise reach the value product as 0 * inf
-            const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)((sc2[i] & keep) >> sh16));
-            const uint32_t wv[2] = {(uint32_t)raw[i] & keep, (uint32_t)(raw[i] >> 32) & keep};
-            u32x4 whi, wlo;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              const uint32_t word = wv[e2 >> 1];
-              const float x0 = d * (float)(int8_t)(word >> (16 * (e2 & 1)));
-              const float x1 = d * (float)(int8_t)(word >> (16 * (e2 & 1) + 8));
-              const uint32_t h = pack_bf16x2(x0, x1);
-              const float h0 = __builtin_bit_cast(float, h << 16);
-              const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
-              whi[e2] = h;
-              wlo[e2] = pack_bf16x2(x0 - h0, x1 - h1);
-            }
-            const int U = tid + NTH * i;
-            *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[0] + 16 * U) = whi;
-            *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[1] + 16 * U) = wlo;
-          }
+          const int U = tid + NTH * i;
+          *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[0] + 16 * U) = whi;
+          *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[1] + 16 * U) = wlo;
         }
       }
       lds_barrier();   // hi (and lo) of tile it visible
@@ -2672,40 +2696,24 @@ __global__ __launch_bounds__(256, 1) void mla_decode_cvt_kernel(DecodeParams a) 
       };
       f32x16 sh, sl;
       bf16x8 kh[KPF], kl[KPF];
-      if constexpr (FP8) {
-        // one chain: the converted values are exact
-        constexpr int KF = 2 * KPF;
-        bf16x8 kf8[KF];
 #pragma unroll
-        for (int j2 = 0; j2 < KF; ++j2) kf8[j2] = rd(khi, j2);
-        __builtin_amdgcn_sched_barrier(0);
-        unroll<36>([&](auto kc) {
-          constexpr int k = decltype(kc)::value;
-          mfma_score(sh, kf8[k % KF], qf[k], k == 0);
-          if constexpr (k + KF < 36) kf8[k % KF] = rd(khi, k + KF);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-        mfma_vgpr_drain(sh);
-      } else {
-#pragma unroll
-        for (int j2 = 0; j2 < KPF; ++j2) {
-          kh[j2] = rd(khi, j2);
-          kl[j2] = rd(klo, j2);
+      for (int j2 = 0; j2 < KPF; ++j2) {
+        kh[j2] = rd(khi, j2);
+        kl[j2] = rd(klo, j2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      unroll<36>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        mfma_score(sh, kh[k % KPF], qf[k], k == 0);
+        mfma_score(sl, kl[k % KPF], qf[k], k == 0);
+        if constexpr (k + KPF < 36) {
+          kh[k % KPF] = rd(khi, k + KPF);
+          kl[k % KPF] = rd(klo, k + KPF);
         }
         __builtin_amdgcn_sched_barrier(0);
-        unroll<36>([&](auto kc) {
-          constexpr int k = decltype(kc)::value;
-          mfma_score(sh, kh[k % KPF], qf[k], k == 0);
-          mfma_score(sl, kl[k % KPF], qf[k], k == 0);
-          if constexpr (k + KPF < 36) {
-            kh[k % KPF] = rd(khi, k + KPF);
-            kl[k % KPF] = rd(klo, k + KPF);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        });
-        mfma_vgpr_drain(sh);
-        mfma_vgpr_drain(sl);
-      }
+      });
+      mfma_vgpr_drain(sh);
+      mfma_vgpr_drain(sl);
 
       // ---- 3. online softmax of the wave's rows (log2 domain); element i of
       // the lane is token 8 (i >> 2) + 4 hi + (i & 3) of row l32
@@ -2714,28 +2722,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_cvt_kernel(DecodeParams a) 
       const bool masked = !__all(t0 + kTile <= n_vis);
       const int limx = masked ? n_vis - t0 - 4 * hi : kTile;
       float x[16];
-      // fp8: per-token scales of the lane's 16 tokens 8 j + 4 hi + (0..3);
-      // a masked token's scale is zeroed (an unused slot may hold NaN)
-      float tsc[16];
-      if constexpr (FP8) {
-        const LDS_AS uint8_t* sst = (const LDS_AS uint8_t*)s_ring[it % NST] + kFp8TileBytes;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 v4 = *reinterpret_cast<const LDS_AS f32x4*>(sst + 4 * (8 * j + 4 * hi));
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) tsc[4 * j + r4] = v4[r4];
-        }
-      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const bool vis = !masked || 8 * (i >> 2) + (i & 3) < limx;
-        float sv;
-        if constexpr (FP8) {
-          tsc[i] = vis ? tsc[i] : 0.f;
-          sv = sh[i] * (cs * tsc[i]);
-        } else {
-          sv = (sh[i] + sl[i]) * cs;
-        }
+        const float sv = (sh[i] + sl[i]) * cs;
         x[i] = vis ? sv : -INFINITY;
       }
       float lmax = max3f(x[0], x[1], x[2]);
@@ -2760,11 +2750,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_cvt_kernel(DecodeParams a) 
         const float p0 = __builtin_amdgcn_exp2f(x[2 * j] + neg_m);
         const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] + neg_m);
         psum += p0 + p1;
-        // fp8: V is scale * value; the scale rides on the probability
-        if constexpr (FP8)
-          pw[j] = pack_bf16x2(p0 * tsc[2 * j], p1 * tsc[2 * j + 1]);
-        else
-          pw[j] = pack_bf16x2(p0, p1);
+        pw[j] = pack_bf16x2(p0, p1);
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
@@ -3151,7 +3137,7 @@ int device_cus() {
 
 struct Plan {
   bool narrow;   // 16-row tile (bf16 cache)
-  bool q8w;      // 128-row tile converted to bf16 in LDS (q8_0 or fp8 cache)
+  bool q8w;      // q8_0 cache, 128-row tile converted to bf16 in LDS
   int HG, CG, MT, m_tiles, P, M;
   size_t off_prefix, off_lse, off_o, bytes;
 };
@@ -3194,9 +3180,11 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   // row groups of 32, each wave owning whole rows); the smallest tile that
   // holds all rows of a sequence, so the cache is streamed once per part.
   // q8_0 cache: 32 or 64 rows, each row group's work split over 4 waves, or
-  // 128 rows (the tile converted once into exact bf16 hi / lo parts). More
-  // rows than one tile holds take several row tiles per KV part, placed on
-  // the same XCD so the second read of each cache tile hits L2.
+  // 128 rows (the tile converted once into exact bf16 hi / lo parts). fp8
+  // cache: 128 rows (the bf16 pipeline, its operands read as E4M3 codes and
+  // converted exactly in registers). More rows than one tile holds take
+  // several row tiles per KV part, placed on the same XCD so the second read
+  // of each cache tile hits L2.
   const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
   const bool fp8 = p->kv_dtype == MLA_KV_FP8;
   if (q8 && p->m_tile == 16)
@@ -3214,7 +3202,7 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   } else {
     pl->HG = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   }
-  pl->q8w = (q8 || fp8) && pl->HG == 4;
+  pl->q8w = q8 && pl->HG == 4;
   pl->CG = q8 ? (pl->q8w ? 1 : 4) : 4 / pl->HG;
   pl->MT = pl->narrow ? 16 : 32 * pl->HG;
   pl->m_tiles = (M + pl->MT - 1) / pl->MT;
@@ -3269,12 +3257,11 @@ hipError_t launch_pipe(const DecodeParams& dp, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int KV>
-hipError_t launch_cvt(const DecodeParams& dp, int grid, hipStream_t stream) {
+hipError_t launch_q8w(const DecodeParams& dp, int grid, hipStream_t stream) {
   if (dp.m_tiles == 1)
-    hipLaunchKernelGGL((mla_decode_cvt_kernel<true, KV>), dim3(grid), dim3(256), 0, stream, dp);
+    hipLaunchKernelGGL(mla_decode_q8w_kernel<true>, dim3(grid), dim3(256), 0, stream, dp);
   else
-    hipLaunchKernelGGL((mla_decode_cvt_kernel<false, KV>), dim3(grid), dim3(256), 0, stream, dp);
+    hipLaunchKernelGGL(mla_decode_q8w_kernel<false>, dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -3473,7 +3460,7 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
       break;
     case MLA_KV_Q8_0:
       if (pl.q8w)
-        e = launch_cvt<MLA_KV_Q8_0>(dp, grid, stream);
+        e = launch_q8w(dp, grid, stream);
       else if (pl.HG == 2)
         e = launch_decode<2, 4, true>(dp, grid, stream);
       else if (pl.HG == 1)
@@ -3482,7 +3469,7 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
         return fail(MLA_ERR_UNSUPPORTED, "no q8_0 kernel for this row tile");
       break;
     case MLA_KV_FP8:
-      if (!pl.q8w) return fail(MLA_ERR_UNSUPPORTED, "no fp8 kernel for this row tile");
+      if (pl.HG != 4) return fail(MLA_ERR_UNSUPPORTED, "no fp8 kernel for this row tile");
       e = launch_pipe<true>(dp, grid, stream);
       break;
     default:
