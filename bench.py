@@ -309,6 +309,20 @@ def main():
         if rec.get("source_hash") == source_hash() and rec.get("num_parts") == parts:
             traffic = rec.get("bytes_per_launch")
 
+    # matrix-core counters of the same workload and source (rocprofv3 run
+    # summarised under profiles/), reported beside the algorithmic fractions
+    mfma_counters = None
+    mfile = os.path.join(ROOT, "profiles", f"mfma_{w.name}.json")
+    if os.path.exists(mfile):
+        rec = json.load(open(mfile))
+        if rec.get("source_hash") == source_hash():
+            mfma_counters = {"probe_tflops": rec.get("probe_tflops"),
+                             "per_kernel": {k: {"busy_frac": v["mfma_busy_frac"],
+                                                "executed_frac_of_probe": v["executed_frac_of_probe"],
+                                                "median_duration_us": v["median_duration_us"]}
+                                            for k, v in rec["per_kernel"].items()
+                                            if v.get("executed_bf16_flops", 0) > 0}}
+
     lo, hi = int(w.seqlens.min()), int(w.seqlens.max())
     seqlen_desc = lo if lo == hi else f"{lo}..{hi} (mean {float(w.seqlens.mean()):.1f})"
     res = {
@@ -330,6 +344,8 @@ def main():
                      "p90": round(float(np.percentile(per_launch_ms, 90)), 5)},
         "roofline": roofline(nbytes, flops, avg_ms, traffic),
     }
+    if mfma_counters:
+        res["roofline"]["mfma_counters"] = mfma_counters
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs)
     print(json.dumps(res), flush=True)
