@@ -54,17 +54,33 @@ __device__ __forceinline__ void store_group(uint16_t* dst, const f32x16& acc, in
   *reinterpret_cast<uint64_t*>(dst) = (uint64_t)w0 | ((uint64_t)w1 << 32);
 }
 
+// Row tiles of a head are split over gridDim.z workgroups only as far as
+// needed to give the chip about 512 workgroups: each split reads the head's
+// weights again, and with 4 workgroups per head 128 heads already give 512.
+unsigned row_splits(int64_t n_tok, int heads) {
+  const int64_t tiles = (n_tok + 31) / 32;
+  int64_t gz = (512 + 4 * (int64_t)heads - 1) / (4 * (int64_t)heads);
+  if (gz > tiles) gz = tiles;
+  if (gz > 8) gz = 8;
+  return (unsigned)(gz < 1 ? 1 : gz);
+}
+
 // Query absorption. Workgroup (h, cb): latent columns 128 cb .. 128 cb + 127
 // of head h, wave w the 32 columns d0 = 128 cb + 32 w. Per 32-row tile of the
 // head's rows: D[d][t] = sum_j A[d][j] B[j][t], A = W_UK[h]^T (stored as
 // w_uk_t[h][d][j], so a lane's 8 contraction values are contiguous), B = the
 // rows' q_nope. The A fragments (8 k-steps, 32 VGPRs) stay in registers over
-// all tiles. Workgroups with cb = 0 also copy the rows' q_rope.
+// all tiles. The tile's 32 x 128 outputs are staged in LDS so that each row's
+// 256 bytes go out as whole 128-byte lines (stored from the MFMA layout, a
+// lane's 8-byte pieces of 32 rows 147 KB apart would be written piecemeal).
+// Workgroups with cb = 0 also copy the rows' q_rope.
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ q_rope,
                                                      const uint16_t* __restrict__ w_uk_t,
                                                      uint16_t* __restrict__ q_abs,
                                                      int64_t n_tok, int H) {
+  constexpr int kPad = 136;   // staged row: 128 outputs + 8 (16-byte aligned, spreads banks)
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[32 * kPad];
   const int h = blockIdx.x, cb = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
   const int d0 = 128 * cb + 32 * wave;
@@ -72,20 +88,36 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
   const uint16_t* wrow = w_uk_t + ((int64_t)h * kDL + d0 + l32) * kDH + 8 * hi;
 #pragma unroll
   for (int k = 0; k < 8; ++k) af[k] = load16(wrow + 16 * k);
-  for (int64_t t0 = (int64_t)blockIdx.z * 32; t0 < n_tok; t0 += (int64_t)gridDim.z * 32) {
+  // the next tile's rows are loaded while this one is computed
+  auto load_rows = [&](int64_t t0, bf16x8* bf) {
     const int64_t t = t0 + l32 < n_tok ? t0 + l32 : n_tok - 1;
     const uint16_t* qrow = q_nope + (t * H + h) * kDH + 8 * hi;
-    bf16x8 bf[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) bf[k] = load16(qrow + 16 * k);
+  };
+  const int64_t tstep = (int64_t)gridDim.z * 32;
+  bf16x8 bn[8];
+  if ((int64_t)blockIdx.z * 32 < n_tok) load_rows((int64_t)blockIdx.z * 32, bn);
+  for (int64_t t0 = (int64_t)blockIdx.z * 32; t0 < n_tok; t0 += tstep) {
+    bf16x8 bf[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) bf[k] = bn[k];
+    if (t0 + tstep < n_tok) load_rows(t0 + tstep, bn);
     f32x16 acc = {};
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k], bf[k], acc, 0, 0, 0);
-    if (t0 + l32 < n_tok) {
-      uint16_t* orow = q_abs + ((t0 + l32) * H + h) * kDK + d0 + 4 * hi;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) store_group(orow + 8 * g, acc, g);
+    for (int g = 0; g < 4; ++g) store_group(s_out + l32 * kPad + 32 * wave + 8 * g + 4 * hi, acc, g);
+    __syncthreads();
+    // row r of the tile, 16-byte piece c (of 16): thread 16 r' + c, two rounds
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = threadIdx.x + 256 * i, r = u >> 4, c = u & 15;
+      if (t0 + r < n_tok)
+        *reinterpret_cast<u32x4*>(q_abs + ((t0 + r) * H + h) * kDK + 128 * cb + 8 * c) =
+            *reinterpret_cast<const u32x4*>(s_out + r * kPad + 8 * c);
     }
+    __syncthreads();
     if (cb == 0) {
       // q_rope of the tile's rows: 128 bytes per row, 8 lanes per row
       for (int u = threadIdx.x; u < 32 * 8; u += 256) {
@@ -117,12 +149,21 @@ __global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict
   const uint16_t* wrow = w_uv + ((int64_t)h * kDH + 32 * jb + l32) * kDL + kbase + 8 * hi;
 #pragma unroll
   for (int k = 0; k < 8; ++k) af[k] = load16(wrow + 16 * k);
-  for (int64_t t0 = (int64_t)blockIdx.z * 32; t0 < n_tok; t0 += (int64_t)gridDim.z * 32) {
+  // the next tile's rows are loaded while this one is computed
+  auto load_rows = [&](int64_t t0, bf16x8* bf) {
     const int64_t t = t0 + l32 < n_tok ? t0 + l32 : n_tok - 1;
     const uint16_t* orow_in = o_lat + (t * H + h) * kDL + kbase + 8 * hi;
-    bf16x8 bf[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) bf[k] = load16(orow_in + 16 * k);
+  };
+  const int64_t tstep = (int64_t)gridDim.z * 32;
+  bf16x8 bn[8];
+  if ((int64_t)blockIdx.z * 32 < n_tok) load_rows((int64_t)blockIdx.z * 32, bn);
+  for (int64_t t0 = (int64_t)blockIdx.z * 32; t0 < n_tok; t0 += tstep) {
+    bf16x8 bf[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) bf[k] = bn[k];
+    if (t0 + tstep < n_tok) load_rows(t0 + tstep, bn);
     f32x16 acc = {};
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k], bf[k], acc, 0, 0, 0);
@@ -295,8 +336,7 @@ mla_status mla_absorb_query(int64_t rows, int32_t num_heads, const void* q_nope,
     return MLA_ERR_INVALID_ARG;
   }
   const int64_t n_tok = rows / num_heads;
-  const int64_t tiles = (n_tok + 31) / 32;
-  const unsigned gz = (unsigned)(tiles < 8 ? tiles : 8);
+  const unsigned gz = row_splits(n_tok, num_heads);
   hipLaunchKernelGGL(absorb_kernel, dim3(num_heads, 4, gz), dim3(256), 0, stream,
                      (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk_t,
                      (uint16_t*)q_abs, n_tok, num_heads);
@@ -324,8 +364,7 @@ mla_status mla_project_output(int64_t rows, int32_t num_heads, const void* o_lat
     return MLA_ERR_INVALID_ARG;
   }
   const int64_t n_tok = rows / num_heads;
-  const int64_t tiles = (n_tok + 31) / 32;
-  const unsigned gz = (unsigned)(tiles < 8 ? tiles : 8);
+  const unsigned gz = row_splits(n_tok, num_heads);
   hipLaunchKernelGGL(project_kernel, dim3(num_heads, 4, gz), dim3(256), 0, stream,
                      (const uint16_t*)o_lat, (const uint16_t*)w_uv, (uint16_t*)o, n_tok,
                      num_heads);
