@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration and "
                          "measured copy bandwidth)")
+    ap.add_argument("--layer-steps", action="store_true",
+                    help="time the steps either side of the decode instead (query absorption, "
+                         "output projection, cache append) at the bench shape")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="run only the MFMA probe kernel (sustained dense bf16 MFMA rate; "
                          "the MFMA-busy counter calibration)")
@@ -84,6 +87,71 @@ def copy_calibration():
     ms = e0.elapsed_time(e1) / 2
     print(json.dumps({"copy_bytes": n, "launches": 3, "copy_ms": round(ms, 4),
                       "read_plus_write_gbs": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
+
+
+def layer_steps(steps: int):
+    """The steps either side of the decode at the bench workload's shape (64
+    query rows x 128 heads): query absorption, output projection and the
+    cache append (bf16, q8_0, fp8), each replayed `steps` times from a HIP
+    graph so that host launch cost stays out; HIP events on the launch stream.
+    Algorithmic bytes: every weight once plus the activations in and out."""
+    import torch
+    import mla_latent_kv_10_amd as mla
+    import workload as wl
+    mla.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev).manual_seed(7)
+    rows, H = 64, 128
+
+    def rnd(*shape):
+        return torch.randn(*shape, device=dev, generator=g).to(torch.bfloat16)
+
+    qn, qr = rnd(rows, 1, H, 128), rnd(rows, 1, H, 64)
+    wk, wv = rnd(H, 512, 128) * 0.05, rnd(H, 128, 512) * 0.05
+    qa = torch.empty(rows, 1, H, 576, dtype=torch.bfloat16, device=dev)
+    ol = rnd(rows, 1, H, 512)
+    o = torch.empty(rows, 1, H, 128, dtype=torch.bfloat16, device=dev)
+    w = wl.config_workload(WORKLOAD_CFG)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seqlens).to(dev)
+    new = rnd(w.B, 1, 576)
+    caches = {"bf16": (torch.empty(w.kv.shape, dtype=torch.bfloat16, device=dev), None),
+              "q8_0": (torch.empty(w.kv.shape, dtype=torch.int8, device=dev),
+                       torch.empty(w.kv.shape[:2] + (18,), dtype=torch.float16, device=dev)),
+              "fp8": (torch.empty(w.kv.shape, dtype=torch.uint8, device=dev),
+                      torch.empty(w.kv.shape[:2], dtype=torch.float32, device=dev))}
+    wbytes = H * 128 * 512 * 2
+    cases = [("absorb_query", lambda: mla.mla_absorb_query(qn, qr, wk, qa),
+              wbytes + qn.numel() * 2 + qr.numel() * 2 + qa.numel() * 2),
+             ("project_output", lambda: mla.mla_project_output(ol, wv, o),
+              wbytes + ol.numel() * 2 + o.numel() * 2)]
+    per_row = {"bf16": 1152, "q8_0": 612, "fp8": 580}
+    for kvd, (kv, sc) in caches.items():
+        cases.append((f"cache_append_{kvd}",
+                      lambda kv=kv, sc=sc: mla.mla_cache_append(new, bt, sl, kv, sc),
+                      new.numel() * 2 + w.B * per_row[kvd]))
+    out = {}
+    stream = torch.cuda.current_stream(dev)
+    for name, fn, nbytes in cases:
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        out[name] = {"us": round(us, 2), "algorithmic_bytes": nbytes,
+                     "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    print(json.dumps({"layer_steps": out, "rows": rows, "heads": H, "launches_per_graph": steps}))
 
 
 def mfma_probe():
@@ -208,6 +276,9 @@ def main():
         return
     if args.mfma_probe:
         mfma_probe()
+        return
+    if args.layer_steps:
+        layer_steps(args.steps)
         return
     import torch
     import mla_latent_kv_10_amd as mla
