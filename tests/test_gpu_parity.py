@@ -93,29 +93,36 @@ def test_full_size_config_all_rows(cfg):
     compare(out, lse, *oracle_rows(w), what=w.name, kv_dtype=w.kv_dtype, flat=cfg != 4)
 
 
-def test_forced_part_counts_agree():
-    w = wl.make_workload("parts", 4, 1, 128, [2000, 1, 4096, 777], seed=5, table="permuted")
+@pytest.mark.parametrize("kvd", ["bf16", "fp8"])
+def test_forced_part_counts_agree(kvd):
+    w = wl.make_workload("parts", 4, 1, 128, [2000, 1, 4096, 777], seed=5, table="permuted",
+                         kv_dtype=kvd)
     ref_out, ref_lse, ref_abs = oracle_rows(w)
     t = device_inputs(w)
     T = int(((np.maximum(w.seqlens, 0) + 63) // 64).sum())
     results = []
     for P in (1, 2, 7, 64, T, T + 13):
-        log(f"parts {P}")
+        log(f"parts {P} {kvd}")
         out, lse, _ = run_gpu(w, t, num_parts=P)
-        compare(out, lse, ref_out, ref_lse, ref_abs, what=f"P={P}")
+        compare(out, lse, ref_out, ref_lse, ref_abs, what=f"P={P} {kvd}", kv_dtype=kvd)
         results.append((out, lse))
     for out, lse in results[1:]:
         assert np.abs(out - results[0][0]).max() <= 2e-2
         assert np.abs(lse - results[0][1]).max() <= 1e-3
 
 
-def test_block_permutation_is_bit_identical():
-    w = wl.make_workload("perm", 3, 1, 128, [900, 64, 2049], seed=6)
+@pytest.mark.parametrize("kvd", ["bf16", "fp8"])
+def test_block_permutation_is_bit_identical(kvd):
+    w = wl.make_workload("perm", 3, 1, 128, [900, 64, 2049], seed=6, kv_dtype=kvd)
     out1, lse1, bits1 = run_gpu(w, num_parts=5)
     perm = wl.permutation(w.num_blocks, 7, 1)
     kv2 = np.empty_like(w.kv)
     kv2[perm] = w.kv
-    w2 = wl.Workload(**{**w.__dict__, "kv": kv2,
+    sc2 = None
+    if w.kv_scales is not None:
+        sc2 = np.empty_like(w.kv_scales)
+        sc2[perm] = w.kv_scales
+    w2 = wl.Workload(**{**w.__dict__, "kv": kv2, "kv_scales": sc2,
                         "block_table": np.where(w.block_table >= 0,
                                                 perm[np.maximum(w.block_table, 0)], -1)
                         .astype(np.int32)})
@@ -318,27 +325,32 @@ def test_repeat_runs_are_bit_identical():
     assert np.array_equal(bits1, bits2) and np.array_equal(lse1, lse2)
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("kvd", ["bf16", "fp8"])
+def test_graph_replay_matches_eager(kvd):
     """A decode step captured in a HIP graph (split plan + decode + combine,
     the way the benchmark replays it) gives the eager result bit for bit on
     every replay, with eager work and synchronisations between replays."""
-    w = wl.make_workload("graph", 4, 1, 128, [700, 1300, 64, 2100], seed=21, table="permuted")
+    w = wl.make_workload("graph", 4, 1, 128, [700, 1300, 64, 2100], seed=21, table="permuted",
+                         kv_dtype=kvd)
     t = device_inputs(w)
     out = torch.empty((w.B, w.s_q, w.H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.s_q, w.H), dtype=torch.float32, device="cuda")
-    prob = mla.make_problem(t["q"], t["kv"], t["bt"], kv_dtype=mla.KV_BF16, max_seqlen=w.max_seqlen,
-                            num_parts=16)
+    prob = mla.make_problem(t["q"], t["kv"], t["bt"],
+                            kv_dtype={"bf16": mla.KV_BF16, "fp8": mla.KV_FP8}[kvd],
+                            max_seqlen=w.max_seqlen, num_parts=16)
     ws = torch.empty(max(16, mla.workspace_size(prob)), dtype=torch.uint8, device="cuda")
 
     def step():
         mla.mla_decode(t["q"], t["kv"], t["bt"], t["sl"], w.softmax_scale, out, lse,
-                       max_seqlen=w.max_seqlen, num_parts=16, workspace=ws)
+                       kv_scales=t["kv_scales"], max_seqlen=w.max_seqlen, num_parts=16,
+                       workspace=ws)
 
     step()
     torch.cuda.synchronize()
     ref_out = out.clone()
     ref_lse = lse.clone()
-    compare(out.float().cpu().numpy(), lse.cpu().numpy(), *oracle_rows(w), what="graph eager")
+    compare(out.float().cpu().numpy(), lse.cpu().numpy(), *oracle_rows(w), what=f"graph eager {kvd}",
+            kv_dtype=kvd)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()

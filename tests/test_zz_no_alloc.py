@@ -58,11 +58,12 @@ def test_noalloc_matches_decode_on_two_calls_in_a_row():
     _check(w2, "noalloc 2", num_parts=5)
 
 
-def test_noalloc_q8_and_causal_pair():
-    w = wl.make_workload("noalloc_q8", 3, 2, 64, [700, 2100, 65], seed=43, table="permuted",
-                         kv_dtype="q8_0")
-    log("noalloc q8_0, causal pairs")
-    _check(w, "noalloc q8")
+@pytest.mark.parametrize("kvd,H", [("q8_0", 64), ("fp8", 128)])
+def test_noalloc_quantised_cache_and_causal_pair(kvd, H):
+    w = wl.make_workload(f"noalloc_{kvd}", 3, 2, H, [700, 2100, 65], seed=43, table="permuted",
+                         kv_dtype=kvd)
+    log(f"noalloc {kvd}, {H} heads, causal pairs")
+    _check(w, f"noalloc {kvd}")
 
 
 def test_noalloc_refuses_a_workspace_beyond_the_array():
