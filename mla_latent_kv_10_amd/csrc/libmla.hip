@@ -3215,10 +3215,11 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
     const int64_t ms = p->max_seqlen > 0 ? (p->max_seqlen < cap_tokens ? p->max_seqlen : cap_tokens)
                                          : cap_tokens;
     const int64_t t_max = (int64_t)p->batch * ((ms + MLA_BLOCK_TOKENS - 1) / MLA_BLOCK_TOKENS);
+    // one workgroup per CU; when the cache has fewer blocks than that, parts
+    // of a single block (two tiles) still cut the latency of small problems,
+    // since all parts run at once and their merge is short
     int64_t want = cus / pl->m_tiles;
-    const int64_t min_blocks_per_part = 4;
-    const int64_t cap = (t_max + min_blocks_per_part - 1) / min_blocks_per_part;
-    if (want > cap) want = cap;
+    if (want > t_max) want = t_max;
     if (want < 1) want = 1;
     P = (int)want;
   }
