@@ -78,6 +78,12 @@ def _load():
         lib.oracle_quantize_q8_0_row.argtypes = [vp, vp, vp]
         lib.oracle_quantize_q8_0_row.restype = None
         lib.oracle_cache_append.argtypes = [i32, i32, i32, vp, vp, i32, vp, i64, vp, vp]
+        lib.oracle_hadamard32.argtypes = [vp, vp]
+        lib.oracle_hadamard32.restype = None
+        lib.oracle_q4_value.argtypes = [ctypes.c_int, u16]
+        lib.oracle_q4_value.restype = dbl
+        lib.oracle_quantize_q4h_row.argtypes = [vp, vp, vp]
+        lib.oracle_quantize_q4h_row.restype = None
         lib.oracle_cache_append.restype = i64
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -89,6 +95,17 @@ def _load():
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+Q4_ROW_BYTES = D_K // 2
+
+
+def _kind(kv) -> int:
+    """Cache type from the array: bf16 bits (uint16), q8_0 (int8), fp8 (uint8
+    rows of 576) or q4_0 in Hadamard rotation (uint8 rows of 288 code bytes)."""
+    if kv.dtype == np.uint8 and kv.shape[-1] == Q4_ROW_BYTES:
+        return 3
+    return {np.dtype(np.uint16): 0, np.dtype(np.int8): 1, np.dtype(np.uint8): 2}[kv.dtype]
 
 
 def _p(a):
@@ -142,8 +159,9 @@ def decode_absorbed(q, kv, block_table, seqlens, softmax_scale, *, kv_scales=Non
                     with_abs=False):
     """Absorbed-form decode (fp64). q: uint16 [B, s_q, H, 576] bf16 bits.
 
-    kv: uint16 bf16 bits, int8 (with kv_scales uint16 fp16 bits [nb, 64, 18]) or
-    uint8 fp8 E4M3 (with kv_scales float32 [nb, 64]).
+    kv: uint16 bf16 bits, int8 (with kv_scales uint16 fp16 bits [nb, 64, 18]),
+    uint8 fp8 E4M3 (with kv_scales float32 [nb, 64]) or uint8 q4_0 codes
+    [nb, 64, 288] in Hadamard rotation (with kv_scales uint16 fp16 bits [nb, 64, 18]).
     rows: optional int64 row ids r = (b * s_q + i) * H + h.
     Returns (out float64 [n, 512], lse float64 [n]); all rows -> shaped [B, s_q, H, ...].
     with_abs: also return out_abs = sum_t p_t |row_t| (same shape as out).
@@ -151,9 +169,9 @@ def decode_absorbed(q, kv, block_table, seqlens, softmax_scale, *, kv_scales=Non
     q = _c(q, np.uint16)
     B, s_q, H, dk = q.shape
     assert dk == D_K
-    kind = {np.dtype(np.uint16): 0, np.dtype(np.int8): 1, np.dtype(np.uint8): 2}[kv.dtype]
+    kind = _kind(kv)
     kv = _c(kv, kv.dtype)
-    sc = None if kind == 0 else _c(kv_scales, np.uint16 if kind == 1 else np.float32)
+    sc = None if kind == 0 else _c(kv_scales, np.float32 if kind == 2 else np.uint16)
     bt = _c(block_table, np.int32)
     sl = _c(seqlens, np.int32)
     rr = None if rows is None else _c(rows, np.int64)
@@ -255,13 +273,55 @@ def cache_append(rows, block_table, seqlens, kv, kv_scales=None):
     rows = _c(rows, np.uint16)
     B, s_q, dk = rows.shape
     assert dk == D_K and kv.flags["C_CONTIGUOUS"]
-    kind = {np.dtype(np.uint16): 0, np.dtype(np.int8): 1, np.dtype(np.uint8): 2}[kv.dtype]
+    kind = _kind(kv)
     if kind:
         assert kv_scales is not None and kv_scales.flags["C_CONTIGUOUS"]
     bt = _c(block_table, np.int32)
     sl = _c(seqlens, np.int32)
     return int(_load().oracle_cache_append(B, s_q, kind, _p(rows), _p(bt), bt.shape[1], _p(sl),
                                            kv.shape[0], _p(kv), _p(kv_scales)))
+
+
+def hadamard32(x):
+    """y = R x per 32-value block (R = H / sqrt(32), H the Sylvester-Hadamard
+    matrix), in double, from the matrix entries. x: float64 [..., 32k]."""
+    x = _c(x, np.float64)
+    flat = x.reshape(-1, 32)
+    y = np.empty_like(flat)
+    for i in range(flat.shape[0]):
+        _load().oracle_hadamard32(_p(flat[i]), y[i:].ctypes.data)
+    return y.reshape(x.shape)
+
+
+def q4_value(code: int, scale_bits: int) -> float:
+    return float(_load().oracle_q4_value(int(code), int(scale_bits)))
+
+
+def quantize_q4h(x):
+    """Rotating q4_0 cache writer on float32 rows of 576 -> (uint8 codes [.., 288],
+    fp16 scale bits [.., 18])."""
+    x = _c(x, np.float32)
+    rows = x.size // D_K
+    flat = x.reshape(rows, D_K)
+    q = np.empty((rows, Q4_ROW_BYTES), np.uint8)
+    sc = np.empty((rows, D_K // 32), np.uint16)
+    for r in range(rows):
+        _load().oracle_quantize_q4h_row(_p(flat[r]), _p(q[r]), _p(sc[r]))
+    return q.reshape(x.shape[:-1] + (Q4_ROW_BYTES,)), sc.reshape(x.shape[:-1] + (D_K // 32,))
+
+
+def q4h_rows(codes, scales):
+    """The cached rows a q4_0-in-rotation cache stands for, in double: per block
+    the stored values scale * (code - 8), rotated back by R. codes uint8
+    [..., 288], scales uint16 fp16 bits [..., 18] -> float64 [..., 576]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint16)
+    lo = (codes & 0xF).astype(np.int64)
+    hi = (codes >> 4).astype(np.int64)
+    c = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (D_K,))
+    d = np.vectorize(fp16_value)(scales.astype(np.int64))
+    y = d.repeat(32, axis=-1) * (c - 8)
+    return hadamard32(y)
 
 
 def combine(part_out, part_lse):

@@ -24,6 +24,11 @@
  *    softmax attention computed directly in two passes.
  *  - The q8_0 cache type (FlashMLA page, "KV cache with MLA"): blocks of 32
  *    int8 values sharing one fp16 scale; a value is scale * int.
+ *  - The low-bit cache with a Hadamard transform of the keys before
+ *    quantisation (same page and section, the q4_0 cache with the K-cache
+ *    Hadamard option): here every 32-value block of a row is rotated by the
+ *    orthonormal 32-point Walsh-Hadamard matrix and stored as a q4_0 block
+ *    (4-bit codes, one fp16 scale); reading it back rotates the block again.
  *
  * Readings where the pages are silent (the paged layout, the causal rule for
  * several new tokens, empty rows, the split plan) follow the API contract of
@@ -49,6 +54,7 @@
 #define Q8_GROUPS (D_K / Q8_GROUP)
 #define D_HEAD_NOPE 128 /* per-head no-RoPE key width of the decompressed form */
 #define D_HEAD_V 128    /* per-head value width of the decompressed form */
+#define Q4_ROW_BYTES (D_K / 2) /* q4_0 codes of one row, two per byte */
 
 /* ------------------------------------------------------------ decoding */
 
@@ -191,10 +197,87 @@ void oracle_quantize_q8_0_row(const float* x, int8_t* q, uint16_t* scales) {
   }
 }
 
+/* --------------------------------------- q4_0 blocks in Hadamard rotation */
+
+/*
+ * The rotation. H is the 32 x 32 Sylvester-Hadamard matrix,
+ * H[m][j] = (-1)^popcount(m & j); R = H / sqrt(32) is symmetric and
+ * orthogonal, so R R = I and R is its own inverse. A cached row is stored
+ * block by block (block g = columns 32g .. 32g+31) as the q4_0 encoding of
+ * y = R x_g, and read back as x_g = R y.
+ */
+int oracle_hadamard_sign(int m, int j) { return (__builtin_popcount((unsigned)(m & j)) & 1) ? -1 : 1; }
+
+/* y = R x for one block, in double, straight from the matrix entries. */
+void oracle_hadamard32(const double* x, double* y) {
+  for (int m = 0; m < Q8_GROUP; ++m) {
+    double acc = 0.0;
+    for (int j = 0; j < Q8_GROUP; ++j) acc += oracle_hadamard_sign(m, j) * x[j];
+    y[m] = acc / sqrt((double)Q8_GROUP);
+  }
+}
+
+/* Value of one cached q4_0 code: scale * (code - 8), exact in double. */
+double oracle_q4_value(int code, uint16_t scale_bits) {
+  return oracle_fp16_value(scale_bits) * (double)(code - 8);
+}
+
+/* Code j (0..31) of a 16-byte q4_0 block: byte j / 2, low nibble for even j. */
+int oracle_q4_code(const uint8_t* blk, int j) { return (blk[j >> 1] >> (4 * (j & 1))) & 0xF; }
+
+/*
+ * The cache writer for one row of 576 values (the reading where the pages
+ * name the format only). Per block, in single precision and in this order
+ * (the decision that picks each integer code is taken in the precision and
+ * order the GPU writer uses):
+ *   1. y = R x by the fast Walsh-Hadamard transform: for s = 1, 2, 4, 8, 16,
+ *      every pair (i, i + s) with i & s = 0 becomes (a + b, a - b); then each
+ *      y times the single-precision value of 1/sqrt(32);
+ *   2. q4_0: m = the first y of largest magnitude, d = m / -8,
+ *      code = min(15, floor(y / d + 8.5)) (so m itself gets code 0), every
+ *      code 8 when d = 0; the stored scale is fp16(d) (round to nearest even).
+ * Codes go two per byte, code j of block g in byte 16 g + j / 2, low nibble
+ * for even j.
+ */
+void oracle_quantize_q4h_row(const float* x, uint8_t* q, uint16_t* scales) {
+  const float inv_sqrt32 = (float)(1.0 / sqrt(32.0));
+  for (int g = 0; g < Q8_GROUPS; ++g) {
+    float y[Q8_GROUP];
+    for (int j = 0; j < Q8_GROUP; ++j) y[j] = x[g * Q8_GROUP + j];
+    for (int st = 1; st < Q8_GROUP; st <<= 1)
+      for (int i = 0; i < Q8_GROUP; ++i)
+        if ((i & st) == 0) {
+          const float a = y[i], b = y[i + st];
+          y[i] = a + b;
+          y[i + st] = a - b;
+        }
+    for (int j = 0; j < Q8_GROUP; ++j) y[j] = y[j] * inv_sqrt32;
+    float m = 0.0f;
+    for (int j = 0; j < Q8_GROUP; ++j)
+      if (fabsf(y[j]) > fabsf(m)) m = y[j];
+    const float d = m / -8.0f;
+    scales[g] = oracle_fp16_bits(d);
+    uint8_t* blk = q + 16 * g;
+    for (int j = 0; j < Q8_GROUP; j += 2) {
+      int c[2];
+      for (int h = 0; h < 2; ++h) {
+        if (d == 0.0f) {
+          c[h] = 8;
+        } else {
+          const float t = floorf(y[j + h] / d + 8.5f);
+          c[h] = t > 15.0f ? 15 : (int)t;
+        }
+      }
+      blk[j >> 1] = (uint8_t)(c[0] | (c[1] << 4));
+    }
+  }
+}
+
 /* ------------------------------------------------------------ paged cache */
 
 typedef struct {
-  int kind; /* 0: bf16 bits, 1: q8_0, 2: fp8 with per-token fp32 scales */
+  int kind; /* 0: bf16 bits, 1: q8_0, 2: fp8 with per-token fp32 scales, 3: q4_0 in
+               Hadamard rotation */
   const void* kv;
   const void* scales;
   int64_t num_blocks;
@@ -214,10 +297,19 @@ static void cache_row(const cache_view* c, int32_t b, int64_t t, double* dst) {
     const int8_t* r = (const int8_t*)c->kv + row * D_K;
     const uint16_t* s = (const uint16_t*)c->scales + row * Q8_GROUPS;
     for (int d = 0; d < D_K; ++d) dst[d] = oracle_q8_value(r[d], s[d / Q8_GROUP]);
-  } else {
+  } else if (c->kind == 2) {
     const uint8_t* r = (const uint8_t*)c->kv + row * D_K;
     const double s = (double)((const float*)c->scales)[row];
     for (int d = 0; d < D_K; ++d) dst[d] = s * oracle_fp8_value(r[d]);
+  } else {
+    /* each block: the stored (rotated) values, rotated back by R */
+    const uint8_t* r = (const uint8_t*)c->kv + row * Q4_ROW_BYTES;
+    const uint16_t* s = (const uint16_t*)c->scales + row * Q8_GROUPS;
+    for (int g = 0; g < Q8_GROUPS; ++g) {
+      double y[Q8_GROUP];
+      for (int j = 0; j < Q8_GROUP; ++j) y[j] = oracle_q4_value(oracle_q4_code(r + 16 * g, j), s[g]);
+      oracle_hadamard32(y, dst + Q8_GROUP * g);
+    }
   }
 }
 
@@ -343,9 +435,10 @@ static int decode_absorbed_core(int32_t B, int32_t s_q, int32_t H, const uint16_
 /*
  * Absorbed-form decode, the contract of the GPU kernel.
  *   q          bf16 bits [B, s_q, H, 576], row r = (b * s_q + i) * H + h
- *   kv         bf16 bits, int8 or fp8 [num_blocks, 64, 576] (kv_kind 0 / 1 / 2)
- *   kv_scales  fp16 bits [num_blocks, 64, 18] for q8_0, fp32 [num_blocks, 64]
- *              for fp8, else NULL
+ *   kv         bf16 bits, int8 or fp8 [num_blocks, 64, 576] (kv_kind 0 / 1 / 2), or
+ *              q4_0 codes [num_blocks, 64, 288] in Hadamard rotation (kv_kind 3)
+ *   kv_scales  fp16 bits [num_blocks, 64, 18] for q8_0 and q4_0, fp32
+ *              [num_blocks, 64] for fp8, else NULL
  *   block_table int32 [B, max_blocks]; seqlens int32 [B] (new tokens included)
  *   rows       optional list of row ids to compute (NULL = all, in order)
  *   out        double [n_rows, 512];  lse double [n_rows] (natural log)
@@ -401,7 +494,9 @@ int oracle_decode_absorbed_f64q(int32_t B, int32_t s_q, int32_t H, const double*
  *   kind 1: kv int8 [num_blocks, 64, 576] + scales fp16 bits [num_blocks, 64, 18],
  *           written by the q8_0 cache writer above;
  *   kind 2: kv fp8 [num_blocks, 64, 576] + scales fp32 [num_blocks, 64], written by
- *           the fp8 cache writer above.
+ *           the fp8 cache writer above;
+ *   kind 3: kv uint8 [num_blocks, 64, 288] (q4_0 codes) + scales fp16 bits
+ *           [num_blocks, 64, 18], written by the rotating q4_0 writer above.
  * Returns the number of rows written.
  */
 int64_t oracle_cache_append(int32_t B, int32_t s_q, int32_t kind, const uint16_t* rows,
@@ -424,8 +519,11 @@ int64_t oracle_cache_append(int32_t B, int32_t s_q, int32_t kind, const uint16_t
         for (int d = 0; d < D_K; ++d) x[d] = (float)oracle_bf16_value(src[d]);
         if (kind == 1)
           oracle_quantize_q8_0_row(x, (int8_t*)kv + dst * D_K, (uint16_t*)scales + dst * Q8_GROUPS);
-        else
+        else if (kind == 2)
           oracle_quantize_fp8_row(x, (uint8_t*)kv + dst * D_K, (float*)scales + dst);
+        else
+          oracle_quantize_q4h_row(x, (uint8_t*)kv + dst * Q4_ROW_BYTES,
+                                  (uint16_t*)scales + dst * Q8_GROUPS);
       }
       ++written;
     }

@@ -5,7 +5,7 @@
  * entry point over small inputs that reach the edge paths (empty and
  * one-token sequences, a tail block, an invalid block id, clamped seqlens, a
  * causal pair, empty and NaN parts in the merge, skipped append rows) for
- * the three cache types. Any out-of-bounds access, use of uninitialised heap,
+ * the four cache types. Any out-of-bounds access, use of uninitialised heap,
  * signed overflow or other undefined behaviour aborts the run; the results
  * themselves are checked by the other oracle tests.
  */
@@ -50,6 +50,8 @@ int64_t oracle_cache_append(int32_t B, int32_t s_q, int32_t kind, const uint16_t
                             int64_t num_blocks, void* kv, void* scales);
 void oracle_quantize_q8_0_row(const float* x, int8_t* q, uint16_t* scales);
 void oracle_quantize_fp8_row(const float* x, uint8_t* q, float* scale);
+void oracle_quantize_q4h_row(const float* x, uint8_t* q, uint16_t* scales);
+void oracle_hadamard32(const double* x, double* y);
 
 static uint64_t state = 0x9e3779b97f4a7c15ull;
 static uint32_t next_u32(void) {   /* xorshift64*: any deterministic filler will do */
@@ -89,19 +91,27 @@ int main(void) {
   uint16_t* sc16 = xmalloc(sizeof(uint16_t) * NBLK * BT * (D_K / 32));
   uint8_t* kvf8 = xmalloc((size_t)NBLK * BT * D_K);
   float* sc32 = xmalloc(sizeof(float) * NBLK * BT);
+  uint8_t* kv4 = xmalloc((size_t)NBLK * BT * (D_K / 2));
+  uint16_t* sc4 = xmalloc(sizeof(uint16_t) * NBLK * BT * (D_K / 32));
   float row[D_K];
   for (int64_t r = 0; r < (int64_t)NBLK * BT; ++r) {
     for (int e = 0; e < D_K; ++e) row[e] = next_f();
     if (r == 5) memset(row, 0, sizeof(row));    /* an all-zero row: scale 0 */
     oracle_quantize_q8_0_row(row, kv8 + r * D_K, sc16 + r * (D_K / 32));
     oracle_quantize_fp8_row(row, kvf8 + r * D_K, sc32 + r);
+    oracle_quantize_q4h_row(row, kv4 + r * (D_K / 2), sc4 + r * (D_K / 32));
+  }
+  {
+    double hx[32], hy[32];
+    for (int j = 0; j < 32; ++j) hx[j] = next_f();
+    oracle_hadamard32(hx, hy);
   }
   double* out = xmalloc(sizeof(double) * rows * D_L);
   double* lse = xmalloc(sizeof(double) * rows);
   double* oabs = xmalloc(sizeof(double) * rows * D_L);
-  const void* kvs[3] = {kv16, kv8, kvf8};
-  const void* scs[3] = {NULL, sc16, sc32};
-  for (int kind = 0; kind < 3; ++kind) {
+  const void* kvs[4] = {kv16, kv8, kvf8, kv4};
+  const void* scs[4] = {NULL, sc16, sc32, sc4};
+  for (int kind = 0; kind < 4; ++kind) {
     if (oracle_decode_absorbed(B, S_Q, H, q, kind, kvs[kind], scs[kind], NBLK, table, MAXB, seqlens,
                                0.07, NULL, 0, out, lse) != 0)
       return 3;
@@ -154,13 +164,14 @@ int main(void) {
    * are skipped */
   uint16_t* new_rows = xmalloc(sizeof(uint16_t) * B * S_Q * D_K);
   for (int i = 0; i < B * S_Q * D_K; ++i) new_rows[i] = next_bf16();
-  void* kv_app[3] = {kv16, kv8, kvf8};
-  void* sc_app[3] = {NULL, sc16, sc32};
-  for (int kind = 0; kind < 3; ++kind)
+  void* kv_app[4] = {kv16, kv8, kvf8, kv4};
+  void* sc_app[4] = {NULL, sc16, sc32, sc4};
+  for (int kind = 0; kind < 4; ++kind)
     (void)oracle_cache_append(B, S_Q, kind, new_rows, table, MAXB, seqlens, NBLK, kv_app[kind],
                               sc_app[kind]);
 
-  free(q); free(kv16); free(kv8); free(sc16); free(kvf8); free(sc32); free(out); free(lse);
+  free(q); free(kv16); free(kv8); free(sc16); free(kvf8); free(sc32); free(kv4); free(sc4);
+  free(out); free(lse);
   free(oabs); free(qn); free(qr); free(wk); free(wv); free(qa); free(o); free(ol); free(po);
   free(new_rows);
   printf("oracle sanitizer run: ok\n");

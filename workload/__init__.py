@@ -75,6 +75,7 @@ def _load():
         lib.gen_scale_rows_bf16.argtypes = [vp, i64, i64, vp, ctypes.c_float]
         lib.gen_quantize_q8_0.argtypes = [vp, i64, i32, vp, vp]
         lib.gen_quantize_fp8.argtypes = [vp, i64, i32, vp, vp]
+        lib.gen_quantize_q4_0.argtypes = [vp, i64, i32, vp, vp]
         _lib = lib
     return _lib
 
@@ -142,6 +143,18 @@ def quantize_q8_0(x: np.ndarray):
     return q, d
 
 
+def quantize_q4_0(x: np.ndarray):
+    """q4_0 block writer on float32 rows of 576 -> (uint8 codes [.., 288], fp16-bit
+    scales [.., 18]); the values stand for the rotated blocks of a q4_0 cache in
+    Hadamard rotation."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows = x.size // D_K
+    q = np.empty(x.shape[:-1] + (D_K // 2,), np.uint8)
+    d = np.empty(x.shape[:-1] + (Q8_GROUPS,), np.uint16)
+    _load().gen_quantize_q4_0(_ptr(x), rows, D_K, _ptr(q), _ptr(d))
+    return q, d
+
+
 def quantize_fp8(x: np.ndarray):
     """fp8 (E4M3) cache writer on float32 rows of 576 -> (uint8 rows, float32 scale per row)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -162,10 +175,11 @@ class Workload:
     seqlens: np.ndarray            # int32 [B]
     block_table: np.ndarray        # int32 [B, max_blocks], -1 = unused slot
     q: np.ndarray                  # uint16 bf16 bits [B, s_q, H, 576]
-    kv: np.ndarray                 # uint16 bf16 bits, int8 or uint8 fp8, [num_blocks, 64, 576]
-    kv_scales: Optional[np.ndarray]  # uint16 fp16 bits [num_blocks, 64, 18] (q8_0),
+    kv: np.ndarray                 # uint16 bf16 bits, int8 or uint8 fp8, [num_blocks, 64, 576],
+    #                                or uint8 q4_0 codes [num_blocks, 64, 288] (q4_0h)
+    kv_scales: Optional[np.ndarray]  # uint16 fp16 bits [num_blocks, 64, 18] (q8_0, q4_0h),
     #                                  float32 [num_blocks, 64] (fp8) or None
-    kv_dtype: str                  # "bf16" | "q8_0" | "fp8"
+    kv_dtype: str                  # "bf16" | "q8_0" | "fp8" | "q4_0h"
     softmax_scale: float = SOFTMAX_SCALE
     seed: int = 0
     recipe: dict = field(default_factory=dict)
@@ -239,6 +253,11 @@ def make_workload(name: str, B: int, s_q: int, H: int, seqlens, *, seed: int,
         x = normal_f32(n_el, seed, S_KV).reshape(pool, BLOCK_TOKENS, D_K)
         kv, scales = quantize_fp8(x)
         del x
+    elif kv_dtype == "q4_0h":
+        # the rotated blocks of N(0,1) rows are N(0,1) values (see gen.c)
+        x = normal_f32(n_el, seed, S_KV).reshape(pool, BLOCK_TOKENS, D_K)
+        kv, scales = quantize_q4_0(x)
+        del x
     else:
         raise ValueError(kv_dtype)
     recipe = dict(seed=seed, table=table, kv_dtype=kv_dtype, outlier_frac=outlier_frac,
@@ -262,6 +281,9 @@ CONFIGS = {
     # the DeepSeek-V3 shape over an fp8 (E4M3, per-token fp32 scale) cache
     6: dict(name="fp8_b64_h128_l4096", B=64, s_q=1, H=128, seqlens=4096, table="sequential",
             kv_dtype="fp8"),
+    # the q8_0 workload's shape over a q4_0 cache stored in Hadamard rotation
+    7: dict(name="q4h_b64_h128_l8192", B=64, s_q=1, H=128, seqlens=8192, table="sequential",
+            kv_dtype="q4_0h"),
 }
 
 
@@ -276,11 +298,13 @@ def config_flops_bytes(w: Workload):
     """Algorithmic work of one decode call: (bytes, flops, visible_token_rows).
 
     Bytes: every cached token row that some query can see, read once per
-    sequence (1152 B bf16, 576 + 36 B q8_0 or 576 + 4 B fp8), plus q, out (bf16) and lse
+    sequence (1152 B bf16, 576 + 36 B q8_0, 576 + 4 B fp8 or 288 + 36 B q4_0h), plus q,
+    out (bf16) and lse
     (fp32) per query row, plus the block-table entries and seqlens read.
     Flops: 2*576 (scores) + 2*512 (value product) per visible (token, row).
     """
-    per_tok = {"bf16": D_K * 2, "q8_0": D_K + Q8_GROUPS * 2, "fp8": D_K + 4}[w.kv_dtype]
+    per_tok = {"bf16": D_K * 2, "q8_0": D_K + Q8_GROUPS * 2, "fp8": D_K + 4,
+               "q4_0h": D_K // 2 + Q8_GROUPS * 2}[w.kv_dtype]
     L = np.clip(w.seqlens.astype(np.int64), 0, w.max_blocks * BLOCK_TOKENS)
     kv_bytes = int(L.sum()) * per_tok
     nblk = (L + BLOCK_TOKENS - 1) // BLOCK_TOKENS

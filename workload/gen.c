@@ -3,8 +3,8 @@
  *
  * This module serves both the CPU oracle and the GPU library's tests and
  * benchmark. It holds no attention arithmetic: only random numbers, the
- * storage roundings of the input formats (bf16, fp16) and the q8_0 cache
- * writer that produces a quantized latent cache from float values.
+ * storage roundings of the input formats (bf16, fp16) and the cache writers
+ * (q8_0, fp8, q4_0) that produce a quantized latent cache from float values.
  *
  * Random numbers come from one counter-based generator: output i of stream
  * (seed, stream) is the splitmix64 finaliser applied to key + (i+1)*gamma,
@@ -246,5 +246,38 @@ void gen_quantize_fp8(const float* x, int64_t rows, int32_t cols, uint8_t* q, fl
     const float d = amax / 448.0f;
     scale[r] = d;
     for (int32_t k = 0; k < cols; ++k) q[r * cols + k] = d > 0.0f ? f32_to_e4m3_rne(xs[k] / d) : 0;
+  }
+}
+
+/*
+ * q4_0 block writer: every 32 floats get one fp16 scale d = m / -8 (m the
+ * first value of largest magnitude) and 4-bit codes min(15, floor(x / d + 8.5))
+ * (all 8 when d = 0), two per byte (code j of block g in byte 16 g + j / 2,
+ * low nibble for even j). The values it is given stand for the rotated
+ * blocks of a cache stored in Hadamard rotation: the rotation of independent
+ * normal values is again independent normal values, so the generator draws
+ * the rotated values directly and never rotates anything.
+ */
+void gen_quantize_q4_0(const float* x, int64_t rows, int32_t cols, uint8_t* q, uint16_t* d16) {
+  const int32_t groups = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int32_t g = 0; g < groups; ++g) {
+      const float* xs = x + r * cols + g * 32;
+      float m = 0.0f;
+      for (int k = 0; k < 32; ++k)
+        if (fabsf(xs[k]) > fabsf(m)) m = xs[k];
+      const float d = m / -8.0f;
+      d16[r * groups + g] = f32_to_fp16_rne(d);
+      uint8_t* qs = q + r * (cols / 2) + g * 16;
+      for (int k = 0; k < 32; k += 2) {
+        int c[2];
+        for (int h = 0; h < 2; ++h) {
+          const float t = d != 0.0f ? floorf(xs[k + h] / d + 8.5f) : 8.0f;
+          c[h] = t > 15.0f ? 15 : (int)t;
+        }
+        qs[k / 2] = (uint8_t)(c[0] | (c[1] << 4));
+      }
+    }
   }
 }
