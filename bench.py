@@ -50,13 +50,16 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=WORKLOAD_CFG,
-                    help="workload index 1..5 (6: the bench shape over an fp8 cache)")
+                    help="workload index 1..5 (6: the bench shape over an fp8 cache; 7: the "
+                         "q8_0 workload's shape over a q4_0 cache in Hadamard rotation)")
     ap.add_argument("--num-parts", type=int, default=0)
     ap.add_argument("--m-tile", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay the steps from HIP graphs instead of launching each from Python")
-    ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle sample")
+    ap.add_argument("--cpu-seqs", type=int, default=0,
+                    help="sequences in the oracle sample (0: 64, or 2 for the q4_0 cache, "
+                         "whose rows the oracle rotates back from the matrix entries)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration and "
                          "measured copy bandwidth)")
@@ -313,7 +316,8 @@ def main():
     out = torch.empty((w.B, w.s_q, w.H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.s_q, w.H), dtype=torch.float32, device=dev)
     prob = mla.make_problem(q, kv0, bt, kv_dtype={"bf16": mla.KV_BF16, "q8_0": mla.KV_Q8_0,
-                                                  "fp8": mla.KV_FP8}[w.kv_dtype],
+                                                  "fp8": mla.KV_FP8,
+                                                  "q4_0h": mla.KV_Q4_0H}[w.kv_dtype],
                             max_seqlen=w.max_seqlen, num_parts=args.num_parts,
                             m_tile=args.m_tile)
     ws = torch.empty(max(16, mla.workspace_size(prob)), dtype=torch.uint8, device=dev)
@@ -405,7 +409,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "q8_0": "q8_0 cache, bf16 MFMA",
-                  "fp8": "fp8 (e4m3) cache, bf16 MFMA"}[w.kv_dtype],
+                  "fp8": "fp8 (e4m3) cache, bf16 MFMA",
+                  "q4_0h": "q4_0 cache in Hadamard rotation, bf16 MFMA"}[w.kv_dtype],
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seqlen": seqlen_desc,
                    "seqlen_q": w.s_q, "kv_cache": f"{w.kv_dtype}, paged 64-token blocks, "
@@ -422,7 +427,8 @@ def main():
     if mfma_counters:
         res["roofline"]["mfma_counters"] = mfma_counters
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs)
+        n_cpu = args.cpu_seqs or (2 if w.kv_dtype == "q4_0h" else 64)
+        res["cpu_baseline"] = cpu_baseline(w, n_cpu)
     print(json.dumps(res), flush=True)
 
 

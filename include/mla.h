@@ -23,7 +23,9 @@
  * space; applying W_UV and W_O is the caller's business. No per-head K or V
  * is ever built. This is exact softmax attention evaluated FlashAttention-
  * style (FlashMLA page of the ik_llama.cpp docs, "What is MLA?"); the
- * optional q8_0 cache follows "KV cache with MLA" on the same page.
+ * optional q8_0 cache follows "KV cache with MLA" on the same page, and so
+ * does the q4_0 cache whose keys are Hadamard-transformed before
+ * quantisation (there the option recommended below 6-bit caches).
  *
  * Layouts (all row-major and contiguous):
  *   q            bf16  [B, s_q, H, 576]        query row r = i*H + h of sequence b
@@ -34,6 +36,15 @@
  *                uint8 [num_blocks, 64, 576]   (MLA_KV_FP8: OCP e4m3, 1-4-3, bias 7) with
  *   kv_scales    fp32  [num_blocks, 64]        one scale per token; a cached value
  *                                              is scale * e4m3 (576 + 4 bytes a token)
+ *                uint8 [num_blocks, 64, 288]   (MLA_KV_Q4_0H: 4-bit codes, two per
+ *                                              byte, code j of block g in byte
+ *                                              16 g + j / 2, low nibble for even j) with
+ *   kv_scales    fp16  [num_blocks, 64, 18]    block g = columns 32g .. 32g+31 holds
+ *                                              y = d_g * (code - 8) and stands for the
+ *                                              cached values R y, R = H / sqrt(32), H
+ *                                              the 32-point Sylvester-Hadamard matrix
+ *                                              (H[m][j] = (-1)^popcount(m & j)); R is
+ *                                              its own inverse (288 + 36 bytes a token)
  *   block_table  int32 [B, max_blocks_per_seq] token t of sequence b is row t % 64
  *                                              of block block_table[b][t / 64]
  *   seqlens      int32 [B]                     cached tokens of sequence b,
@@ -92,7 +103,7 @@ typedef enum {
   MLA_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
 } mla_status;
 
-typedef enum { MLA_KV_BF16 = 0, MLA_KV_Q8_0 = 1, MLA_KV_FP8 = 2 } mla_kv_dtype;
+typedef enum { MLA_KV_BF16 = 0, MLA_KV_Q8_0 = 1, MLA_KV_FP8 = 2, MLA_KV_Q4_0H = 3 } mla_kv_dtype;
 
 /* Problem descriptor (host struct, read during a call only). */
 typedef struct {
@@ -108,9 +119,10 @@ typedef struct {
   int32_t num_parts;          /* 0: automatic; else P >= 1 KV partitions (see mla_plan) */
   int32_t m_tile;             /* 0: automatic; else 16, 32, 64 or 128 query rows
                                  per workgroup (16: bf16 cache only; fp8 cache:
-                                 128 only). Automatic picks the smallest tile
-                                 that holds seqlen_q * num_heads rows (16 only
-                                 for bf16), else 128; always 128 for fp8. */
+                                 128 only; q4_0 cache: 32 or 64 only). Automatic
+                                 picks the smallest tile that holds
+                                 seqlen_q * num_heads rows (16 only for bf16),
+                                 else 128 (q4_0: 64); always 128 for fp8. */
 } mla_problem;
 
 /* Bytes of device workspace mla_decode needs for *p (written to *bytes, host).
@@ -233,7 +245,15 @@ mla_status mla_project_output(int64_t rows, int32_t num_heads, const void* o_lat
  *   MLA_KV_FP8: kv_cache uint8 [num_blocks, 64, 576] + kv_scales fp32 [num_blocks, 64]:
  *     one scale per token, d = max |x| / 448 (fp32, stored as is), code = OCP E4M3
  *     of x / d, nearest even, saturated to +-448 (the forum's fp8 KV cache,
- *     snowgate.dev thread 35); max |x| = 0 gives scale 0 and codes 0.
+ *     snowgate.dev thread 35); max |x| = 0 gives scale 0 and codes 0;
+ *   MLA_KV_Q4_0H: kv_cache uint8 [num_blocks, 64, 288] + kv_scales fp16
+ *     [num_blocks, 64, 18]: each block g of 32 columns is rotated by the
+ *     Hadamard matrix before it is quantised (FlashMLA page, "KV cache with
+ *     MLA", the K-cache Hadamard option for low-bit caches), in fp32: the fast
+ *     transform (for strides 1, 2, 4, 8, 16 every pair (a, b) -> (a + b, a - b)),
+ *     then each value times fp32(1 / sqrt(32)); then q4_0: m = the first value
+ *     of largest magnitude, d = m / -8, code = min(15, floor(y / d + 8.5)) (all
+ *     codes 8 when d = 0), scale = fp16(d) to nearest even.
  * rows must be finite.
  * rows and kv_cache 16-byte aligned, the other arrays 4-byte. Two new rows
  * aimed at the same slot race. */

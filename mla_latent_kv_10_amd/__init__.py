@@ -17,7 +17,7 @@ import torch
 from ._build import LIB_PATH, build  # noqa: F401
 
 D_LATENT, D_ROPE, D_K, BLOCK_TOKENS = 512, 64, 576, 64
-KV_BF16, KV_Q8_0, KV_FP8 = 0, 1, 2
+KV_BF16, KV_Q8_0, KV_FP8, KV_Q4_0H = 0, 1, 2, 3
 MAX_BATCH, MAX_ROWS = 2048, 4096
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
@@ -125,20 +125,30 @@ def _require(t: torch.Tensor, name: str, dtype, ndim: int):
 
 
 def _cache_kind(kv_cache: torch.Tensor) -> int:
-    """bf16 -> KV_BF16, int8 -> KV_Q8_0, uint8 -> KV_FP8 (E4M3 bytes)."""
+    """bf16 -> KV_BF16, int8 -> KV_Q8_0, uint8 rows of 576 -> KV_FP8 (E4M3 bytes),
+    uint8 rows of 288 -> KV_Q4_0H (q4_0 codes in Hadamard rotation)."""
     kinds = {torch.bfloat16: KV_BF16, torch.int8: KV_Q8_0, torch.uint8: KV_FP8}
     if not isinstance(kv_cache, torch.Tensor) or kv_cache.dtype not in kinds:
-        raise TypeError("kv_cache must be a bfloat16, int8 (q8_0) or uint8 (fp8 E4M3) tensor")
+        raise TypeError("kv_cache must be a bfloat16, int8 (q8_0) or uint8 (fp8 E4M3 or "
+                        "q4_0 codes) tensor")
     _require(kv_cache, "kv_cache", kv_cache.dtype, 3)
+    if kv_cache.dtype == torch.uint8 and kv_cache.shape[-1] == D_K // 2:
+        return KV_Q4_0H
     return kinds[kv_cache.dtype]
+
+
+def _check_cache_shape(kind: int, kv_cache: torch.Tensor):
+    width = D_K // 2 if kind == KV_Q4_0H else D_K
+    if tuple(kv_cache.shape[1:]) != (BLOCK_TOKENS, width):
+        raise ValueError(f"kv_cache must be [num_blocks, 64, {width}]")
 
 
 def _check_scales(kind: int, kv_cache: torch.Tensor, kv_scales):
     if kind == KV_BF16:
         return
     if kv_scales is None:
-        raise ValueError("kv_scales is required for a quantised (q8_0 or fp8) cache")
-    if kind == KV_Q8_0:
+        raise ValueError("kv_scales is required for a quantised (q8_0, fp8 or q4_0) cache")
+    if kind in (KV_Q8_0, KV_Q4_0H):
         _require(kv_scales, "kv_scales", torch.float16, 3)
         if tuple(kv_scales.shape) != (kv_cache.shape[0], BLOCK_TOKENS, D_K // 32):
             raise ValueError("kv_scales must be [num_blocks, 64, 18]")
@@ -155,8 +165,7 @@ def _decode_args(q, kv_cache, block_table, seqlens, out, lse, kv_scales, workspa
     if q.shape[-1] != D_K:
         raise ValueError("q rows must be 576 wide")
     kind = _cache_kind(kv_cache)
-    if tuple(kv_cache.shape[1:]) != (BLOCK_TOKENS, D_K):
-        raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    _check_cache_shape(kind, kv_cache)
     _check_scales(kind, kv_cache, kv_scales)
     _require(block_table, "block_table", torch.int32, 2)
     _require(seqlens, "seqlens", torch.int32, 1)
@@ -193,8 +202,9 @@ def mla_decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     """Decode step over a paged latent cache (see include/mla.h).
 
     q bf16 [B, s_q, H, 576]; kv_cache bf16 [nb, 64, 576], int8 (q8_0, with
-    kv_scales float16 [nb, 64, 18]) or uint8 (fp8 E4M3, with kv_scales
-    float32 [nb, 64]); block_table int32 [B, max_blocks];
+    kv_scales float16 [nb, 64, 18]), uint8 (fp8 E4M3, with kv_scales
+    float32 [nb, 64]) or uint8 [nb, 64, 288] (q4_0 codes in Hadamard rotation,
+    with kv_scales float16 [nb, 64, 18]); block_table int32 [B, max_blocks];
     seqlens int32 [B] (device). Returns (out bf16 [B, s_q, H, 512],
     lse float32 [B, s_q, H]). Runs on the current stream; never synchronises.
     """
@@ -348,7 +358,9 @@ def mla_cache_append(rows: torch.Tensor, block_table: torch.Tensor, seqlens: tor
                      kv_cache: torch.Tensor, kv_scales: Optional[torch.Tensor] = None) -> None:
     """Write the new rows (bf16 [B, s_q, 576]) of a decode step into the paged
     cache in place: bf16 [nb, 64, 576], int8 q8_0 with kv_scales float16
-    [nb, 64, 18], or uint8 fp8 with kv_scales float32 [nb, 64] (include/mla.h)."""
+    [nb, 64, 18], uint8 fp8 with kv_scales float32 [nb, 64], or uint8 q4_0 codes
+    [nb, 64, 288] in Hadamard rotation with kv_scales float16 [nb, 64, 18]
+    (include/mla.h)."""
     _require(rows, "rows", torch.bfloat16, 3)
     if rows.shape[-1] != D_K:
         raise ValueError("rows must be [B, s_q, 576]")
@@ -356,8 +368,7 @@ def mla_cache_append(rows: torch.Tensor, block_table: torch.Tensor, seqlens: tor
     _require(block_table, "block_table", torch.int32, 2)
     _require(seqlens, "seqlens", torch.int32, 1)
     kind = _cache_kind(kv_cache)
-    if tuple(kv_cache.shape[1:]) != (BLOCK_TOKENS, D_K):
-        raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    _check_cache_shape(kind, kv_cache)
     _check_scales(kind, kv_cache, kv_scales)
     if block_table.shape[0] != B or seqlens.shape[0] != B:
         raise ValueError("block_table and seqlens must have B rows")

@@ -59,6 +59,12 @@ constexpr int kQ8ScaleRowBytes = 36;
 constexpr int kQ8TileBytes = kTile * kQ8RowBytes;               // 18432
 constexpr int kQ8ScaleTileBytes = kTile * kQ8ScaleRowBytes;     // 1152
 constexpr int kQ8StageBytes = kQ8TileBytes + 2048;              // int8 + scales, padded
+// q4_0 tiles in Hadamard rotation: 32 rows x 288 code bytes plus the same
+// 32 x 18 fp16 scales; code block g of token t is 16-byte unit 32 g + t
+constexpr int kQ4RowBytes = kDK / 2;        // 288
+constexpr int kQ4TileBytes = kTile * kQ4RowBytes;               // 9216
+constexpr int kQ4StageBytes = kQ4TileBytes + 2048;              // codes + scales, padded
+constexpr float kInvSqrt32 = 0.17677669529663688f;               // 1 / sqrt(32)
 // fp8 (e4m3) tiles: 32 rows x 576 bytes plus 32 fp32 per-token scales
 constexpr int kFp8TileBytes = kTile * kDK;                      // 18432
 constexpr int kFp8StageBytes = kFp8TileBytes + 1024;            // fp8 + scales, padded
@@ -292,13 +298,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Decode kernel with the work of each 32-row group split over CG waves (the
-// q8_0 cache: HG = 1 or 2 row groups, CG = 4). The 576-column score
+// q8_0 cache and the q4_0 cache in Hadamard rotation: HG = 1 or 2 row groups,
+// CG = 4). The 576-column score
 // contraction is split by columns (partial scores summed through LDS) and the
 // 512-wide value product by output columns. q8_0: the scores are exact (the
 // int8 values are exact in bf16; each 32-column group's partial sum is scaled
 // by its fp16 scale in fp32), and the value product reads an LDS tile of
 // bf16(scale * int8) written once per tile by all threads.
-template <int HG, int CG, bool Q8>
+// Q4 (with Q8): the cache holds, per 32-column block of a row, the q4_0 codes
+// of the row's block rotated by R = H / sqrt(32) (H the 32-point
+// Sylvester-Hadamard matrix, R its own inverse), so a cached block is
+// x = R y = (d / sqrt(32)) H (c - 8). Once per tile all waves form
+// n = H (c - 8) for every block of every token on the matrix core (H times
+// the tile's codes: integers of magnitude <= 256, exact in bf16 and in the
+// fp32 accumulators) into an LDS tile of bf16 n that the score steps read
+// in place of the int8 values, the per-group scale being d; 1 / sqrt(32) is
+// folded into the softmax scale by the host. The value tile is
+// bf16(d / sqrt(32) * n).
+template <int HG, int CG, bool Q8, bool Q4 = false>
 __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParams a) {
   constexpr int NW = HG * CG;             // waves per workgroup
   constexpr int NT = 64 * NW;             // threads
@@ -307,14 +324,20 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
   constexpr int NCT = 16 / CG;            // 32-column output tiles per wave
   constexpr int SL = 16 / CG;             // score registers of this wave's slice
   constexpr int REC = SL / 2 + 2 <= 4 ? 4 : 8;   // dwords per lane in a slice record
-  constexpr int TILE_LOADS = Q8 ? 20 : 36;  // 1 KiB LDS-DMA loads per tile
-  constexpr int STAGE_BYTES = Q8 ? kQ8StageBytes : kTileBytes;
+  // 1 KiB LDS-DMA loads per tile: code loads, then two of scales (quantised)
+  constexpr int CODE_LOADS = Q4 ? 9 : (Q8 ? 18 : 36);
+  constexpr int TILE_LOADS = Q8 ? CODE_LOADS + 2 : 36;
+  constexpr int STAGE_BYTES = Q4 ? kQ4StageBytes : (Q8 ? kQ8StageBytes : kTileBytes);
+  constexpr int SCALE_OFF = Q4 ? kQ4TileBytes : kQ8TileBytes;   // scales in a stage
   constexpr int MAX_LOADS = (TILE_LOADS + NW - 1) / NW;
   static_assert(36 % CG == 0 && 16 % CG == 0 && SL % 4 == 0, "bad split");
+  static_assert(!Q4 || Q8, "the q4_0 path is a variant of the quantised path");
 
   __shared__ __attribute__((aligned(1024))) uint8_t s_stage[kStages][STAGE_BYTES];
   // q8_0: dequantised value tile (columns 0..511, bf16, tile_unit layout)
   __shared__ __attribute__((aligned(1024))) uint8_t s_deq[Q8 ? kTile * kDL * 2 : 16];
+  // q4_0: n = H (c - 8) of the tile as bf16 (576 columns, tile_unit layout)
+  __shared__ __attribute__((aligned(1024))) uint8_t s_nt[Q4 ? kTile * kDK * 2 : 16];
   // partial scores per wave: bf16 path [4][64] x f32x4 in accumulator order;
   // q8_0 path as a padded 32 x 33 [head][token] matrix for the transpose
   __shared__ __attribute__((aligned(16))) float s_sx[(CG > 1 || Q8) ? NW : 1][Q8 ? 32 * 33 : 16 * 64];
@@ -394,6 +417,8 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
   // 2k+1 (lanes 32..63); lane position l32 of chunk c holds token
   // l32 ^ 4(c & 3). q8_0: loads 0..17 fill the int8 rows chunk-major in
   // 16-column units (unit 32c' + t), loads 18..19 the 1152 bytes of scales.
+  // q4_0: loads 0..8 fill the code rows block-major (unit 32g + t holds the
+  // 32 codes of block g of token t), loads 9..10 the scales.
   uint32_t doff[MAX_LOADS];
 #pragma unroll
   for (int j = 0; j < MAX_LOADS; ++j) {
@@ -402,9 +427,21 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
     if constexpr (!Q8) {
       doff[j] = (uint32_t)((l32 ^ (4 * (c & 3))) * kRowBytes + c * 16);
     } else {
-      const int off = (k - 18) * 1024 + lane * 16;
-      doff[j] = k < 18 ? (uint32_t)(l32 * kQ8RowBytes + c * 16)
-                       : (uint32_t)(off < kQ8ScaleTileBytes ? off : 0);
+      constexpr int RB = Q4 ? kQ4RowBytes : kQ8RowBytes;
+      const int off = (k - CODE_LOADS) * 1024 + lane * 16;
+      doff[j] = k < CODE_LOADS ? (uint32_t)(l32 * RB + c * 16)
+                               : (uint32_t)(off < kQ8ScaleTileBytes ? off : 0);
+    }
+  }
+  // q4_0: A operand of the Hadamard product, H[m][k] for this lane's row
+  // m = l32 and columns k = 8 hi + e (first MFMA) and 16 + 8 hi + e (second)
+  bf16x8 hA0, hA1;
+  if constexpr (Q4) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k0 = 8 * hi + e;
+      hA0[e] = (__bf16)((__builtin_popcount(l32 & k0) & 1) ? -1.f : 1.f);
+      hA1[e] = (__bf16)((__builtin_popcount(l32 & (k0 + 16)) & 1) ? -1.f : 1.f);
     }
   }
 
@@ -467,16 +504,17 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
           if (k < TILE_LOADS) dma16_sbase(src, doff[j], dst + k * 1024);
         }
       } else {
-        const uint8_t* src = a.kv + (phys * kBT + (tt & 1) * kTile) * kQ8RowBytes;
+        constexpr int RB = Q4 ? kQ4RowBytes : kQ8RowBytes;
+        const uint8_t* src = a.kv + (phys * kBT + (tt & 1) * kTile) * RB;
         const uint8_t* ssrc =
             a.kv_scales + (phys * kBT + (tt & 1) * kTile) * kQ8ScaleRowBytes;
 #pragma unroll
         for (int j = 0; j < MAX_LOADS; ++j) {
           const int k = wave + NW * j;
-          if (k < 18)
+          if (k < CODE_LOADS)
             dma16_sbase(src, doff[j], dst + k * 1024);
           else if (k < TILE_LOADS)
-            dma16_sbase(ssrc, doff[j], dst + kQ8TileBytes + (k - 18) * 1024);
+            dma16_sbase(ssrc, doff[j], dst + SCALE_OFF + (k - CODE_LOADS) * 1024);
         }
       }
     };
@@ -507,13 +545,14 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
             *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       } else {
-        for (int u = tid; u < kTile * 36; u += NT) {
+        // q4_0: zero codes still mean -8; the zeroed scales make the values 0
+        for (int u = tid; u < kTile * (Q4 ? 18 : 36); u += NT) {
           if ((u & 31) >= valid)
             *reinterpret_cast<LDS_AS f32x4*>(st + 16 * u) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         for (int t = valid + tid; t < kTile; t += NT) {
           LDS_AS uint32_t* srow =
-              reinterpret_cast<LDS_AS uint32_t*>(st + kQ8TileBytes + t * kQ8ScaleRowBytes);
+              reinterpret_cast<LDS_AS uint32_t*>(st + SCALE_OFF + t * kQ8ScaleRowBytes);
 #pragma unroll
           for (int e = 0; e < kQ8ScaleRowBytes / 4; ++e) srow[e] = 0u;
         }
@@ -526,6 +565,48 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
       // registers i in [SL cg, SL cg + SL), token t0 + 8(i>>2) + 4hi + (i&3)
       float tot[SL];
       if constexpr (Q8) {
+      if constexpr (Q4) {
+        // n = H (c - 8) for block g of all 32 tokens: two MFMAs (k = code
+        // index 0..15, 16..31) of H rows against the codes as bf16(128 + c)
+        // (bits 0x4300 | c), which adds 136 * sum_k H[m][k] = 4352 to row
+        // m = 0 only; that is taken off. Lane (t, hi) then holds n[m][t] for
+        // m = 8 q + 4 hi + (0..3), i.e. bf16 bytes 8 hi .. 8 hi + 7 of
+        // chunk 4 g + q of token t in the n tile, and (g < 16) the same
+        // positions of the value tile as bf16(d / sqrt(32) * n).
+        auto nib8 = [](uint32_t w) {
+          u32x4 r;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            r[k] = ((w >> (8 * k)) & 0xFu) | (((w >> (8 * k + 4)) & 0xFu) << 16) | 0x43004300u;
+          return __builtin_bit_cast(bf16x8, r);
+        };
+        LDS_AS uint8_t* nt = (LDS_AS uint8_t*)s_nt;
+        LDS_AS uint8_t* dq = (LDS_AS uint8_t*)s_deq;
+        for (int g = wave; g < 18; g += NW) {
+          const LDS_AS uint8_t* cu = st + 16 * (32 * g + l32);
+          const uint32_t w0 = *reinterpret_cast<const LDS_AS uint32_t*>(cu + 4 * hi);
+          const uint32_t w1 = *reinterpret_cast<const LDS_AS uint32_t*>(cu + 8 + 4 * hi);
+          const uint16_t sbits = *reinterpret_cast<const LDS_AS uint16_t*>(
+              st + SCALE_OFF + l32 * kQ8ScaleRowBytes + 2 * g);
+          const float dv = (float)__builtin_bit_cast(_Float16, sbits) * kInvSqrt32;
+          const f32x16 zero = {};
+          f32x16 n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA0, nib8(w0), zero, 0, 0, 0);
+          n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA1, nib8(w1), n, 0, 0, 0);
+          if (hi == 0) n[0] -= 4352.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int u = 16 * tile_unit(l32, 4 * g + q) + 8 * hi;
+            *reinterpret_cast<LDS_AS uint64_t*>(nt + u) =
+                (uint64_t)pack_bf16x2(n[4 * q], n[4 * q + 1]) |
+                ((uint64_t)pack_bf16x2(n[4 * q + 2], n[4 * q + 3]) << 32);
+            if (g < 16)
+              *reinterpret_cast<LDS_AS uint64_t*>(dq + u) =
+                  (uint64_t)pack_bf16x2(dv * n[4 * q], dv * n[4 * q + 1]) |
+                  ((uint64_t)pack_bf16x2(dv * n[4 * q + 2], dv * n[4 * q + 3]) << 32);
+          }
+        }
+        lds_barrier();   // every wave's blocks of the n tile are written
+      } else {
         // Value tile: bf16(scale * int8) for columns 0..511.
         LDS_AS uint8_t* dq = (LDS_AS uint8_t*)s_deq;
         for (int u = tid; u < kTile * (kDL / 8); u += NT) {
@@ -540,6 +621,7 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
           for (int e = 0; e < 8; ++e) vals[e] = (__bf16)(sc * (float)(int8_t)(raw >> (8 * e)));
           *reinterpret_cast<LDS_AS bf16x8*>(dq + 16 * tile_unit(t, c)) = vals;
         }
+      }
         // Exact scores: S (heads x tokens, one token per lane) on the int8
         // values themselves (exact in bf16), each 32-column group's partial
         // sum times that token's fp16 scale in fp32.
@@ -547,7 +629,7 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
         f32x16 snt;
 #pragma unroll
         for (int i = 0; i < 16; ++i) snt[i] = 0.f;
-        const LDS_AS uint8_t* srow = st + kQ8TileBytes + l32 * kQ8ScaleRowBytes;
+        const LDS_AS uint8_t* srow = st + SCALE_OFF + l32 * kQ8ScaleRowBytes;
         const LDS_AS uint8_t* kraw = st + (32 * cg * KS + l32) * 16 + 8 * hi;
         // The wave's k-steps s = cg KS + ks cover columns 16s .. 16s+15; a
         // group (32 columns) is k-steps 2g, 2g+1. PAR = parity of the wave's
@@ -560,9 +642,19 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
           constexpr int PAR = decltype(parc)::value;
           f32x16 acc[2];
           uint64_t raw[KS];
+          bf16x8 kq[KS];   // q4_0: the n-tile operands, read two k-steps ahead
           float dg[2] = {0.f, 0.f};
-          raw[0] = *reinterpret_cast<const LDS_AS uint64_t*>(kraw);
-          if constexpr (KS > 1) raw[1] = *reinterpret_cast<const LDS_AS uint64_t*>(kraw + 512);
+          auto rd4 = [&](int ks) {
+            return lds_read_b128((const LDS_AS uint8_t*)s_nt + 1024 * (cg * KS + ks) +
+                                 ((ks & 1) ? kofsB : kofsA));
+          };
+          if constexpr (Q4) {
+            kq[0] = rd4(0);
+            if constexpr (KS > 1) kq[1] = rd4(1);
+          } else {
+            raw[0] = *reinterpret_cast<const LDS_AS uint64_t*>(kraw);
+            if constexpr (KS > 1) raw[1] = *reinterpret_cast<const LDS_AS uint64_t*>(kraw + 512);
+          }
           auto scale_of = [&](int ks) {
             const uint16_t sbits = *reinterpret_cast<const LDS_AS uint16_t*>(
                 srow + ((cg * KS + ks) >> 1) * 2);
@@ -583,11 +675,19 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
           unroll<KS>([&](auto kc) {
             constexpr int ks = decltype(kc)::value;
             constexpr int buf = buf_of(ks);
-            if constexpr (ks + 2 < KS)
-              raw[ks + 2] = *reinterpret_cast<const LDS_AS uint64_t*>(kraw + 512 * (ks + 2));
+            if constexpr (ks + 2 < KS) {
+              if constexpr (Q4)
+                kq[ks + 2] = rd4(ks + 2);
+              else
+                raw[ks + 2] = *reinterpret_cast<const LDS_AS uint64_t*>(kraw + 512 * (ks + 2));
+            }
             bf16x8 kf;
+            if constexpr (Q4) {
+              kf = kq[ks];
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kf[e] = (__bf16)(float)(int8_t)(raw[ks] >> (8 * e));
+              for (int e = 0; e < 8; ++e) kf[e] = (__bf16)(float)(int8_t)(raw[ks] >> (8 * e));
+            }
             if constexpr (starts(ks)) {
               const f32x16 zero = {};
               acc[buf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf, zero, 0, 0, 0);
@@ -2031,55 +2131,60 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       }
     };
 
-    // The first block-id window, the query rows, then the first two tiles
-    // (ring stages 0, 1).
+    // The first block-id window and the query rows are loaded together; once
+    // the ids have landed, the first two tiles are issued into ring stages 0
+    // and 1 while the query rows are still in flight. The query rows then
+    // pass through ring stages 2 and 3 (idle until the third tile is issued),
+    // 18 KiB per wave, to be read back in the score operand layout.
     load_ids();
-    wait_vmcnt<0>();
-    check_ids();
     bf16x8 qf[36];
     if (n_run > 0) {
-      // Query rows of this wave: its 32 consecutive rows are one contiguous
-      // 36 KiB block, read as 36 contiguous KiB (lane l of load j takes the
-      // 16-byte chunk 64 j + l: row t = (64 j + l) / 72, chunk c = that mod
-      // 72), which the memory path serves much faster than loads spread over
-      // rows. Rows past M read row M-1 and are zeroed after the read. Each
-      // chunk is stored into the K-tile layout (unit 32 c + (t ^ 4 (c & 3)))
-      // of ring stage w (the ring is idle until the first tiles are issued)
-      // and read back in the score operand layout with the conflict-free
-      // fragment reads used for the K tiles.
+      // Query rows of this wave (32 rows, one contiguous 36 KiB block): load
+      // 4 C + R takes block (C, R) of the K-tile layout (rows 8R..8R+7,
+      // chunks 8C..8C+7) from eight whole 128-byte lines, each lane reading
+      // the unit it holds in that block, the placement of the cache copies,
+      // so that the LDS writes are contiguous and conflict-free. Rows past M
+      // read row M-1 and are zeroed after the read.
       const uint8_t* qblk = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * a.M * kDK);
       const int row0 = mt * MT + 32 * wave;
-      const int rmax = a.M - 1 - row0;          // last valid row of the block
-      u32x4 raw[36];
-      {
-        int t = 0, c = lane;
+      uint32_t qoff[4];
 #pragma unroll
-        for (int j = 0; j < 36; ++j) {
-          raw[j] = *reinterpret_cast<const u32x4*>(qblk + (int64_t)(row0 + min(t, rmax)) * kRowBytes + 16 * c);
-          c += 64;
-          if (c >= 72) { c -= 72; ++t; }
-        }
+      for (int R = 0; R < 4; ++R) {
+        const int dcq = dc0 | ((((lane >> 3) ^ R) & 1) << 1) | (((lane >> 5) & 1) << 2);
+        qoff[R] = (uint32_t)(min(row0 + 8 * R + dr, a.M - 1) * kRowBytes + 16 * dcq);
       }
-      {
-        LDS_AS uint8_t* stq = (LDS_AS uint8_t*)(s_ring + kTileBytes * wave);
-        int t = 0, c = lane;
+      u32x4 raw[36];
 #pragma unroll
-        for (int j = 0; j < 36; ++j) {
-          *reinterpret_cast<LDS_AS u32x4*>(stq + 16 * rg_unit(t, c)) = raw[j];
-          c += 64;
-          if (c >= 72) { c -= 72; ++t; }
-        }
-        const uint32_t sg = row_ok ? a.q_sign2 : 0u;
-        const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+      for (int C = 0; C < 9; ++C)
 #pragma unroll
-        for (int s2 = 0; s2 < 36; ++s2) {
-          const u32x4 z = __builtin_bit_cast(u32x4, lds_read_b128(stq + kstep_ofs(s2) + ((s2 & 1) ? kofs1 : kofs0)));
+        for (int R = 0; R < 4; ++R)
+          raw[4 * C + R] = *reinterpret_cast<const u32x4*>(qblk + qoff[R] + 128 * C);
+      asm volatile("" ::: "memory");
+      wait_vmcnt<36>();   // the ids have landed (loads complete in issue order)
+      check_ids();
+      issue(0);
+      issue(1);
+      // three passes of at most four column groups (16 KiB) each: write the
+      // blocks, read back the k-steps they hold (a wave's LDS operations
+      // complete in order, so a pass's writes follow the previous reads)
+      LDS_AS uint8_t* stq = (LDS_AS uint8_t*)(s_ring + 2 * kTileBytes + (kTileBytes / 2) * wave);
+      const uint32_t sg = row_ok ? a.q_sign2 : 0u;
+      const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass) {
+#pragma unroll
+        for (int C = 4 * pass; C < 4 * pass + 4 && C < 9; ++C)
+#pragma unroll
+          for (int R = 0; R < 4; ++R)
+            *reinterpret_cast<LDS_AS u32x4*>(stq + 1024 * (4 * (C - 4 * pass) + R) + 16 * lane) = raw[4 * C + R];
+#pragma unroll
+        for (int s2 = 16 * pass; s2 < 16 * pass + 16 && s2 < 36; ++s2) {
+          const u32x4 z = __builtin_bit_cast(
+              u32x4, lds_read_b128(stq + kstep_ofs(s2) - 16384 * pass + ((s2 & 1) ? kofs1 : kofs0)));
           qf[s2] = __builtin_bit_cast(bf16x8, (z ^ sg) & keep);
         }
       }
-      lds_barrier();   // every wave holds its query rows; the ring is free
-      issue(0);
-      issue(1);
+      lds_barrier();   // every wave holds its query rows; stages 2 and 3 are free
       // "tile -1" (value product before the first tile) reads the last
       // stage with P = 0: both are zero-filled so that it adds exact zeros
       for (int u = tid; u < STB / 16; u += NTH)
@@ -2088,6 +2193,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       s_p[wave][0][lane] = u32x4{0u, 0u, 0u, 0u};
       s_p[wave][1][lane] = u32x4{0u, 0u, 0u, 0u};
     } else {
+      wait_vmcnt<0>();
+      check_ids();
 #pragma unroll
       for (int s = 0; s < 36; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
@@ -3159,7 +3266,8 @@ mla_status validate_problem(const mla_problem* p) {
     return fail(MLA_ERR_UNSUPPORTED, "block table too large");
   if (p->num_blocks < 0) return fail(MLA_ERR_INVALID_ARG, "num_blocks must be >= 0");
   if (p->max_seqlen < 0) return fail(MLA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
-  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_Q8_0 && p->kv_dtype != MLA_KV_FP8)
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_Q8_0 && p->kv_dtype != MLA_KV_FP8 &&
+      p->kv_dtype != MLA_KV_Q4_0H)
     return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);
   if (p->num_parts < 0) return fail(MLA_ERR_INVALID_ARG, "num_parts must be >= 0");
   if (p->m_tile != 0 && p->m_tile != 16 && p->m_tile != 32 && p->m_tile != 64 &&
@@ -3182,28 +3290,35 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   // q8_0 cache: 32 or 64 rows, each row group's work split over 4 waves, or
   // 128 rows (the tile converted once into exact bf16 hi / lo parts). fp8
   // cache: 128 rows (the bf16 pipeline, its operands read as E4M3 codes and
-  // converted exactly in registers). More rows than one tile holds take
+  // converted exactly in registers). q4_0 cache in Hadamard rotation: 32 or
+  // 64 rows (the q8_0 kernel's work split). More rows than one tile holds take
   // several row tiles per KV part, placed on the same XCD so the second read
   // of each cache tile hits L2.
   const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
   const bool fp8 = p->kv_dtype == MLA_KV_FP8;
+  const bool q4 = p->kv_dtype == MLA_KV_Q4_0H;
   if (q8 && p->m_tile == 16)
     return fail(MLA_ERR_UNSUPPORTED, "m_tile %d is not available for the q8_0 cache", p->m_tile);
+  if (q4 && (p->m_tile == 16 || p->m_tile == 128))
+    return fail(MLA_ERR_UNSUPPORTED, "the q4_0 cache takes 32- or 64-row tiles only (m_tile %d)",
+                p->m_tile);
   if (fp8 && p->m_tile != 0 && p->m_tile != 128)
     return fail(MLA_ERR_UNSUPPORTED, "the fp8 cache takes 128-row tiles only (m_tile %d)",
                 p->m_tile);
-  pl->narrow = !q8 && !fp8 && (p->m_tile == 16 || (p->m_tile == 0 && M <= 16));
+  pl->narrow = !q8 && !fp8 && !q4 && (p->m_tile == 16 || (p->m_tile == 0 && M <= 16));
   if (pl->narrow) {
     pl->HG = 1;
   } else if (fp8) {
     pl->HG = 4;
   } else if (p->m_tile) {
     pl->HG = p->m_tile / 32;
+  } else if (q4) {
+    pl->HG = M <= 32 ? 1 : 2;
   } else {
     pl->HG = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   }
   pl->q8w = q8 && pl->HG == 4;
-  pl->CG = q8 ? (pl->q8w ? 1 : 4) : 4 / pl->HG;
+  pl->CG = (q8 || q4) ? (pl->q8w ? 1 : 4) : 4 / pl->HG;
   pl->MT = pl->narrow ? 16 : 32 * pl->HG;
   pl->m_tiles = (M + pl->MT - 1) / pl->MT;
   int P = p->num_parts;
@@ -3242,10 +3357,10 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
-template <int HG, int CG, bool Q8>
+template <int HG, int CG, bool Q8, bool Q4 = false>
 hipError_t launch_decode(const DecodeParams& dp, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_decode_kernel<HG, CG, Q8>), dim3(grid), dim3(64 * HG * CG), 0, stream,
-                     dp);
+  hipLaunchKernelGGL((mla_decode_kernel<HG, CG, Q8, Q4>), dim3(grid), dim3(64 * HG * CG), 0,
+                     stream, dp);
   return hipGetLastError();
 }
 
@@ -3438,14 +3553,17 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
   dp.max_blocks = p->max_blocks_per_seq;
   dp.P = pl.P;
   dp.m_tiles = pl.m_tiles;
-  dp.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  // q4_0 in Hadamard rotation: the kernel's scores leave out the rotation's
+  // 1 / sqrt(32), which is taken here
+  const double rot = p->kv_dtype == MLA_KV_Q4_0H ? 0.17677669529663688110 : 1.0;
+  dp.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074 * rot);
   dp.scale_mag_log2 = fabsf(dp.scale_log2);
   dp.q_sign2 = softmax_scale < 0.f ? 0x80008000u : 0u;
 
   const int grid = pl.P * pl.m_tiles;
   hipError_t e;
   // every cache type has its own kernels: a kernel reads the cache in its
-  // own row size (1152 B bf16, 576 B int8 or E4M3)
+  // own row size (1152 B bf16, 576 B int8 or E4M3, 288 B of q4_0 codes)
   switch (p->kv_dtype) {
     case MLA_KV_BF16:
       if (pl.narrow) {
@@ -3472,6 +3590,14 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
     case MLA_KV_FP8:
       if (pl.HG != 4) return fail(MLA_ERR_UNSUPPORTED, "no fp8 kernel for this row tile");
       e = launch_pipe<true>(dp, grid, stream);
+      break;
+    case MLA_KV_Q4_0H:
+      if (pl.HG == 2)
+        e = launch_decode<2, 4, true, true>(dp, grid, stream);
+      else if (pl.HG == 1)
+        e = launch_decode<1, 4, true, true>(dp, grid, stream);
+      else
+        return fail(MLA_ERR_UNSUPPORTED, "no q4_0 kernel for this row tile");
       break;
     default:
       return fail(MLA_ERR_INVALID_ARG, "unknown kv_dtype %d", p->kv_dtype);

@@ -211,7 +211,13 @@ __device__ __forceinline__ uint32_t e4m3_rne(float f) {
 // bf16: the row is copied. q8_0: lane g < 18 quantises column group g
 // (32 values): a = max |x|, d = a / 127 (fp32, correctly rounded), scale =
 // fp16(d) to nearest even, code = x / d rounded half away from zero, clamped
-// to [-127, 127]; a = 0 gives scale 0 and codes 0.
+// to [-127, 127]; a = 0 gives scale 0 and codes 0. q4_0 in Hadamard rotation:
+// lane g < 18 takes block g (32 values), rotates it by H / sqrt(32) with the
+// fast transform (strides 1, 2, 4, 8, 16: each pair (a, b) -> (a + b, a - b),
+// then every value times the fp32 value of 1 / sqrt(32)), and writes its
+// q4_0 encoding: m = the first value of largest magnitude, d = m / -8,
+// code = min(15, floor(y / d + 8.5)) (all 8 when d = 0), scale fp16(d) to
+// nearest even, codes two per byte (even code in the low nibble).
 __global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__ rows,
                                                     const int32_t* __restrict__ block_table,
                                                     int max_blocks, const int32_t* __restrict__ seqlens,
@@ -267,6 +273,50 @@ __global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__
           u32x4{packed[0], packed[1], packed[2], packed[3]};
       if (lane == 0) reinterpret_cast<float*>(scales)[dst] = d;
     }
+    return;
+  }
+  if (kind == MLA_KV_Q4_0H) {
+    if (lane >= kDK / MLA_Q8_GROUP) return;
+    const u32x4* s = reinterpret_cast<const u32x4*>(src + MLA_Q8_GROUP * lane);
+    float y[MLA_Q8_GROUP];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = s[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[8 * c + 2 * e] = __uint_as_float(w[e] << 16);
+        y[8 * c + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int st = 1; st < MLA_Q8_GROUP; st <<= 1)
+#pragma unroll
+      for (int k = 0; k < MLA_Q8_GROUP; ++k)
+        if ((k & st) == 0) {
+          const float a = y[k], b = y[k + st];
+          y[k] = a + b;
+          y[k + st] = a - b;
+        }
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < MLA_Q8_GROUP; ++k) {
+      y[k] = y[k] * 0.17677669529663688f;
+      if (fabsf(y[k]) > fabsf(m)) m = y[k];
+    }
+    const float d = m / -8.0f;
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < MLA_Q8_GROUP; ++k) {
+      uint32_t c = 8u;
+      if (d != 0.0f) {
+        const float t = floorf(y[k] / d + 8.5f);
+        c = t > 15.0f ? 15u : (uint32_t)(int)t;
+      }
+      packed[k >> 3] |= c << (4 * (k & 7));
+    }
+    *reinterpret_cast<u32x4*>(kv + dst * (kDK / 2) + 16 * lane) =
+        u32x4{packed[0], packed[1], packed[2], packed[3]};
+    scales[dst * (kDK / MLA_Q8_GROUP) + lane] = __builtin_bit_cast(uint16_t, (_Float16)d);
     return;
   }
   // q8_0
@@ -384,7 +434,8 @@ mla_status mla_cache_append(int32_t batch, int32_t seqlen_q, const void* rows,
     mla_set_last_error("batch >= 0, seqlen_q >= 1, max_blocks_per_seq >= 1, num_blocks >= 0");
     return MLA_ERR_INVALID_ARG;
   }
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_Q8_0 && kv_dtype != MLA_KV_FP8) {
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_Q8_0 && kv_dtype != MLA_KV_FP8 &&
+      kv_dtype != MLA_KV_Q4_0H) {
     mla_set_last_error("unknown kv_dtype");
     return MLA_ERR_INVALID_ARG;
   }

@@ -29,9 +29,13 @@ import workload as wl
 #      held in bf16 until the parts are merged (merge weights sum to 1, so the
 #      parts' A_e average to A_e);
 #   4. a q8_0 cache: the dequantised value scale * int8 (exact in fp32) is
-#      rounded to bf16 for the value product (the scores use it unrounded).
-# So k = 3 for a bf16 cache and 4 for a q8_0 cache (the split case bounds the
-# unsplit one). An fp8 (E4M3) cache converts to bf16 exactly and its
+#      rounded to bf16 for the value product (the scores use it unrounded);
+#      a q4_0 cache in Hadamard rotation likewise: the rotated-back value
+#      d / sqrt(32) * n (n the integer Hadamard sum of the codes, exact) is
+#      rounded to bf16 for the value product, the scores use n exactly and
+#      d in fp32.
+# So k = 3 for a bf16 cache and 4 for a q8_0 or q4_0 cache (the split case
+# bounds the unsplit one). An fp8 (E4M3) cache converts to bf16 exactly and its
 # per-token scale multiplies the score and the probability in fp32 before
 # rounding (1), so k = 3 as for bf16. The 2e-2 term absorbs what is left:
 # fp32 accumulation, the exp2 approximation and score rounding, all orders of
@@ -44,7 +48,7 @@ import workload as wl
 #   |lse_gpu - lse_ref| <= 1e-3 (absolute).
 OUT_ABS_TOL = 2e-2
 BF16_U = 2.0 ** -8
-ROUNDINGS = {"bf16": 3, "q8_0": 4, "fp8": 3}
+ROUNDINGS = {"bf16": 3, "q8_0": 4, "fp8": 3, "q4_0h": 4}
 OUT_REL_TOL = 1e-2
 LSE_ABS_TOL = 1e-3
 

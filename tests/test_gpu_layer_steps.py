@@ -91,7 +91,7 @@ def test_project_output_matches_the_oracle(B, s_q, H):
     assert np.all(err <= _product_bar(ref, mag, 512))
 
 
-@pytest.mark.parametrize("kvd", ["bf16", "q8_0", "fp8"])
+@pytest.mark.parametrize("kvd", ["bf16", "q8_0", "fp8", "q4_0h"])
 def test_cache_append_is_bit_exact(kvd):
     """Every byte of the cache after an append equals the oracle's: the new
     rows land at their positions (q8_0: quantised by the same rule), rows
@@ -117,7 +117,7 @@ def test_cache_append_is_bit_exact(kvd):
         assert np.array_equal(t["kv_scales"].view(torch.int16).cpu().numpy().view(np.uint16), sc_ref)
 
 
-@pytest.mark.parametrize("kvd", ["bf16", "q8_0", "fp8"])
+@pytest.mark.parametrize("kvd", ["bf16", "q8_0", "fp8", "q4_0h"])
 def test_append_then_decode(kvd):
     """A decode step after the append reads the appended rows: it matches the
     oracle's decode of the oracle-appended cache."""

@@ -60,6 +60,16 @@ SMALL = [
     ("h256_fp8", 2, 2, 128, [77, 1300], "sequential", "fp8", 0),
     ("h128_fp8_many", 12, 1, 128, [1, 0, 31, 33, 64, 65, 130, 0, 2, 300, 97, 5000],
      "permuted", "fp8", 0),
+    # q4_0 in Hadamard rotation: the 32/64-row kernels (two 64-row tiles for
+    # 128 heads), a padded tile, causal pairs, a forced 32-row tile, many
+    # segments and a segment longer than one id window
+    ("h128_q4", 2, 1, 128, [700, 129], "permuted", "q4_0h", 0),
+    ("h16_q4", 3, 1, 16, [64, 1, 999], "permuted", "q4_0h", 0),
+    ("h40_q4", 3, 1, 40, [65, 700, 33], "permuted", "q4_0h", 0),
+    ("h64_pair_q4", 2, 2, 64, [300, 2000], "permuted", "q4_0h", 64),
+    ("h64_mt32_q4", 2, 1, 64, [513, 64], "sequential", "q4_0h", 32),
+    ("h128_q4_many", 12, 1, 128, [1, 0, 31, 33, 64, 65, 130, 0, 2, 300, 97, 5000],
+     "permuted", "q4_0h", 0),
 ]
 
 
@@ -91,6 +101,25 @@ def test_full_size_config_all_rows(cfg):
     # the flat 2e-2 bound is asserted too, except with the x8 outlier rows of
     # the long-context workload (|out| up to 30, beyond what bf16 holds to 2e-2)
     compare(out, lse, *oracle_rows(w), what=w.name, kv_dtype=w.kv_dtype, flat=cfg != 4)
+
+
+def test_full_size_q4_cache_sampled_rows():
+    """The q8_0 workload's shape over a q4_0 cache in Hadamard rotation, in the
+    benchmark's launch configuration. The oracle rotates every cached block
+    back from the matrix entries, about 30 times the work of reading a bf16
+    row, so it checks two rows of every sequence (chosen by a seeded draw)
+    and, on the GPU side, that every row is finite."""
+    w = wl.config_workload(7)
+    log(f"config 7 ({w.name}): generated, rows={w.rows}")
+    out, lse, _ = run_gpu(w)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    per = w.s_q * w.H
+    pick = wl.uniform_int(2 * w.B, 7, 1, 0, per - 1).reshape(w.B, 2)
+    rows = np.sort((np.arange(w.B)[:, None] * per + pick).reshape(-1)).astype(np.int64)
+    log(f"config 7: GPU done, running the oracle on {rows.size} rows")
+    ref = oracle_rows(w, rows)
+    compare(out.reshape(-1, 512)[rows], lse.reshape(-1)[rows], *ref, what=f"{w.name} sampled",
+            kv_dtype=w.kv_dtype, flat=True)
 
 
 @pytest.mark.parametrize("kvd", ["bf16", "fp8"])
