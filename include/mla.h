@@ -119,10 +119,9 @@ typedef struct {
   int32_t num_parts;          /* 0: automatic; else P >= 1 KV partitions (see mla_plan) */
   int32_t m_tile;             /* 0: automatic; else 16, 32, 64 or 128 query rows
                                  per workgroup (16: bf16 cache only; fp8 cache:
-                                 128 only; q4_0 cache: 32 or 64 only). Automatic
-                                 picks the smallest tile that holds
-                                 seqlen_q * num_heads rows (16 only for bf16),
-                                 else 128 (q4_0: 64); always 128 for fp8. */
+                                 128 only). Automatic picks the smallest tile
+                                 that holds seqlen_q * num_heads rows (16 only
+                                 for bf16), else 128; always 128 for fp8. */
 } mla_problem;
 
 /* Bytes of device workspace mla_decode needs for *p (written to *bytes, host).

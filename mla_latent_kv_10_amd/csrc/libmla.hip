@@ -2548,15 +2548,23 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
 // 32-column group's partial score (the 32/64-row q8_0 kernel), the conversion
 // work is done once per tile for all 128 rows and the scores are pure MFMA
 // work.
-template <bool NT>
+// Q4: the q4_0 cache in Hadamard rotation (9 KiB of codes per tile). Step 1
+// forms, per 32-column block, n = H (c - 8) on the matrix core (the integer
+// Hadamard sums, exact), then x = d / sqrt(32) * n in fp32 and its hi / lo
+// parts; everything after it is the q8_0 path.
+template <bool NT, bool Q4 = false>
 __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) {
   constexpr int NW = 4;
   constexpr int NTH = 64 * NW;
   constexpr int MT = 128;
   constexpr int NST = 3;                  // ring stages of the quantised tiles
   constexpr int KPF = 2;                  // score k-steps in flight (hi and lo each)
-  constexpr int CPW = 5;                  // 1 KiB copies per wave per tile (at most 20 per tile)
-  constexpr int STAGE = kQ8StageBytes;
+  // 1 KiB copies per wave per tile: q8_0 20 (5 a wave), q4_0 11 (3, wave 3 two)
+  constexpr int NCOPY = Q4 ? 11 : 20;
+  constexpr int CPW = (NCOPY + NW - 1) / NW;
+  constexpr int CODE_COPIES = Q4 ? 9 : 18;
+  constexpr int SCALE_OFF = Q4 ? kQ4TileBytes : kQ8TileBytes;   // scales in a stage
+  constexpr int STAGE = Q4 ? kQ4StageBytes : kQ8StageBytes;
 
   __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NST][STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t s_hl[2][kTileBytes];   // hi, lo
@@ -2700,21 +2708,33 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
       }
       const int64_t phys = uniform(__builtin_amdgcn_readlane(bt_lane, rel));
       const int64_t row0 = phys * kBT + ((t_begin + idx) & 1) * kTile;
-      const uint8_t* src = a.kv + row0 * kQ8RowBytes;
+      const uint8_t* src = a.kv + row0 * (Q4 ? kQ4RowBytes : kQ8RowBytes);
       const uint32_t dst = lds_addr_of(s_ring[idx % NST]);
       const uint8_t* ssrc = a.kv_scales + row0 * kQ8ScaleRowBytes;
 #pragma unroll
       for (int j = 0; j < CPW; ++j) {
         const int k = wave + 4 * j;
-        if (k < 18) {
+        if (k < CODE_COPIES) {
           copy(src + 1024 * k, 16 * lane, dst + 1024 * k);
-        } else {
+        } else if (k < NCOPY) {
           // scales: default policy (the tail lanes re-read a partial line)
-          const int off = 1024 * (k - 18) + 16 * lane;
-          dma16_sbase(ssrc, off < kQ8ScaleTileBytes ? off : 0, dst + kQ8TileBytes + 1024 * (k - 18));
+          const int off = 1024 * (k - CODE_COPIES) + 16 * lane;
+          dma16_sbase(ssrc, off < kQ8ScaleTileBytes ? off : 0,
+                      dst + SCALE_OFF + 1024 * (k - CODE_COPIES));
         }
       }
     };
+    // q4_0: A operand of the Hadamard product, H[m][k] for row m = l32 and
+    // columns k = 8 hi + e (first MFMA) and 16 + 8 hi + e (second)
+    bf16x8 hA0, hA1;
+    if constexpr (Q4) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k0 = 8 * hi + e;
+        hA0[e] = (__bf16)((__builtin_popcount(l32 & k0) & 1) ? -1.f : 1.f);
+        hA1[e] = (__bf16)((__builtin_popcount(l32 & (k0 + 16)) & 1) ? -1.f : 1.f);
+      }
+    }
 
     // Query fragments of this lane's row (B operand of the score MFMA): 16
     // bytes per k-step, read directly; rows past M read zero.
@@ -2739,13 +2759,65 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
       // ---- 1. int8 tile it landed (tile it+1 may be in flight); everyone is
       // done with the previous tile's hi / lo / P
       if (it + 1 < n_run) {
-        wait_vmcnt<CPW>();
+        if constexpr (NCOPY % NW == 0) {
+          wait_vmcnt<CPW>();
+        } else {
+          if (wave < NCOPY % NW)
+            wait_vmcnt<CPW>();
+          else
+            wait_vmcnt<CPW - 1>();
+        }
       } else {
         wait_vmcnt<0>();
       }
       lds_barrier();
       if (it + 2 < n_run) issue(it + 2);
-      {
+      if constexpr (Q4) {
+        // Wave w converts blocks g = w, w + 4, ...: n = H (c - 8) by two MFMAs
+        // (H rows against the codes as bf16(128 + c), bits 0x4300 | c, which
+        // adds 4352 to row m = 0 only, taken off), then x = d / sqrt(32) * n
+        // and its hi / lo parts. Lane (t, hi) holds n[m][t] for
+        // m = 8 q + 4 hi + (0..3): bytes 8 hi .. 8 hi + 7 of chunk 4 g + q of
+        // token t. Tokens past the end of the sequence get scale 0.
+        const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_ring[it % NST];
+        const int valid = L - (t_begin + it) * kTile;
+        const bool tok_ok = l32 < valid;
+        auto nib8 = [](uint32_t w) {
+          u32x4 r;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            r[k] = ((w >> (8 * k)) & 0xFu) | (((w >> (8 * k + 4)) & 0xFu) << 16) | 0x43004300u;
+          return __builtin_bit_cast(bf16x8, r);
+        };
+        LDS_AS uint8_t* hib = (LDS_AS uint8_t*)s_hl[0];
+        LDS_AS uint8_t* lob = (LDS_AS uint8_t*)s_hl[1];
+        for (int g = wave; g < 18; g += NW) {
+          const LDS_AS uint8_t* cu = st + kQ4RowBytes * l32 + 16 * g;
+          const uint32_t w0 = *reinterpret_cast<const LDS_AS uint32_t*>(cu + 4 * hi);
+          const uint32_t w1 = *reinterpret_cast<const LDS_AS uint32_t*>(cu + 8 + 4 * hi);
+          const uint16_t sbits = *reinterpret_cast<const LDS_AS uint16_t*>(
+              st + SCALE_OFF + kQ8ScaleRowBytes * l32 + 2 * g);
+          const float dv = tok_ok ? (float)__builtin_bit_cast(_Float16, sbits) * kInvSqrt32 : 0.f;
+          const f32x16 zero4 = {};
+          f32x16 n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA0, nib8(w0), zero4, 0, 0, 0);
+          n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA1, nib8(w1), n, 0, 0, 0);
+          if (hi == 0) n[0] -= 4352.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t h[2], lo[2];
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              const float x0 = dv * n[4 * q + 2 * e2], x1 = dv * n[4 * q + 2 * e2 + 1];
+              h[e2] = pack_bf16x2(x0, x1);
+              lo[e2] = pack_bf16x2(x0 - __builtin_bit_cast(float, h[e2] << 16),
+                                   x1 - __builtin_bit_cast(float, h[e2] & 0xffff0000u));
+            }
+            const int u = 16 * rg_unit(l32, 4 * g + q) + 8 * hi;
+            *reinterpret_cast<LDS_AS uint64_t*>(hib + u) = (uint64_t)h[0] | ((uint64_t)h[1] << 32);
+            *reinterpret_cast<LDS_AS uint64_t*>(lob + u) = (uint64_t)lo[0] | ((uint64_t)lo[1] << 32);
+          }
+        }
+      } else {
         // Thread (w, l) converts unit 256 i + 64 w + l of the hi / lo tiles,
         // i = 0..8: token 8 w + r(l), chunk 8 i + c(l) (the row-group
         // placement inverted), i.e. one token per thread. All reads first,
@@ -3244,7 +3316,7 @@ int device_cus() {
 
 struct Plan {
   bool narrow;   // 16-row tile (bf16 cache)
-  bool q8w;      // q8_0 cache, 128-row tile converted to bf16 in LDS
+  bool q8w;      // q8_0 or q4_0 cache, 128-row tile converted to bf16 in LDS
   int HG, CG, MT, m_tiles, P, M;
   size_t off_prefix, off_lse, off_o, bytes;
 };
@@ -3290,8 +3362,9 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   // q8_0 cache: 32 or 64 rows, each row group's work split over 4 waves, or
   // 128 rows (the tile converted once into exact bf16 hi / lo parts). fp8
   // cache: 128 rows (the bf16 pipeline, its operands read as E4M3 codes and
-  // converted exactly in registers). q4_0 cache in Hadamard rotation: 32 or
-  // 64 rows (the q8_0 kernel's work split). More rows than one tile holds take
+  // converted exactly in registers). q4_0 cache in Hadamard rotation: as
+  // q8_0 (its 128-row tile converted through the matrix core). More rows
+  // than one tile holds take
   // several row tiles per KV part, placed on the same XCD so the second read
   // of each cache tile hits L2.
   const bool q8 = p->kv_dtype == MLA_KV_Q8_0;
@@ -3299,9 +3372,8 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
   const bool q4 = p->kv_dtype == MLA_KV_Q4_0H;
   if (q8 && p->m_tile == 16)
     return fail(MLA_ERR_UNSUPPORTED, "m_tile %d is not available for the q8_0 cache", p->m_tile);
-  if (q4 && (p->m_tile == 16 || p->m_tile == 128))
-    return fail(MLA_ERR_UNSUPPORTED, "the q4_0 cache takes 32- or 64-row tiles only (m_tile %d)",
-                p->m_tile);
+  if (q4 && p->m_tile == 16)
+    return fail(MLA_ERR_UNSUPPORTED, "m_tile %d is not available for the q4_0 cache", p->m_tile);
   if (fp8 && p->m_tile != 0 && p->m_tile != 128)
     return fail(MLA_ERR_UNSUPPORTED, "the fp8 cache takes 128-row tiles only (m_tile %d)",
                 p->m_tile);
@@ -3312,12 +3384,10 @@ mla_status make_plan(const mla_problem* p, Plan* pl) {
     pl->HG = 4;
   } else if (p->m_tile) {
     pl->HG = p->m_tile / 32;
-  } else if (q4) {
-    pl->HG = M <= 32 ? 1 : 2;
   } else {
     pl->HG = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   }
-  pl->q8w = q8 && pl->HG == 4;
+  pl->q8w = (q8 || q4) && pl->HG == 4;
   pl->CG = (q8 || q4) ? (pl->q8w ? 1 : 4) : 4 / pl->HG;
   pl->MT = pl->narrow ? 16 : 32 * pl->HG;
   pl->m_tiles = (M + pl->MT - 1) / pl->MT;
@@ -3373,11 +3443,12 @@ hipError_t launch_pipe(const DecodeParams& dp, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool Q4>
 hipError_t launch_q8w(const DecodeParams& dp, int grid, hipStream_t stream) {
   if (dp.m_tiles == 1)
-    hipLaunchKernelGGL(mla_decode_q8w_kernel<true>, dim3(grid), dim3(256), 0, stream, dp);
+    hipLaunchKernelGGL((mla_decode_q8w_kernel<true, Q4>), dim3(grid), dim3(256), 0, stream, dp);
   else
-    hipLaunchKernelGGL(mla_decode_q8w_kernel<false>, dim3(grid), dim3(256), 0, stream, dp);
+    hipLaunchKernelGGL((mla_decode_q8w_kernel<false, Q4>), dim3(grid), dim3(256), 0, stream, dp);
   return hipGetLastError();
 }
 
@@ -3553,9 +3624,10 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
   dp.max_blocks = p->max_blocks_per_seq;
   dp.P = pl.P;
   dp.m_tiles = pl.m_tiles;
-  // q4_0 in Hadamard rotation: the kernel's scores leave out the rotation's
-  // 1 / sqrt(32), which is taken here
-  const double rot = p->kv_dtype == MLA_KV_Q4_0H ? 0.17677669529663688110 : 1.0;
+  // q4_0 in Hadamard rotation: the 32/64-row kernel's scores leave out the
+  // rotation's 1 / sqrt(32), which is taken here (the 128-row kernel scales
+  // its converted tile by it)
+  const double rot = p->kv_dtype == MLA_KV_Q4_0H && !pl.q8w ? 0.17677669529663688110 : 1.0;
   dp.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074 * rot);
   dp.scale_mag_log2 = fabsf(dp.scale_log2);
   dp.q_sign2 = softmax_scale < 0.f ? 0x80008000u : 0u;
@@ -3579,7 +3651,7 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
       break;
     case MLA_KV_Q8_0:
       if (pl.q8w)
-        e = launch_q8w(dp, grid, stream);
+        e = launch_q8w<false>(dp, grid, stream);
       else if (pl.HG == 2)
         e = launch_decode<2, 4, true>(dp, grid, stream);
       else if (pl.HG == 1)
@@ -3592,7 +3664,9 @@ mla_status launch_decode_step(const mla_problem* p, const Plan& pl, const void* 
       e = launch_pipe<true>(dp, grid, stream);
       break;
     case MLA_KV_Q4_0H:
-      if (pl.HG == 2)
+      if (pl.q8w)
+        e = launch_q8w<true>(dp, grid, stream);
+      else if (pl.HG == 2)
         e = launch_decode<2, 4, true, true>(dp, grid, stream);
       else if (pl.HG == 1)
         e = launch_decode<1, 4, true, true>(dp, grid, stream);

@@ -113,12 +113,11 @@ def test_row_tile_choices(L):
     for mt in (32, 64, 128):
         assert L.mla_workspace_size(ctypes.byref(_prob(m_tile=mt, kv_dtype=1)),
                                     ctypes.byref(n)) == 0
-    # the q4_0 cache in Hadamard rotation: 32- and 64-row tiles only
-    for mt in (16, 128):
-        assert L.mla_workspace_size(ctypes.byref(_prob(m_tile=mt, kv_dtype=3)),
-                                    ctypes.byref(n)) == 2
-        assert "q4_0" in L.mla_last_error().decode()
-    for mt in (0, 32, 64):
+    # the q4_0 cache in Hadamard rotation: as q8_0
+    assert L.mla_workspace_size(ctypes.byref(_prob(m_tile=16, kv_dtype=3)),
+                                ctypes.byref(n)) == 2
+    assert "q4_0" in L.mla_last_error().decode()
+    for mt in (0, 32, 64, 128):
         assert L.mla_workspace_size(ctypes.byref(_prob(m_tile=mt, kv_dtype=3)),
                                     ctypes.byref(n)) == 0
     assert _decode(L, _prob(kv_dtype=3)) == 1           # q4_0 needs kv_scales too

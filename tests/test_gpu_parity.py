@@ -60,10 +60,14 @@ SMALL = [
     ("h256_fp8", 2, 2, 128, [77, 1300], "sequential", "fp8", 0),
     ("h128_fp8_many", 12, 1, 128, [1, 0, 31, 33, 64, 65, 130, 0, 2, 300, 97, 5000],
      "permuted", "fp8", 0),
-    # q4_0 in Hadamard rotation: the 32/64-row kernels (two 64-row tiles for
-    # 128 heads), a padded tile, causal pairs, a forced 32-row tile, many
+    # q4_0 in Hadamard rotation: the 128-row converting kernel (also with two
+    # row tiles per part, and padded rows in a forced 128-row tile) and the
+    # 32/64-row kernels (also forced for 128 heads), causal pairs, many
     # segments and a segment longer than one id window
     ("h128_q4", 2, 1, 128, [700, 129], "permuted", "q4_0h", 0),
+    ("h128_pair_q4", 2, 2, 128, [300, 4500], "permuted", "q4_0h", 0),
+    ("h40_mt128_q4", 2, 1, 40, [500, 77], "permuted", "q4_0h", 128),
+    ("h128_mt64_q4", 2, 1, 128, [700, 129], "permuted", "q4_0h", 64),
     ("h16_q4", 3, 1, 16, [64, 1, 999], "permuted", "q4_0h", 0),
     ("h40_q4", 3, 1, 40, [65, 700, 33], "permuted", "q4_0h", 0),
     ("h64_pair_q4", 2, 2, 64, [300, 2000], "permuted", "q4_0h", 64),
