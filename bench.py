@@ -95,7 +95,7 @@ def copy_calibration():
 def layer_steps(steps: int):
     """The steps either side of the decode at the bench workload's shape (64
     query rows x 128 heads): query absorption, output projection and the
-    cache append (bf16, q8_0, fp8), each replayed `steps` times from a HIP
+    cache append (bf16, q8_0, fp8, rotated q4_0), each replayed `steps` times from a HIP
     graph so that host launch cost stays out; HIP events on the launch stream.
     Algorithmic bytes: every weight once plus the activations in and out."""
     import torch
@@ -123,13 +123,15 @@ def layer_steps(steps: int):
               "q8_0": (torch.empty(w.kv.shape, dtype=torch.int8, device=dev),
                        torch.empty(w.kv.shape[:2] + (18,), dtype=torch.float16, device=dev)),
               "fp8": (torch.empty(w.kv.shape, dtype=torch.uint8, device=dev),
-                      torch.empty(w.kv.shape[:2], dtype=torch.float32, device=dev))}
+                      torch.empty(w.kv.shape[:2], dtype=torch.float32, device=dev)),
+              "q4_0h": (torch.empty(w.kv.shape[:2] + (288,), dtype=torch.uint8, device=dev),
+                        torch.empty(w.kv.shape[:2] + (18,), dtype=torch.float16, device=dev))}
     wbytes = H * 128 * 512 * 2
     cases = [("absorb_query", lambda: mla.mla_absorb_query(qn, qr, wk, qa),
               wbytes + qn.numel() * 2 + qr.numel() * 2 + qa.numel() * 2),
              ("project_output", lambda: mla.mla_project_output(ol, wv, o),
               wbytes + ol.numel() * 2 + o.numel() * 2)]
-    per_row = {"bf16": 1152, "q8_0": 612, "fp8": 580}
+    per_row = {"bf16": 1152, "q8_0": 612, "fp8": 580, "q4_0h": 324}
     for kvd, (kv, sc) in caches.items():
         cases.append((f"cache_append_{kvd}",
                       lambda kv=kv, sc=sc: mla.mla_cache_append(new, bt, sl, kv, sc),
