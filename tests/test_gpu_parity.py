@@ -126,7 +126,7 @@ def test_full_size_q4_cache_sampled_rows():
             kv_dtype=w.kv_dtype, flat=True)
 
 
-@pytest.mark.parametrize("kvd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kvd", ["bf16", "fp8", "q4_0h"])
 def test_forced_part_counts_agree(kvd):
     w = wl.make_workload("parts", 4, 1, 128, [2000, 1, 4096, 777], seed=5, table="permuted",
                          kv_dtype=kvd)
@@ -144,7 +144,7 @@ def test_forced_part_counts_agree(kvd):
         assert np.abs(lse - results[0][1]).max() <= 1e-3
 
 
-@pytest.mark.parametrize("kvd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kvd", ["bf16", "fp8", "q4_0h"])
 def test_block_permutation_is_bit_identical(kvd):
     w = wl.make_workload("perm", 3, 1, 128, [900, 64, 2049], seed=6, kv_dtype=kvd)
     out1, lse1, bits1 = run_gpu(w, num_parts=5)
@@ -191,11 +191,12 @@ def test_one_hot_probe_returns_the_exact_row(H):
 
 
 @pytest.mark.parametrize("H,kvd", [(16, "bf16"), (40, "bf16"), (128, "bf16"),
-                                   (40, "q8_0"), (128, "q8_0"), (128, "fp8")])
+                                   (40, "q8_0"), (128, "q8_0"), (128, "fp8"),
+                                   (40, "q4_0h"), (128, "q4_0h")])
 def test_unused_cache_slots_never_reach_the_result(H, kvd):
     """The slots of a sequence's last block past its length hold NaN (bf16
-    rows; q8_0 scales): every kernel gives the oracle's result, which never
-    reads them."""
+    rows; q8_0, fp8 and q4_0 scales): every kernel gives the oracle's result,
+    which never reads them."""
     w = wl.make_workload("tailnan", 3, 1, H, [100, 65, 1000], seed=21, table="permuted",
                          kv_dtype=kvd)
     for b, L in enumerate(w.seqlens):
@@ -207,7 +208,7 @@ def test_unused_cache_slots_never_reach_the_result(H, kvd):
                 w.kv[blk, L % 64:, :] = 0x7F          # E4M3 NaN
                 w.kv_scales[blk, L % 64:] = np.nan
             else:
-                w.kv_scales[blk, L % 64:, :] = 0x7E00  # fp16 NaN
+                w.kv_scales[blk, L % 64:, :] = 0x7E00  # fp16 NaN (q8_0, q4_0)
     ref = oracle_rows(w)
     for parts in (0, 1, 5):
         out, lse, _ = run_gpu(w, num_parts=parts)
@@ -249,7 +250,7 @@ def test_invalid_block_id_in_a_later_id_window():
 
 
 @pytest.mark.parametrize("H,kvd", [(16, "bf16"), (40, "bf16"), (128, "bf16"), (16, "q8_0"),
-                                   (128, "fp8")])
+                                   (128, "fp8"), (16, "q4_0h"), (128, "q4_0h")])
 def test_empty_pool_poisons_every_nonempty_sequence(H, kvd):
     """num_blocks = 0: no block id is valid, so every sequence with tokens is
     poisoned and nothing is read from the cache; empty sequences stay empty."""
@@ -260,7 +261,7 @@ def test_empty_pool_poisons_every_nonempty_sequence(H, kvd):
     lse = torch.empty((w.B, 1, H), dtype=torch.float32, device="cuda")
     prob = mla.make_problem(t["q"], t["kv"], t["bt"],
                             kv_dtype={"bf16": mla.KV_BF16, "q8_0": mla.KV_Q8_0,
-                                      "fp8": mla.KV_FP8}[kvd],
+                                      "fp8": mla.KV_FP8, "q4_0h": mla.KV_Q4_0H}[kvd],
                             max_seqlen=w.max_seqlen, num_parts=2)
     prob.num_blocks = 0
     ws = torch.empty(max(16, mla.workspace_size(prob)), dtype=torch.uint8, device="cuda")
@@ -358,7 +359,7 @@ def test_repeat_runs_are_bit_identical():
     assert np.array_equal(bits1, bits2) and np.array_equal(lse1, lse2)
 
 
-@pytest.mark.parametrize("kvd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kvd", ["bf16", "fp8", "q4_0h"])
 def test_graph_replay_matches_eager(kvd):
     """A decode step captured in a HIP graph (split plan + decode + combine,
     the way the benchmark replays it) gives the eager result bit for bit on
@@ -369,7 +370,8 @@ def test_graph_replay_matches_eager(kvd):
     out = torch.empty((w.B, w.s_q, w.H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.s_q, w.H), dtype=torch.float32, device="cuda")
     prob = mla.make_problem(t["q"], t["kv"], t["bt"],
-                            kv_dtype={"bf16": mla.KV_BF16, "fp8": mla.KV_FP8}[kvd],
+                            kv_dtype={"bf16": mla.KV_BF16, "fp8": mla.KV_FP8,
+                                      "q4_0h": mla.KV_Q4_0H}[kvd],
                             max_seqlen=w.max_seqlen, num_parts=16)
     ws = torch.empty(max(16, mla.workspace_size(prob)), dtype=torch.uint8, device="cuda")
 

@@ -58,7 +58,7 @@ def test_noalloc_matches_decode_on_two_calls_in_a_row():
     _check(w2, "noalloc 2", num_parts=5)
 
 
-@pytest.mark.parametrize("kvd,H", [("q8_0", 64), ("fp8", 128)])
+@pytest.mark.parametrize("kvd,H", [("q8_0", 64), ("fp8", 128), ("q4_0h", 128)])
 def test_noalloc_quantised_cache_and_causal_pair(kvd, H):
     w = wl.make_workload(f"noalloc_{kvd}", 3, 2, H, [700, 2100, 65], seed=43, table="permuted",
                          kv_dtype=kvd)
