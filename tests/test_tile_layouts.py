@@ -1,5 +1,6 @@
 """Host-side checks of the LDS tile layouts used by the bf16 decode kernels
-(128-, 32/64- and 16-row tiles; no GPU). The index formulas below restate the kernels' own
+(128-, 32/64- and 16-row tiles), of the 128-row kernel's query-row load, and
+of the index arithmetic of the q4_0 (Hadamard) path (no GPU). The index formulas below restate the kernels' own
 (lane offsets of the LDS-DMA copies, score and value operand reads, tail
 clearing); the checks are that the copies fill every 16-byte unit of the
 36 KiB tile exactly once from whole 128-byte lines, that every read fetches
@@ -109,3 +110,114 @@ def test_narrow_layout():
             assert (byte % 16) // 8 == vq & 1
             slots.append(((byte // 16) % 16, (byte % 16) // 8))
         assert len(set(slots)) == 32
+
+
+# ---- query rows of the 128-row kernel: load 4C + R of a wave reads block
+# (C, R) of the K-tile layout with the copies' lane placement (rows past M
+# read row M - 1); pass p writes blocks C = 4p .. 4p + 3 at 1024 (4 (C - 4p) + R)
+# of the wave's 18 KiB region and reads k-steps 16p .. 16p + 15 back at
+# kstep_ofs(k) - 16384 p + kofs.
+def test_query_rows_load_and_read_back():
+    for M in (128, 40, 16, 256):
+        for row0 in range(0, 128, 32):
+            region = {}
+            for C, R, l in itertools.product(range(9), range(4), range(64)):
+                dc0 = (l >> 4) & 1
+                dr = (l & 3) | ((((l >> 2) & 1) ^ dc0) << 2)
+                dcq = dc0 | ((((l >> 3) ^ R) & 1) << 1) | (((l >> 5) & 1) << 2)
+                src_row = min(row0 + 8 * R + dr, M - 1)
+                assert 0 <= src_row < M
+                p = C // 4
+                byte = 1024 * (4 * (C - 4 * p) + R) + 16 * l
+                assert byte + 16 <= 18432          # inside the wave's region
+                region[(p, byte // 16)] = (8 * R + dr, 8 * C + dcq)
+            # each load reads eight whole 128-byte lines when no row is clamped
+            if row0 + 32 <= M:
+                for C, R in itertools.product(range(9), range(4)):
+                    lines = {}
+                    for l in range(64):
+                        dc0 = (l >> 4) & 1
+                        dr = (l & 3) | ((((l >> 2) & 1) ^ dc0) << 2)
+                        dcq = dc0 | ((((l >> 3) ^ R) & 1) << 1) | (((l >> 5) & 1) << 2)
+                        off = (8 * R + dr) * ROW + 16 * (8 * C + dcq)
+                        lines.setdefault(off // 128, set()).add(off % 128)
+                    assert len(lines) == 8 and all(len(v) == 8 for v in lines.values())
+            for k, lane in itertools.product(range(36), range(64)):
+                hi, l32 = lane >> 5, lane & 31
+                R, r = l32 >> 3, l32 & 7
+                kpart = 1024 * R + 16 * ((r & 3) | ((((r >> 2) ^ hi) & 1) << 2) | (hi << 4))
+                kofs = kpart + 128 * ((R & 1) ^ (k & 1))
+                p = k // 16
+                byte = 4096 * (k >> 2) + 512 * ((k >> 1) & 1) - 16384 * p + kofs
+                assert region[(p, byte // 16)] == (l32, 2 * k + hi)
+
+
+# ---- q4_0 cache in Hadamard rotation: the matrix-core form of n = H (c - 8)
+def _hadamard(m, k):
+    return -1 if bin(m & k).count("1") & 1 else 1
+
+
+def test_q4_hadamard_product_and_tile_writes():
+    import numpy as np
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, size=(32, 32))          # [token, code index] of one block
+    packed = np.zeros((32, 16), np.int64)               # 16 bytes per token, low nibble first
+    for j in range(32):
+        packed[:, j // 2] |= codes[:, j] << (4 * (j & 1))
+    # B operand: lane (t, hi) of MFMA 1 holds codes 8 hi + e from the dword at
+    # byte 4 hi, of MFMA 2 codes 16 + 8 hi + e from byte 8 + 4 hi, each as
+    # bf16 bits 0x4300 | c, i.e. the value 128 + c
+    def dword(t, byte):
+        return sum(int(packed[t, byte + i]) << (8 * i) for i in range(4))
+
+    def nib8(w):
+        vals = []
+        for k in range(4):
+            lo, hi_ = (w >> (8 * k)) & 0xF, (w >> (8 * k + 4)) & 0xF
+            for bits in ((0x4300 | lo), (0x4300 | hi_)):
+                assert bits >> 7 == 0x86                 # exponent of 128, mantissa = c
+                vals.append(128 + (bits & 0x7F))
+        return vals
+    D = np.zeros((32, 32), np.int64)                    # D[m][t]
+    for t, hi in itertools.product(range(32), range(2)):
+        b0 = nib8(dword(t, 4 * hi))
+        b1 = nib8(dword(t, 8 + 4 * hi))
+        assert b0 == [128 + c for c in codes[t, 8 * hi:8 * hi + 8]]
+        assert b1 == [128 + c for c in codes[t, 16 + 8 * hi:16 + 8 * hi + 8]]
+        for m in range(32):
+            D[m, t] += sum(_hadamard(m, 8 * hi + e) * b0[e] for e in range(8))
+            D[m, t] += sum(_hadamard(m, 16 + 8 * hi + e) * b1[e] for e in range(8))
+    D[0, :] -= 4352
+    H = np.array([[_hadamard(m, j) for j in range(32)] for m in range(32)])
+    assert np.array_equal(D, H @ (codes.T - 8))
+    assert np.abs(D).max() <= 256                       # exact in bf16 (8 significant bits)
+    # accumulator element i of lane (t, hi) is row m = 8 (i >> 2) + 4 hi + (i & 3);
+    # the lane writes rows 8 q + 4 hi .. + 3 as 8 bytes at offset 8 hi of
+    # chunk 4 g + q of token t: every (token, column) once, in column order
+    for g in (0, 5, 17):
+        seen = {}
+        for t, hi, q in itertools.product(range(32), range(2), range(4)):
+            chunk = 4 * g + q
+            for e in range(4):
+                col = 8 * chunk + 4 * hi + e
+                i = 4 * q + e
+                assert 8 * (i >> 2) + 4 * hi + (i & 3) == col - 32 * g
+                assert (t, col) not in seen
+                seen[(t, col)] = True
+        assert len(seen) == 32 * 32
+
+
+def test_q4_code_copies_of_the_64_row_kernel():
+    # load k < 9: lane (l32, hi) reads 16 bytes at l32 * 288 + (2k + hi) * 16
+    # into unit 64 k + l, which must be unit 32 g + t of block g = 2k + hi,
+    # token t = l32; the two scale loads cover the 1152 scale bytes
+    seen = set()
+    for k, l in itertools.product(range(9), range(64)):
+        hi, l32 = l >> 5, l & 31
+        src = l32 * 288 + (2 * k + hi) * 16
+        assert src + 16 <= 32 * 288
+        unit = 64 * k + l
+        assert unit == 32 * (2 * k + hi) + l32
+        assert src == 288 * (unit % 32) + 16 * (unit // 32)
+        seen.add(unit)
+    assert seen == set(range(18 * 32))
