@@ -2,11 +2,13 @@
 // gfx950 (MI355X). The operation and the C ABI are defined in include/mla.h.
 //
 // Design in brief (CDNA4):
-//  * One workgroup = 4 waves on one CU (8 for the 64-row q8_0 tile),
+//  * One workgroup = 4 waves on one CU (8 for the 64-row quantised tile),
 //    processing one KV partition of the cache for a tile of query rows:
 //    16 rows (mla_decode_narrow_kernel), 32 or 64 (mla_decode_rows_kernel),
-//    128 (mla_decode_pipe_kernel) for a bf16 cache; 32 or 64
-//    (mla_decode_kernel) for a q8_0 cache.
+//    128 (mla_decode_pipe_kernel) for a bf16 cache; 128 for an fp8 cache
+//    (the pipe kernel reading E4M3 codes); 32 or 64 (mla_decode_kernel) and
+//    128 (mla_decode_q8w_kernel) for a q8_0 cache and for a q4_0 cache stored
+//    in Hadamard rotation.
 //  * The cache streams through LDS in 32-token tiles (half a 64-token block,
 //    36 KiB in bf16), fetched with global_load_lds_dwordx4 (direct to LDS, no
 //    VGPRs) into a 3- or 4-stage ring, so two or three tiles are in flight
@@ -1894,7 +1896,9 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   // in registers (exact: every E4M3 value is a bf16 value), which halves the
   // LDS traffic of both products
   constexpr int STB = FP8 ? kFp8StageBytes : kTileBytes;   // bytes per ring stage
-  constexpr int RING = 4 * kTileBytes;    // the query is transposed through 4 x 36 KiB
+  // 4 x 36 KiB: the bf16 stages; the query rows pass through the upper half
+  // (18 KiB a wave) before the third tile is issued, for both cache types
+  constexpr int RING = 4 * kTileBytes;
   static_assert(NST * STB <= RING, "ring stages");
   using KOp = std::conditional_t<FP8, u32x2, bf16x8>;       // score operand as read
   // LDS-DMA copy of one block (NT: non-temporal, when no other workgroup
@@ -2525,12 +2529,12 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   }
 }
 
-// ------------------- q8_0 / fp8 decode kernel (128-row tile, converted tiles)
+// ------------------ q8_0 / q4_0 decode kernel (128-row tile, converted tiles)
 
-// Quantised cache (q8_0 or fp8), 128 query rows per workgroup, 4 waves; wave w
-// computes the scores and the softmax of rows 32w..32w+31 and the value
-// product of all 128 rows for output columns 128w..128w+127 (the division of
-// the 128-row bf16 kernel). Per 32-token tile, in four phases separated by
+// Quantised cache (q8_0; with Q4 the q4_0 cache in Hadamard rotation), 128
+// query rows per workgroup, 4 waves; wave w computes the scores and the
+// softmax of rows 32w..32w+31 and the value product of all 128 rows for
+// output columns 128w..128w+127 (the division of the 128-row bf16 kernel). Per 32-token tile, in four phases separated by
 // barriers:
 //  1. the int8 tile (18 KiB) and its scales (1152 B), copied by LDS-DMA into a
 //     3-stage ring, are converted once by all threads into two bf16 tiles in
