@@ -84,6 +84,8 @@ def _load():
         lib.oracle_q4_value.restype = dbl
         lib.oracle_quantize_q4h_row.argtypes = [vp, vp, vp]
         lib.oracle_quantize_q4h_row.restype = None
+        lib.oracle_q4h_dequantize.argtypes = [i64, vp, vp, vp]
+        lib.oracle_q4h_dequantize.restype = None
         lib.oracle_cache_append.restype = i64
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -102,10 +104,12 @@ Q4_ROW_BYTES = D_K // 2
 
 def _kind(kv) -> int:
     """Cache type from the array: bf16 bits (uint16), q8_0 (int8), fp8 (uint8
-    rows of 576) or q4_0 in Hadamard rotation (uint8 rows of 288 code bytes)."""
+    rows of 576), q4_0 in Hadamard rotation (uint8 rows of 288 code bytes) or
+    the rows themselves (float64)."""
     if kv.dtype == np.uint8 and kv.shape[-1] == Q4_ROW_BYTES:
         return 3
-    return {np.dtype(np.uint16): 0, np.dtype(np.int8): 1, np.dtype(np.uint8): 2}[kv.dtype]
+    return {np.dtype(np.uint16): 0, np.dtype(np.int8): 1, np.dtype(np.uint8): 2,
+            np.dtype(np.float64): 4}[kv.dtype]
 
 
 def _p(a):
@@ -160,8 +164,9 @@ def decode_absorbed(q, kv, block_table, seqlens, softmax_scale, *, kv_scales=Non
     """Absorbed-form decode (fp64). q: uint16 [B, s_q, H, 576] bf16 bits.
 
     kv: uint16 bf16 bits, int8 (with kv_scales uint16 fp16 bits [nb, 64, 18]),
-    uint8 fp8 E4M3 (with kv_scales float32 [nb, 64]) or uint8 q4_0 codes
-    [nb, 64, 288] in Hadamard rotation (with kv_scales uint16 fp16 bits [nb, 64, 18]).
+    uint8 fp8 E4M3 (with kv_scales float32 [nb, 64]), uint8 q4_0 codes
+    [nb, 64, 288] in Hadamard rotation (with kv_scales uint16 fp16 bits [nb, 64, 18])
+    or float64 rows [nb, 64, 576] (no scales).
     rows: optional int64 row ids r = (b * s_q + i) * H + h.
     Returns (out float64 [n, 512], lse float64 [n]); all rows -> shaped [B, s_q, H, ...].
     with_abs: also return out_abs = sum_t p_t |row_t| (same shape as out).
@@ -171,7 +176,7 @@ def decode_absorbed(q, kv, block_table, seqlens, softmax_scale, *, kv_scales=Non
     assert dk == D_K
     kind = _kind(kv)
     kv = _c(kv, kv.dtype)
-    sc = None if kind == 0 else _c(kv_scales, np.float32 if kind == 2 else np.uint16)
+    sc = None if kind in (0, 4) else _c(kv_scales, np.float32 if kind == 2 else np.uint16)
     bt = _c(block_table, np.int32)
     sl = _c(seqlens, np.int32)
     rr = None if rows is None else _c(rows, np.int64)
@@ -308,6 +313,18 @@ def quantize_q4h(x):
     for r in range(rows):
         _load().oracle_quantize_q4h_row(_p(flat[r]), _p(q[r]), _p(sc[r]))
     return q.reshape(x.shape[:-1] + (Q4_ROW_BYTES,)), sc.reshape(x.shape[:-1] + (D_K // 32,))
+
+
+def q4h_dequantize(codes, scales):
+    """The whole q4_0-in-rotation cache read back once, in C (parallel over
+    rows): codes uint8 [..., 288], scales uint16 fp16 bits [..., 18] ->
+    float64 [..., 576], for decode_absorbed over large workloads."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint16)
+    rows = codes.size // Q4_ROW_BYTES
+    out = np.empty(codes.shape[:-1] + (D_K,), np.float64)
+    _load().oracle_q4h_dequantize(rows, _p(codes), _p(scales), _p(out))
+    return out
 
 
 def q4h_rows(codes, scales):

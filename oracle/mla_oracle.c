@@ -273,11 +273,32 @@ void oracle_quantize_q4h_row(const float* x, uint8_t* q, uint16_t* scales) {
   }
 }
 
+/* One cached row of a q4_0 cache in Hadamard rotation, read back: per block
+ * the stored values scale * (code - 8), rotated back by R. */
+void oracle_q4h_row(const uint8_t* codes, const uint16_t* scales, double* dst) {
+  for (int g = 0; g < Q8_GROUPS; ++g) {
+    double y[Q8_GROUP];
+    for (int j = 0; j < Q8_GROUP; ++j) y[j] = oracle_q4_value(oracle_q4_code(codes + 16 * g, j), scales[g]);
+    oracle_hadamard32(y, dst + Q8_GROUP * g);
+  }
+}
+
+/* The same for `rows` consecutive rows (codes [rows, 288], scales [rows, 18],
+ * out double [rows, 576]): the whole cache read back once, so that a decode
+ * of a large workload can run over it as fp64 rows (cache kind 4) instead of
+ * rotating every block back for every query row. */
+void oracle_q4h_dequantize(int64_t rows, const uint8_t* codes, const uint16_t* scales,
+                           double* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    oracle_q4h_row(codes + r * Q4_ROW_BYTES, scales + r * Q8_GROUPS, out + r * D_K);
+}
+
 /* ------------------------------------------------------------ paged cache */
 
 typedef struct {
   int kind; /* 0: bf16 bits, 1: q8_0, 2: fp8 with per-token fp32 scales, 3: q4_0 in
-               Hadamard rotation */
+               Hadamard rotation, 4: fp64 rows */
   const void* kv;
   const void* scales;
   int64_t num_blocks;
@@ -301,15 +322,13 @@ static void cache_row(const cache_view* c, int32_t b, int64_t t, double* dst) {
     const uint8_t* r = (const uint8_t*)c->kv + row * D_K;
     const double s = (double)((const float*)c->scales)[row];
     for (int d = 0; d < D_K; ++d) dst[d] = s * oracle_fp8_value(r[d]);
+  } else if (c->kind == 3) {
+    oracle_q4h_row((const uint8_t*)c->kv + row * Q4_ROW_BYTES,
+                   (const uint16_t*)c->scales + row * Q8_GROUPS, dst);
   } else {
-    /* each block: the stored (rotated) values, rotated back by R */
-    const uint8_t* r = (const uint8_t*)c->kv + row * Q4_ROW_BYTES;
-    const uint16_t* s = (const uint16_t*)c->scales + row * Q8_GROUPS;
-    for (int g = 0; g < Q8_GROUPS; ++g) {
-      double y[Q8_GROUP];
-      for (int j = 0; j < Q8_GROUP; ++j) y[j] = oracle_q4_value(oracle_q4_code(r + 16 * g, j), s[g]);
-      oracle_hadamard32(y, dst + Q8_GROUP * g);
-    }
+    /* rows given as doubles (a cache read back once, e.g. by
+       oracle_q4h_dequantize, for large workloads) */
+    memcpy(dst, (const double*)c->kv + row * D_K, sizeof(double) * D_K);
   }
 }
 
@@ -435,8 +454,9 @@ static int decode_absorbed_core(int32_t B, int32_t s_q, int32_t H, const uint16_
 /*
  * Absorbed-form decode, the contract of the GPU kernel.
  *   q          bf16 bits [B, s_q, H, 576], row r = (b * s_q + i) * H + h
- *   kv         bf16 bits, int8 or fp8 [num_blocks, 64, 576] (kv_kind 0 / 1 / 2), or
- *              q4_0 codes [num_blocks, 64, 288] in Hadamard rotation (kv_kind 3)
+ *   kv         bf16 bits, int8 or fp8 [num_blocks, 64, 576] (kv_kind 0 / 1 / 2),
+ *              q4_0 codes [num_blocks, 64, 288] in Hadamard rotation (kv_kind 3),
+ *              or double [num_blocks, 64, 576] (kv_kind 4, the rows themselves)
  *   kv_scales  fp16 bits [num_blocks, 64, 18] for q8_0 and q4_0, fp32
  *              [num_blocks, 64] for fp8, else NULL
  *   block_table int32 [B, max_blocks]; seqlens int32 [B] (new tokens included)

@@ -5,7 +5,7 @@
  * entry point over small inputs that reach the edge paths (empty and
  * one-token sequences, a tail block, an invalid block id, clamped seqlens, a
  * causal pair, empty and NaN parts in the merge, skipped append rows) for
- * the four cache types. Any out-of-bounds access, use of uninitialised heap,
+ * the four cache types and for rows given as doubles. Any out-of-bounds access, use of uninitialised heap,
  * signed overflow or other undefined behaviour aborts the run; the results
  * themselves are checked by the other oracle tests.
  */
@@ -52,6 +52,8 @@ void oracle_quantize_q8_0_row(const float* x, int8_t* q, uint16_t* scales);
 void oracle_quantize_fp8_row(const float* x, uint8_t* q, float* scale);
 void oracle_quantize_q4h_row(const float* x, uint8_t* q, uint16_t* scales);
 void oracle_hadamard32(const double* x, double* y);
+void oracle_q4h_dequantize(int64_t rows, const uint8_t* codes, const uint16_t* scales,
+                           double* out);
 
 static uint64_t state = 0x9e3779b97f4a7c15ull;
 static uint32_t next_u32(void) {   /* xorshift64*: any deterministic filler will do */
@@ -109,9 +111,11 @@ int main(void) {
   double* out = xmalloc(sizeof(double) * rows * D_L);
   double* lse = xmalloc(sizeof(double) * rows);
   double* oabs = xmalloc(sizeof(double) * rows * D_L);
-  const void* kvs[4] = {kv16, kv8, kvf8, kv4};
-  const void* scs[4] = {NULL, sc16, sc32, sc4};
-  for (int kind = 0; kind < 4; ++kind) {
+  double* kvd = xmalloc(sizeof(double) * NBLK * BT * D_K);
+  oracle_q4h_dequantize((int64_t)NBLK * BT, kv4, sc4, kvd);
+  const void* kvs[5] = {kv16, kv8, kvf8, kv4, kvd};
+  const void* scs[5] = {NULL, sc16, sc32, sc4, NULL};
+  for (int kind = 0; kind < 5; ++kind) {
     if (oracle_decode_absorbed(B, S_Q, H, q, kind, kvs[kind], scs[kind], NBLK, table, MAXB, seqlens,
                                0.07, NULL, 0, out, lse) != 0)
       return 3;
@@ -171,6 +175,7 @@ int main(void) {
                               sc_app[kind]);
 
   free(q); free(kv16); free(kv8); free(sc16); free(kvf8); free(sc32); free(kv4); free(sc4);
+  free(kvd);
   free(out); free(lse);
   free(oabs); free(qn); free(qr); free(wk); free(wv); free(qa); free(o); free(ol); free(po);
   free(new_rows);

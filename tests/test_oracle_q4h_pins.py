@@ -213,3 +213,27 @@ def test_workload_writer_matches_the_oracle_writer_on_rotated_values():
     cg, co = _codes(qg), _codes(qo)
     assert np.mean(cg == co) > 0.999 and np.max(np.abs(cg - co)) <= 1
     assert np.max(np.abs(_fp16_value(sg) / _fp16_value(so) - 1)) < 2.0 ** -10
+
+
+# ---------------------------------------------- read back once, decode as rows
+def test_bulk_read_back_equals_the_independent_dequantisation():
+    w = wl.make_workload("t", 3, 1, 4, [70, 33, 200], seed=37, kv_dtype="q4_0h", table="permuted")
+    rows = oracle.q4h_dequantize(w.kv, w.kv_scales)
+    assert rows.shape == w.kv.shape[:2] + (576,)
+    assert np.allclose(rows, _rows(w.kv, w.kv_scales), rtol=0, atol=1e-12)
+
+
+def test_decode_over_fp64_rows_is_the_decode_over_the_cache_they_hold():
+    # rows given as doubles: exactly the bf16 decode when they are the bf16
+    # values, and the q4_0 decode when they are its read-back rows
+    w = wl.make_workload("t", 3, 2, 4, [1, 70, 130], seed=41, table="permuted")
+    as_f64 = wl.bf16_bits_to_f32(w.kv).astype(np.float64).reshape(w.kv.shape)
+    o0, l0 = oracle.decode_absorbed(w.q, w.kv, w.block_table, w.seqlens, w.softmax_scale)
+    o4, l4 = oracle.decode_absorbed(w.q, as_f64, w.block_table, w.seqlens, w.softmax_scale)
+    assert np.array_equal(o0, o4) and np.array_equal(l0, l4)
+    w = wl.make_workload("t", 3, 2, 4, [1, 70, 130], seed=41, table="permuted", kv_dtype="q4_0h")
+    o3, l3 = oracle.decode_absorbed(w.q, w.kv, w.block_table, w.seqlens, w.softmax_scale,
+                                    kv_scales=w.kv_scales)
+    rows = oracle.q4h_dequantize(w.kv, w.kv_scales)
+    o4, l4 = oracle.decode_absorbed(w.q, rows, w.block_table, w.seqlens, w.softmax_scale)
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
