@@ -216,26 +216,30 @@ def test_empty_rows_and_causal_visibility(H):
         assert np.all(np.isneginf(lse[1, 0])) and np.all(np.isfinite(lse[1, 1]))
 
 
-def test_invalid_block_ids_poison_only_their_sequence():
-    w = wl.make_workload("bad", 3, 1, 128, [300, 300, 300], seed=10)
+@pytest.mark.parametrize("kvd", ["bf16", "q8_0", "fp8", "q4_0h"])
+def test_invalid_block_ids_poison_only_their_sequence(kvd):
+    w = wl.make_workload("bad", 3, 1, 128, [300, 300, 300], seed=10, kv_dtype=kvd)
     w.block_table[1, 2] = w.num_blocks + 5
     for parts in (1, 4, 48):   # 48: the combine's four-waves-per-row form
         out, lse, _ = run_gpu(w, num_parts=parts)
-        compare(out, lse, *oracle_rows(w), what=f"invalid ids P={parts}")
+        compare(out, lse, *oracle_rows(w), what=f"invalid ids {kvd} P={parts}", kv_dtype=kvd)
         assert np.all(np.isnan(lse[1])) and np.all(np.isnan(out[1]))
     w.block_table[1, 2] = -1
     out, lse, _ = run_gpu(w, num_parts=2)
     assert np.all(np.isnan(lse[1])) and np.all(np.isfinite(lse[[0, 2]]))
 
 
-def test_invalid_block_id_in_a_later_id_window():
-    """16-row tile: block ids are read 64 at a time; a bad id in the second
-    window of a long segment poisons that sequence only."""
-    w = wl.make_workload("bad2", 3, 1, 16, [300, 4500, 700], seed=11)
+@pytest.mark.parametrize("H,kvd", [(16, "bf16"), (128, "bf16"), (128, "q8_0"), (128, "fp8"),
+                                   (128, "q4_0h")])
+def test_invalid_block_id_in_a_later_id_window(H, kvd):
+    """Block ids are read 64 at a time (16- and 128-row kernels); a bad id in
+    the second window of a long segment poisons that sequence only."""
+    w = wl.make_workload("bad2", 3, 1, H, [300, 4500, 700], seed=11, kv_dtype=kvd)
     w.block_table[1, 66] = w.num_blocks + 1
     for parts in (1, 3, 48):
         out, lse, _ = run_gpu(w, num_parts=parts)
-        compare(out, lse, *oracle_rows(w), what=f"invalid id, later window P={parts}")
+        compare(out, lse, *oracle_rows(w), what=f"invalid id, later window {kvd} H={H} P={parts}",
+                kv_dtype=kvd)
         assert np.all(np.isnan(lse[1])) and np.all(np.isnan(out[1]))
         assert np.all(np.isfinite(lse[[0, 2]]))
 
