@@ -299,6 +299,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 
+// x - h, for h the bf16 pair holding bf16(x) in its low or high half: one
+// v_dot2c_f32_bf16, h times sel plus x, with sel the bf16 pair (-1, 0)
+// (bits 0x0000BF80) or (0, -1) (0xBF800000) held in a register (see
+// DotSel). The products are exact and so is the difference (h is x
+// rounded), so the result is exact whatever the order of the additions.
+__device__ __forceinline__ float lo_part(uint32_t h, float x, uint32_t sel) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, h), __builtin_bit_cast(bf16x2v, sel),
+                                         x, false);
+}
+// The two selectors of lo_part in VGPRs. Left to the compiler, 0x0000BF80
+// becomes the inline constant -1.0, which the hardware reads as the 32-bit
+// pattern 0xBF800000, i.e. the other half (measured).
+struct DotSel {
+  uint32_t lo = 0x0000BF80u, hi = 0xBF800000u;
+  __device__ DotSel() { asm volatile("" : "+v"(lo), "+v"(hi)); }
+};
+
 // Decode kernel with the work of each 32-row group split over CG waves (the
 // q8_0 cache and the q4_0 cache in Hadamard rotation: HG = 1 or 2 row groups,
 // CG = 4). The 576-column score
@@ -2101,8 +2119,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       } else {
         const uint32_t dst = lds_addr_of(s_stage(idx % NST)) + 1024 * wave;
         const uint8_t* src = tile_src(idx);
+        // a tile past the last one is never used: its lanes all read one line
+        const uint32_t d = idx < n_run ? doff : 0u;
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) copy(src + 128 * j, doff, dst + 4096 * j);
+        for (int j = 0; j < LPW; ++j) copy(src + 128 * j, d, dst + 4096 * j);
       }
     };
     // copies this wave issues per tile
@@ -2244,6 +2264,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       const uint8_t* nsrc = a.kv + nrow0 * (FP8 ? kDK : kRowBytes);
       const uint8_t* nssrc = a.kv_scales + nrow0 * 4;   // fp8 only
       const uint32_t ndst = lds_addr_of(s_stage((it + 2) % NST)) + (FP8 ? 0 : 1024 * wave);
+      // The loop's last two iterations copy a tile that is never used (the
+      // copies stay in the code so that every iteration is the same); their
+      // lanes all read the first 16 bytes of the clamped tile, one cache line
+      // per instruction instead of eight.
+      const uint32_t ndoff = it + 2 < n_run ? doff : 0u;
 
       // value step q = (kk, cb, rb) with kk = q / 16, cb = (q / 4) % 4,
       // rb = q % 4: O^T block (rb, cb) += V^T (column block cb, token half kk)
@@ -2322,7 +2347,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         if constexpr (FP8) {
           if constexpr ((k & 7) == 1) copy8(nsrc, nssrc, ndst, k >> 3);
         } else {
-          if constexpr ((k & 3) == 1) copy(nsrc + 128 * (k >> 2), doff, ndst + 4096 * (k >> 2));
+          if constexpr ((k & 3) == 1) copy(nsrc + 128 * (k >> 2), ndoff, ndst + 4096 * (k >> 2));
         }
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -2795,12 +2820,22 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
         };
         LDS_AS uint8_t* hib = (LDS_AS uint8_t*)s_hl[0];
         LDS_AS uint8_t* lob = (LDS_AS uint8_t*)s_hl[1];
-        for (int g = wave; g < 18; g += NW) {
+        const DotSel sel;
+        // the codes and scale of block g + 4 are read while block g is
+        // converted (the last block re-reads block 17)
+        auto rd_codes = [&](int g, uint32_t& w0, uint32_t& w1, uint16_t& sbits) {
           const LDS_AS uint8_t* cu = st + kQ4RowBytes * l32 + 16 * g;
-          const uint32_t w0 = *reinterpret_cast<const LDS_AS uint32_t*>(cu + 4 * hi);
-          const uint32_t w1 = *reinterpret_cast<const LDS_AS uint32_t*>(cu + 8 + 4 * hi);
-          const uint16_t sbits = *reinterpret_cast<const LDS_AS uint16_t*>(
-              st + SCALE_OFF + kQ8ScaleRowBytes * l32 + 2 * g);
+          w0 = *reinterpret_cast<const LDS_AS uint32_t*>(cu + 4 * hi);
+          w1 = *reinterpret_cast<const LDS_AS uint32_t*>(cu + 8 + 4 * hi);
+          sbits = *reinterpret_cast<const LDS_AS uint16_t*>(st + SCALE_OFF + kQ8ScaleRowBytes * l32 + 2 * g);
+        };
+        uint32_t nw0, nw1;
+        uint16_t nsb;
+        rd_codes(wave, nw0, nw1, nsb);
+        for (int g = wave; g < 18; g += NW) {
+          const uint32_t w0 = nw0, w1 = nw1;
+          const uint16_t sbits = nsb;
+          rd_codes(min(g + NW, 17), nw0, nw1, nsb);
           const float dv = tok_ok ? (float)__builtin_bit_cast(_Float16, sbits) * kInvSqrt32 : 0.f;
           const f32x16 zero4 = {};
           f32x16 n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA0, nib8(w0), zero4, 0, 0, 0);
@@ -2813,8 +2848,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
             for (int e2 = 0; e2 < 2; ++e2) {
               const float x0 = dv * n[4 * q + 2 * e2], x1 = dv * n[4 * q + 2 * e2 + 1];
               h[e2] = pack_bf16x2(x0, x1);
-              lo[e2] = pack_bf16x2(x0 - __builtin_bit_cast(float, h[e2] << 16),
-                                   x1 - __builtin_bit_cast(float, h[e2] & 0xffff0000u));
+              lo[e2] = pack_bf16x2(lo_part(h[e2], x0, sel.lo), lo_part(h[e2], x1, sel.hi));
             }
             const int u = 16 * rg_unit(l32, 4 * g + q) + 8 * hi;
             *reinterpret_cast<LDS_AS uint64_t*>(hib + u) = (uint64_t)h[0] | ((uint64_t)h[1] << 32);
@@ -2846,6 +2880,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
           sc2[i] = scl[i];   // scales of groups 2i, 2i+1; chunk 8i + cc is group 2i + (cc >> 2)
         }
         const int sh16 = 16 * (cc >> 2);
+        const DotSel sel;
 #pragma unroll
         for (int i = 0; i < 9; ++i) {
           // the scale is zeroed too: a NaN or infinite scale in an unused
@@ -2859,10 +2894,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
             const float x0 = d * (float)(int8_t)(word >> (16 * (e2 & 1)));
             const float x1 = d * (float)(int8_t)(word >> (16 * (e2 & 1) + 8));
             const uint32_t h = pack_bf16x2(x0, x1);
-            const float h0 = __builtin_bit_cast(float, h << 16);
-            const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
             whi[e2] = h;
-            wlo[e2] = pack_bf16x2(x0 - h0, x1 - h1);
+            wlo[e2] = pack_bf16x2(lo_part(h, x0, sel.lo), lo_part(h, x1, sel.hi));
           }
           const int U = tid + NTH * i;
           *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[0] + 16 * U) = whi;
