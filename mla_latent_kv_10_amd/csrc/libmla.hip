@@ -2820,6 +2820,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
         };
         LDS_AS uint8_t* hib = (LDS_AS uint8_t*)s_hl[0];
         LDS_AS uint8_t* lob = (LDS_AS uint8_t*)s_hl[1];
+        // (the lo parts by lo_part: measured faster here, where each block is a
+        // dependent chain, and slower in the q8_0 conversion below)
         const DotSel sel;
         // the codes and scale of block g + 4 are read while block g is
         // converted (the last block re-reads block 17)
@@ -2880,7 +2882,6 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
           sc2[i] = scl[i];   // scales of groups 2i, 2i+1; chunk 8i + cc is group 2i + (cc >> 2)
         }
         const int sh16 = 16 * (cc >> 2);
-        const DotSel sel;
 #pragma unroll
         for (int i = 0; i < 9; ++i) {
           // the scale is zeroed too: a NaN or infinite scale in an unused
@@ -2894,8 +2895,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
             const float x0 = d * (float)(int8_t)(word >> (16 * (e2 & 1)));
             const float x1 = d * (float)(int8_t)(word >> (16 * (e2 & 1) + 8));
             const uint32_t h = pack_bf16x2(x0, x1);
+            const float h0 = __builtin_bit_cast(float, h << 16);
+            const float h1 = __builtin_bit_cast(float, h & 0xffff0000u);
             whi[e2] = h;
-            wlo[e2] = pack_bf16x2(lo_part(h, x0, sel.lo), lo_part(h, x1, sel.hi));
+            wlo[e2] = pack_bf16x2(x0 - h0, x1 - h1);
           }
           const int U = tid + NTH * i;
           *reinterpret_cast<LDS_AS u32x4*>((LDS_AS uint8_t*)s_hl[0] + 16 * U) = whi;
