@@ -205,31 +205,81 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 // Block-wide exclusive prefix of cache blocks per sequence: s_pre[0..B].
 // Every thread of the workgroup (NT threads) must call it.
+// x shifted by n lanes up within each row of 16 lanes, 0 below: one DPP move
+template <int N>
+__device__ __forceinline__ int row_shr(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, 0x110 + N, 0xf, 0xf, true);
+}
+
+// Block prefix of the batch: s_pre[b] = blocks of sequences 0..b-1 (B + 1
+// entries). Thread t takes sequences t*per .. t*per + per - 1 and keeps their
+// block counts in registers; the scan is in-wave (DPP within rows of 16
+// lanes, then the row totals by readlane) and across the waves through
+// s_wsum[0..3]. Also sets s_wsum[8] = INT_MAX, s_wsum[9] = -1 for part_range.
 template <int NT>
 __device__ void plan_prefix(const int32_t* __restrict__ seqlens, int B, int max_blocks,
                             int* s_pre, int* s_wsum) {
+  constexpr int PER = (kMaxBatch + NT - 1) / NT;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int per = (B + NT - 1) / NT;
-  const int lo = min(B, t * per), hi = min(B, lo + per);
-  int local = 0;
-  for (int b = lo; b < hi; ++b) local += nblocks_of(seqlens[b], max_blocks);
-  int x = local;
+  const int lo = min(B, t * per);
+  int nb[PER];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
+  for (int k = 0; k < PER; ++k)   // all loads first (per is uniform)
+    if (k < per) nb[k] = seqlens[min(lo + k, max(B - 1, 0))];
+  int local = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    nb[k] = k < per && lo + k < B ? nblocks_of(nb[k], max_blocks) : 0;
+    local += nb[k];
   }
+  int x = local;
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  x += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);   // inclusive
   if (lane == 63) s_wsum[w] = x;
+  if (t == 0) {
+    s_wsum[8] = 0x7fffffff;
+    s_wsum[9] = -1;
+  }
   __syncthreads();
   int base = 0;
   for (int i = 0; i < w; ++i) base += s_wsum[i];
   int run = base + x - local;
-  for (int b = lo; b < hi; ++b) {
-    s_pre[b] = run;
-    run += nblocks_of(seqlens[b], max_blocks);
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    if (k < per && lo + k < B) s_pre[lo + k] = run;
+    run += nb[k];
   }
   if (t == NT - 1) s_pre[B] = base + x;
   __syncthreads();
+}
+
+// The sequences of part `part` (block range [p_lo, p_hi) of the T blocks)
+// form a contiguous range [b_first, b_last], empty when b_first > b_last: a
+// sequence with blocks belongs to every part whose range meets its own, one
+// without blocks to the part that holds its position (the last part when
+// the position is T). Uses s_misc[8..9] as plan_prefix left them.
+template <int NT>
+__device__ void part_range(const int* s_pre, int B, int T, bool last_part, int p_lo, int p_hi,
+                           int* s_misc, int& b_first, int& b_last) {
+  for (int b = threadIdx.x; b < B; b += NT) {
+    const int lo = s_pre[b], hi2 = s_pre[b + 1];
+    const bool mine = hi2 > lo ? lo < p_hi && hi2 > p_lo
+                               : (lo < T ? lo >= p_lo && lo < p_hi : last_part);
+    if (mine) {
+      atomicMin(&s_misc[8], b);
+      atomicMax(&s_misc[9], b);
+    }
+  }
+  __syncthreads();
+  b_first = uniform(s_misc[8]);
+  b_last = uniform(s_misc[9]);
 }
 
 // ------------------------------------------------------------ decode kernel
@@ -387,28 +437,9 @@ __global__ __launch_bounds__(64 * HG * CG, 1) void mla_decode_kernel(DecodeParam
   const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
 
   // Sequences of this part form a contiguous range [b_first, b_last].
-  if (tid == 0) {
-    s_misc[8] = 0x7fffffff;
-    s_misc[9] = -1;
-    s_raise[0] = s_raise[1] = 0;
-  }
-  __syncthreads();
-  for (int b = tid; b < a.B; b += NT) {
-    const int lo = s_pre[b], hi2 = s_pre[b + 1];
-    bool mine;
-    if (hi2 > lo) {
-      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
-    } else {
-      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
-      mine = owner == part;
-    }
-    if (mine) {
-      atomicMin(&s_misc[8], b);
-      atomicMax(&s_misc[9], b);
-    }
-  }
-  __syncthreads();
-  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+  if (tid == 0) s_raise[0] = s_raise[1] = 0;
+  int b_first, b_last;
+  part_range<NT>(s_pre, a.B, T, part == P - 1, p_lo, p_hi, s_misc, b_first, b_last);
 
   const int r = mt * MT + hg * 32 + l32;     // this lane's query row in its sequence
   const bool row_ok = r < a.M;
@@ -1083,28 +1114,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_rows_kernel(DecodeParams a)
   if (blockIdx.x == 0)
     for (int b = tid; b <= a.B; b += NT) a.ws_prefix[b] = s_pre[b];
   const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
-
-  if (tid == 0) {
-    s_misc[8] = 0x7fffffff;
-    s_misc[9] = -1;
-  }
-  __syncthreads();
-  for (int b = tid; b < a.B; b += NT) {
-    const int lo = s_pre[b], hi2 = s_pre[b + 1];
-    bool mine;
-    if (hi2 > lo) {
-      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
-    } else {
-      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
-      mine = owner == part;
-    }
-    if (mine) {
-      atomicMin(&s_misc[8], b);
-      atomicMax(&s_misc[9], b);
-    }
-  }
-  __syncthreads();
-  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+  int b_first, b_last;
+  part_range<NT>(s_pre, a.B, T, part == P - 1, p_lo, p_hi, s_misc, b_first, b_last);
 
   const int r = mt * MT + hg * 32 + l32;     // this lane's query row in its sequence
   const bool row_ok = r < a.M;
@@ -1492,27 +1503,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_narrow_kernel(DecodeParams 
   if (blockIdx.x == 0)
     for (int b = tid; b <= a.B; b += NT) a.ws_prefix[b] = s_pre[b];
   const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
-  if (tid == 0) {
-    s_misc[8] = 0x7fffffff;
-    s_misc[9] = -1;
-  }
-  __syncthreads();
-  for (int b = tid; b < a.B; b += NT) {
-    const int lo = s_pre[b], hi2 = s_pre[b + 1];
-    bool mine;
-    if (hi2 > lo) {
-      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
-    } else {
-      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
-      mine = owner == part;
-    }
-    if (mine) {
-      atomicMin(&s_misc[8], b);
-      atomicMax(&s_misc[9], b);
-    }
-  }
-  __syncthreads();
-  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+  int b_first, b_last;
+  part_range<NT>(s_pre, a.B, T, part == P - 1, p_lo, p_hi, s_misc, b_first, b_last);
   const int pre_first = b_first <= b_last ? uniform(s_pre[b_first]) : 0;
   __syncthreads();   // ring stage 3 is free from here on
   if (b_first > b_last) return;
@@ -1953,28 +1945,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   if (blockIdx.x == 0)
     for (int b = tid; b <= a.B; b += NTH) a.ws_prefix[b] = s_pre[b];
   const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
-
-  if (tid == 0) {
-    s_misc[8] = 0x7fffffff;
-    s_misc[9] = -1;
-  }
-  __syncthreads();
-  for (int b = tid; b < a.B; b += NTH) {
-    const int lo = s_pre[b], hi2 = s_pre[b + 1];
-    bool mine;
-    if (hi2 > lo) {
-      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
-    } else {
-      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
-      mine = owner == part;
-    }
-    if (mine) {
-      atomicMin(&s_misc[8], b);
-      atomicMax(&s_misc[9], b);
-    }
-  }
-  __syncthreads();
-  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+  int b_first, b_last;
+  part_range<NTH>(s_pre, a.B, T, part == P - 1, p_lo, p_hi, s_misc, b_first, b_last);
   int pre_b = b_first <= b_last ? uniform(s_pre[b_first]) : 0;
   __syncthreads();   // ring stage 3 is free from here on
 
@@ -2627,28 +2599,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
   if (blockIdx.x == 0)
     for (int b = tid; b <= a.B; b += NTH) a.ws_prefix[b] = s_pre[b];
   const int p_lo = part_start(part, P, T), p_hi = part_start(part + 1, P, T);
-
-  if (tid == 0) {
-    s_misc[8] = 0x7fffffff;
-    s_misc[9] = -1;
-  }
-  __syncthreads();
-  for (int b = tid; b < a.B; b += NTH) {
-    const int lo = s_pre[b], hi2 = s_pre[b + 1];
-    bool mine;
-    if (hi2 > lo) {
-      mine = part_of(lo, P, T) <= part && part <= part_of(hi2 - 1, P, T);
-    } else {
-      const int owner = lo < T ? part_of(lo, P, T) : P - 1;
-      mine = owner == part;
-    }
-    if (mine) {
-      atomicMin(&s_misc[8], b);
-      atomicMax(&s_misc[9], b);
-    }
-  }
-  __syncthreads();
-  const int b_first = uniform(s_misc[8]), b_last = uniform(s_misc[9]);
+  int b_first, b_last;
+  part_range<NTH>(s_pre, a.B, T, part == P - 1, p_lo, p_hi, s_misc, b_first, b_last);
   int pre_b = b_first <= b_last ? uniform(s_pre[b_first]) : 0;
   __syncthreads();   // the hi / lo tiles are free from here on
 
@@ -3287,7 +3239,7 @@ __global__ __launch_bounds__(kThreads) void mla_plan_kernel(const int32_t* seqle
                                                             int max_blocks, int P,
                                                             int32_t* plan) {
   __shared__ int pre[kMaxBatch + 1];
-  __shared__ int wsum[8];
+  __shared__ int wsum[16];
   plan_prefix<kThreads>(seqlens, B, max_blocks, pre, wsum);
   const int T = pre[B];
   int32_t* o_pre = plan;
