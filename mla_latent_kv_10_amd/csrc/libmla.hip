@@ -150,19 +150,6 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds_addr + 16 * l (global_load_lds_dwordx4, M0 = LDS base). Issued as
-// inline asm so that the compiler's wait-count pass, which cannot tell which
-// ring stage a DMA targets, does not serialise every later LDS read behind
-// it; ordering comes from the explicit vmcnt waits and LDS barriers. There is
-// no VGPR destination; the address VGPRs are read at issue.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(lds_addr)
-               : "memory", "m0");
-}
-
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const LDS_AS void*)p;
 }
@@ -299,8 +286,14 @@ __device__ void part_range(const int* s_pre, int B, int T, bool last_part, int p
 constexpr float kRescaleThreshold = 48.0f;
 constexpr float kRefHeadroom = 48.0f;
 
-// LDS-DMA with an SGPR base and a per-lane 32-bit offset (no per-tile
-// address arithmetic); lane l's 16 bytes land at lds_addr + 16 l.
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4, M0 = LDS base), from an SGPR base and a per-lane
+// 32-bit offset (no per-tile address arithmetic); lane l's 16 bytes land at
+// lds_addr + 16 l. Issued as inline asm so that the compiler's wait-count
+// pass, which cannot tell which ring stage a DMA targets, does not serialise
+// every later LDS read behind it; ordering comes from the explicit vmcnt
+// waits and LDS barriers. There is no VGPR destination; the offset VGPR is
+// read at issue.
 __device__ __forceinline__ void dma16_sbase(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
@@ -2775,8 +2768,19 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
         // (the lo parts by lo_part: measured faster here, where each block is a
         // dependent chain, and slower in the q8_0 conversion below)
         const DotSel sel;
-        // the codes and scale of block g + 4 are read while block g is
-        // converted (the last block re-reads block 17)
+        // x = d / sqrt(32) * n for four consecutive rows m of one token, and
+        // its hi / lo parts, to the 8 bytes at u of the two tiles
+        auto put4 = [&](float dv, float n0, float n1, float n2, float n3, int u) {
+          const float x0 = dv * n0, x1 = dv * n1, x2 = dv * n2, x3 = dv * n3;
+          const uint32_t h0 = pack_bf16x2(x0, x1), h1 = pack_bf16x2(x2, x3);
+          const uint32_t l0 = pack_bf16x2(lo_part(h0, x0, sel.lo), lo_part(h0, x1, sel.hi));
+          const uint32_t l1 = pack_bf16x2(lo_part(h1, x2, sel.lo), lo_part(h1, x3, sel.hi));
+          *reinterpret_cast<LDS_AS uint64_t*>(hib + u) = (uint64_t)h0 | ((uint64_t)h1 << 32);
+          *reinterpret_cast<LDS_AS uint64_t*>(lob + u) = (uint64_t)l0 | ((uint64_t)l1 << 32);
+        };
+        // Blocks 0..15: wave w converts w, w + 4, w + 8, w + 12, reading the
+        // codes and scale of the next one while the current one converts
+        // (the last read is not used).
         auto rd_codes = [&](int g, uint32_t& w0, uint32_t& w1, uint16_t& sbits) {
           const LDS_AS uint8_t* cu = st + kQ4RowBytes * l32 + 16 * g;
           w0 = *reinterpret_cast<const LDS_AS uint32_t*>(cu + 4 * hi);
@@ -2786,28 +2790,61 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
         uint32_t nw0, nw1;
         uint16_t nsb;
         rd_codes(wave, nw0, nw1, nsb);
-        for (int g = wave; g < 18; g += NW) {
+        // the half block's codes and scale (below) are read now as well
+        const int gh = 16 + (wave >> 1);
+        const int th = 16 * (wave & 1) + (lane & 15), qd = lane >> 4;
+        const uint32_t wh = *reinterpret_cast<const LDS_AS uint32_t*>(st + kQ4RowBytes * th + 16 * gh + 4 * qd);
+        const uint16_t sbh = *reinterpret_cast<const LDS_AS uint16_t*>(st + SCALE_OFF + kQ8ScaleRowBytes * th + 2 * gh);
+        for (int g = wave; g < 16; g += NW) {
           const uint32_t w0 = nw0, w1 = nw1;
           const uint16_t sbits = nsb;
-          rd_codes(min(g + NW, 17), nw0, nw1, nsb);
+          rd_codes(min(g + NW, 15), nw0, nw1, nsb);
           const float dv = tok_ok ? (float)__builtin_bit_cast(_Float16, sbits) * kInvSqrt32 : 0.f;
           const f32x16 zero4 = {};
           f32x16 n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA0, nib8(w0), zero4, 0, 0, 0);
           n = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hA1, nib8(w1), n, 0, 0, 0);
           if (hi == 0) n[0] -= 4352.f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t h[2], lo[2];
+          for (int q = 0; q < 4; ++q)
+            put4(dv, n[4 * q], n[4 * q + 1], n[4 * q + 2], n[4 * q + 3],
+                 16 * rg_unit(l32, 4 * g + q) + 8 * hi);
+        }
+        // Blocks 16 and 17, split by token halves so that every wave converts
+        // four and a half blocks: wave w takes tokens 16 (w & 1) .. + 15 of
+        // block 16 + (w >> 1) on 16x16x32 MFMAs. Lane l: token
+        // th = 16 (w & 1) + (l & 15); A = H rows m = l & 15 (second MFMA
+        // m + 16) at columns k = 8 (l >> 4) + e; B = codes k = 8 (l >> 4) + e
+        // of token th (word l >> 4 of its 16 bytes); the results hold
+        // n[m][th] for m = 4 (l >> 4) + (0..3) and m + 16.
+        {
+          // (the lane index is made opaque so that the H operands below are
+          // formed here, not hoisted out of the tile loop and kept, spilled)
+          int lx = lane;
+          asm volatile("" : "+v"(lx));
+          const int g = gh, l16 = lx & 15;
+          // sign of H[m][k] = parity(m & k) = parity(l16 & 8 qd) ^ parity(l16 & e)
+          // (^ (qd >> 1) for m + 16); bit e of byte r of the table is
+          // parity(r & e)
+          const uint32_t rmask = (uint32_t)(0x963C5AF066CCAA00ull >> (8 * (l16 & 7)));
+          const uint32_t s0 = ((l16 >> 3) & qd & 1) ? 0x80008000u : 0u;
+          const uint32_t s1 = (qd & 2) ? 0x80008000u : 0u;
+          u32x4 ha, hb;
 #pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-              const float x0 = dv * n[4 * q + 2 * e2], x1 = dv * n[4 * q + 2 * e2 + 1];
-              h[e2] = pack_bf16x2(x0, x1);
-              lo[e2] = pack_bf16x2(lo_part(h[e2], x0, sel.lo), lo_part(h[e2], x1, sel.hi));
-            }
-            const int u = 16 * rg_unit(l32, 4 * g + q) + 8 * hi;
-            *reinterpret_cast<LDS_AS uint64_t*>(hib + u) = (uint64_t)h[0] | ((uint64_t)h[1] << 32);
-            *reinterpret_cast<LDS_AS uint64_t*>(lob + u) = (uint64_t)lo[0] | ((uint64_t)lo[1] << 32);
+          for (int j = 0; j < 4; ++j) {
+            ha[j] = 0x3F803F80u | (((rmask >> (2 * j)) & 1u) << 15) | (((rmask >> (2 * j + 1)) & 1u) << 31);
+            ha[j] ^= s0;
+            hb[j] = ha[j] ^ s1;
           }
+          const bf16x8 a0 = __builtin_bit_cast(bf16x8, ha), a1 = __builtin_bit_cast(bf16x8, hb);
+          const uint32_t w = wh;
+          const float dv = th < valid ? (float)__builtin_bit_cast(_Float16, sbh) * kInvSqrt32 : 0.f;
+          const f32x4 zero4 = {};
+          f32x4 n0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, nib8(w), zero4, 0, 0, 0);
+          const f32x4 n1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, nib8(w), zero4, 0, 0, 0);
+          if (qd == 0) n0[0] -= 4352.f;
+          // rows 4 qd .. 4 qd + 3 are half (qd & 1) of chunk 4 g + (qd >> 1)
+          put4(dv, n0[0], n0[1], n0[2], n0[3], 16 * rg_unit(th, 4 * g + (qd >> 1)) + 8 * (qd & 1));
+          put4(dv, n1[0], n1[1], n1[2], n1[3], 16 * rg_unit(th, 4 * g + 2 + (qd >> 1)) + 8 * (qd & 1));
         }
       } else {
         // Thread (w, l) converts unit 256 i + 64 w + l of the hi / lo tiles,

@@ -207,6 +207,72 @@ def test_q4_hadamard_product_and_tile_writes():
         assert len(seen) == 32 * 32
 
 
+def _rg_unit(t, c):
+    R, r, C, cc = t >> 3, t & 7, c >> 3, c & 7
+    return 64 * (4 * C + R) + ((r & 3) | ((((r >> 2) ^ cc) & 1) << 2) | (((R ^ (cc >> 1)) & 1) << 3)
+                               | ((cc & 1) << 4) | (((cc >> 2) & 1) << 5))
+
+
+def test_q4_half_blocks_of_the_128_row_kernel():
+    """Blocks 16 and 17 of a tile are converted by token halves on 16x16x32
+    MFMAs: the H operands built from the sign table equal H[m][k]; the
+    product of lane (l & 15, l >> 4) gives n[m][th] for m = 4 (l >> 4) + i
+    (and + 16); together with the full blocks 0..15 (four per wave) every
+    8-byte half-unit of both tiles is written exactly once, with the rows
+    it holds."""
+    import numpy as np
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 16, size=(32, 32))          # one block: [token, code index]
+    packed = np.zeros((32, 16), np.int64)
+    for j in range(32):
+        packed[:, j // 2] |= codes[:, j] << (4 * (j & 1))
+    H = np.array([[_hadamard(m, j) for j in range(32)] for m in range(32)])
+    want = H @ (codes.T - 8)                             # n[m][t]
+    writes = {}
+    for w in range(4):
+        for g in range(w, 16, 4):                        # full blocks: lane (t, hi), 4 q
+            for t, hi, q in itertools.product(range(32), range(2), range(4)):
+                key = (_rg_unit(t, 4 * g + q), hi)
+                assert key not in writes
+                writes[key] = (g, t, [8 * q + 4 * hi + i for i in range(4)])
+        g = 16 + (w >> 1)
+        for lane in range(64):
+            l16, qd = lane & 15, lane >> 4
+            th = 16 * (w & 1) + l16
+            rmask = (0x963C5AF066CCAA00 >> (8 * (l16 & 7))) & 0xFFFFFFFF
+            s0 = 0x80008000 if ((l16 >> 3) & qd & 1) else 0
+            s1 = 0x80008000 if (qd & 2) else 0
+            a0, a1 = [], []
+            for j in range(4):
+                ha = 0x3F803F80 | (((rmask >> (2 * j)) & 1) << 15) | (((rmask >> (2 * j + 1)) & 1) << 31)
+                ha ^= s0
+                for h in range(2):
+                    a0.append(-1 if (ha >> (16 * h + 15)) & 1 else 1)
+                    a1.append(-1 if ((ha ^ s1) >> (16 * h + 15)) & 1 else 1)
+            assert a0 == [_hadamard(l16, 8 * qd + e) for e in range(8)]
+            assert a1 == [_hadamard(l16 + 16, 8 * qd + e) for e in range(8)]
+            # word qd of the token's 16 bytes holds codes 8 qd .. 8 qd + 7
+            wd = sum(int(packed[th, 4 * qd + i]) << (8 * i) for i in range(4))
+            assert [(wd >> (4 * e)) & 0xF for e in range(8)] == list(codes[th, 8 * qd:8 * qd + 8])
+            for base, off in ((0, 0), (16, 2)):
+                key = (_rg_unit(th, 4 * g + off + (qd >> 1)), qd & 1)
+                assert key not in writes
+                writes[key] = (g, th, [base + 4 * qd + i for i in range(4)])
+    assert len(writes) == 32 * 72 * 2
+    for (u, half), (g, t, rows) in writes.items():
+        # the half-unit belongs to token t, chunk c with rows 8 (c % 4) + 4 half ..
+        c = [c for c in range(72) if _rg_unit(t, c) == u]
+        assert len(c) == 1 and c[0] // 4 == g
+        assert rows == [8 * (c[0] % 4) + 4 * half + i for i in range(4)]
+    # the product over 16x16x32 (rows m, 16 tokens, k = 32 codes) is n
+    for h in range(2):
+        for m in range(32):
+            for n in range(16):
+                t = 16 * h + n
+                acc = sum(_hadamard(m, k) * (128 + codes[t, k]) for k in range(32))
+                assert acc - (4352 if m == 0 else 0) == want[m, t]
+
+
 def test_q4_code_copies_of_the_64_row_kernel():
     # load k < 9: lane (l32, hi) reads 16 bytes at l32 * 288 + (2k + hi) * 16
     # into unit 64 k + l, which must be unit 32 g + t of block g = 2k + hi,
