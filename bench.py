@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -37,10 +38,16 @@ WORKLOAD_CFG = 2                 # 64 x 128 heads x 4096 tokens, bf16 cache
 
 
 def source_hash() -> str:
+    """Hash of the decode kernels' code (libmla.hip and mla.h) with comments
+    and blank space left out, so that a profile stays matched to the code
+    it measured across edits of comments only."""
     h = hashlib.sha256()
-    for rel in ("mla_latent_kv_10_amd/csrc/libmla.hip", "include/mla.h"):   # the decode kernels
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for rel in ("mla_latent_kv_10_amd/csrc/libmla.hip", "include/mla.h"):
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -2747,7 +2747,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_q8w_kernel(DecodeParams a) 
       lds_barrier();
       if (it + 2 < n_run) issue(it + 2);
       if constexpr (Q4) {
-        // Wave w converts blocks g = w, w + 4, ...: n = H (c - 8) by two MFMAs
+        // Wave w converts blocks g = w, w + 4, w + 8, w + 12 and half of
+        // block 16 or 17 (below): n = H (c - 8) by two MFMAs
         // (H rows against the codes as bf16(128 + c), bits 0x4300 | c, which
         // adds 4352 to row m = 0 only, taken off), then x = d / sqrt(32) * n
         // and its hi / lo parts. Lane (t, hi) holds n[m][t] for
