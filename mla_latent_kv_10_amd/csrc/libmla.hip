@@ -1876,11 +1876,11 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
 //    product's B-operand layout) through LDS;
 //  * accumulates the value product of all 128 rows for output columns
 //    128w..128w+127, so each V^T operand read from LDS feeds four MFMAs.
-// The value product of tile i-1 is interleaved with the score product of
-// tile i: the independent value MFMAs fill the latency of the dependent score
-// chain, and the transposing V reads mix with the score operand reads. A
-// 4-stage ring keeps tile i-1 resident while tile i is scored and tiles i+1,
-// i+2 stream in. The reference maximum of the online softmax moves rarely;
+// Iteration i runs the dependent score chain of tile i (phase A, with the
+// copies of tile i+2 and the first V reads of tile i-1 in its shadow), then
+// the value product of tile i-1 with the online softmax of tile i cut into
+// short VALU steps between its MFMAs (phase B). A 4-stage ring keeps tile
+// i-1 resident while tile i is scored and tiles i+1, i+2 stream in. The reference maximum of the online softmax moves rarely;
 // when a row's does, its owner publishes the factor and every wave rescales
 // that row's accumulators. The plan prefix and the epilogue's scratch live in
 // ring space that is idle at those times, which keeps LDS under 160 KiB.
