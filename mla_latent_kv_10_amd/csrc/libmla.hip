@@ -2524,8 +2524,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
 // Quantised cache (q8_0; with Q4 the q4_0 cache in Hadamard rotation), 128
 // query rows per workgroup, 4 waves; wave w computes the scores and the
 // softmax of rows 32w..32w+31 and the value product of all 128 rows for
-// output columns 128w..128w+127 (the division of the 128-row bf16 kernel). Per 32-token tile, in four phases separated by
-// barriers:
+// output columns 128w..128w+127 (the division of the 128-row bf16 kernel).
+// Per 32-token tile, in four phases separated by barriers:
 //  1. the int8 tile (18 KiB) and its scales (1152 B), copied by LDS-DMA into a
 //     3-stage ring, are converted once by all threads into two bf16 tiles in
 //     the row-group layout: hi = bf16(scale * value) and
