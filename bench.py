@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--layer-steps", action="store_true",
                     help="time the steps either side of the decode instead (query absorption, "
                          "output projection, cache append) at the bench shape")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="the LDS read rate per CU with 1, 2, 4 and 8 waves (probe library)")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="run only the MFMA probe kernel (sustained dense bf16 MFMA rate; "
                          "the MFMA-busy counter calibration)")
@@ -209,6 +211,34 @@ def mfma_probe():
                       "implied_clock_ghz": round(clock_ghz, 3)}))
 
 
+def lds_probe():
+    """ds_read_b128 from conflict-free addresses by 1, 2, 4 and 8 waves per CU
+    (mla_latent_kv_10_amd/csrc/mla_probe.hip): the rate at which one wave,
+    and a CU, receive LDS data, in bytes per shader cycle."""
+    import ctypes
+    import torch
+    from mla_latent_kv_10_amd._build import PROBE_PATH
+    lib = ctypes.CDLL(PROBE_PATH)
+    lib.mla_probe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    lib.mla_probe_lds.restype = ctypes.c_int
+    wgs = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 2000
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for waves in (1, 2, 4, 8):
+        out = torch.zeros(wgs * waves * 4, dtype=torch.int32, device="cuda")
+        for _ in range(2):   # the second launch is the one read
+            assert lib.mla_probe_lds(ctypes.c_void_p(out.data_ptr()), wgs, waves, iters, stream) == 0
+        torch.cuda.synchronize()
+        cyc = out.view(-1, 4)[:, 0].to(torch.int64).cpu().numpy().astype(np.float64)
+        per_wave = 8 * 1024 * iters / cyc
+        res[str(waves)] = {"bytes_per_cycle_per_wave": round(float(per_wave.mean()), 2),
+                           "bytes_per_cycle_per_cu": round(float(per_wave.mean()) * waves, 1)}
+    print(json.dumps({"probe": "lds_read_b128", "workgroups": wgs, "iters": iters,
+                      "waves_per_cu": res}))
+
+
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -300,6 +330,9 @@ def main():
         return
     if args.mfma_probe:
         mfma_probe()
+        return
+    if args.lds_probe:
+        lds_probe()
         return
     if args.layer_steps:
         layer_steps(args.steps)
