@@ -2121,13 +2121,20 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     };
 
     // The first block-id window and the query rows are loaded together; once
-    // the ids have landed, the first two tiles are issued into ring stages 0
-    // and 1 while the query rows are still in flight. The query rows then
-    // pass through ring stages 2 and 3 (idle until the third tile is issued),
-    // 18 KiB per wave, to be read back in the score operand layout.
+    // The block ids come first, alone, then the first two tiles are issued
+    // into ring stages 0 and 1, and then the query rows, which pass through
+    // ring stages 2 and 3 (idle until the third tile is issued), 18 KiB per
+    // wave, to be read back in the score operand layout. (Issuing the query
+    // rows together with the ids and the tiles once the ids had landed made
+    // the ids wait behind the chip-wide burst of query loads: measured, the
+    // prologue took about 1.4K cycles longer.)
     load_ids();
     bf16x8 qf[36];
     if (n_run > 0) {
+      wait_vmcnt<0>();
+      check_ids();
+      issue(0);
+      issue(1);
       // Query rows of this wave (32 rows, one contiguous 36 KiB block): load
       // 4 C + R takes block (C, R) of the K-tile layout (rows 8R..8R+7,
       // chunks 8C..8C+7) from eight whole 128-byte lines, each lane reading
@@ -2149,10 +2156,6 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
         for (int R = 0; R < 4; ++R)
           raw[4 * C + R] = *reinterpret_cast<const u32x4*>(qblk + qoff[R] + 128 * C);
       asm volatile("" ::: "memory");
-      wait_vmcnt<36>();   // the ids have landed (loads complete in issue order)
-      check_ids();
-      issue(0);
-      issue(1);
       // three passes of at most four column groups (16 KiB) each: write the
       // blocks, read back the k-steps they hold (a wave's LDS operations
       // complete in order, so a pass's writes follow the previous reads)
