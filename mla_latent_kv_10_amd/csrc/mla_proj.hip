@@ -73,7 +73,8 @@ unsigned row_splits(int64_t n_tok, int heads) {
 // all tiles. The tile's 32 x 128 outputs are staged in LDS so that each row's
 // 256 bytes go out as whole 128-byte lines (stored from the MFMA layout, a
 // lane's 8-byte pieces of 32 rows 147 KB apart would be written piecemeal).
-// Workgroups with cb = 0 also copy the rows' q_rope.
+// Workgroups with cb = 0 also copy the rows' q_rope (32 rows x 128 bytes per
+// tile: one 16-byte piece per thread).
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ q_rope,
                                                      const uint16_t* __restrict__ w_uk_t,
@@ -103,6 +104,14 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int k = 0; k < 8; ++k) bf[k] = bn[k];
     if (t0 + tstep < n_tok) load_rows(t0 + tstep, bn);
+    // cb = 0 also copies the tile's q_rope (128 bytes per row, 8 lanes per
+    // row, one 16-byte piece per thread): read now, written after the
+    // outputs, so that the read's latency hides under the tile's work
+    const int64_t tr = t0 + (threadIdx.x >> 3);
+    const bool rope = cb == 0 && tr < n_tok;
+    u32x4 rp = {};
+    if (rope)
+      rp = *reinterpret_cast<const u32x4*>(q_rope + (tr * H + h) * kDR + 8 * (threadIdx.x & 7));
     f32x16 acc = {};
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[k], bf[k], acc, 0, 0, 0);
@@ -118,17 +127,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
             *reinterpret_cast<const u32x4*>(s_out + r * kPad + 8 * c);
     }
     __syncthreads();
-    if (cb == 0) {
-      // q_rope of the tile's rows: 128 bytes per row, 8 lanes per row
-      for (int u = threadIdx.x; u < 32 * 8; u += 256) {
-        const int64_t tr = t0 + (u >> 3);
-        if (tr < n_tok) {
-          const int64_t row = tr * H + h;
-          *reinterpret_cast<u32x4*>(q_abs + row * kDK + kDL + 8 * (u & 7)) =
-              *reinterpret_cast<const u32x4*>(q_rope + row * kDR + 8 * (u & 7));
-        }
-      }
-    }
+    if (rope) *reinterpret_cast<u32x4*>(q_abs + (tr * H + h) * kDK + kDL + 8 * (threadIdx.x & 7)) = rp;
   }
 }
 
