@@ -117,6 +117,24 @@ def test_full_size_config_all_rows(cfg):
     compare(out, lse, *ref, what=w.name, kv_dtype=w.kv_dtype, flat=cfg != 4)
 
 
+@pytest.mark.parametrize("H,kvd,hi_len", [(16, "bf16", 200), (128, "bf16", 64),
+                                           (128, "q8_0", 64)])
+def test_maximum_batch_all_rows(H, kvd, hi_len):
+    """The largest batch the library takes (MLA_MAX_BATCH sequences, eight per
+    thread in every kernel's plan prologue), ragged lengths including empty
+    sequences, on every row: automatic plan and a forced part count. Rows of
+    sequences with one or a few tokens have A_e as large as |V| (up to about
+    4.6 here), so only the derived bar applies, not the flat 2e-2."""
+    B = mla.MAX_BATCH
+    w = wl.make_workload(f"maxb_h{H}_{kvd}", B, 1, H, ("uniform", 0, hi_len), seed=91,
+                         table="permuted", kv_dtype=kvd)
+    log(f"max batch B={B} H={H} {kvd}: {int(w.seqlens.sum())} tokens")
+    ref = oracle_rows(w)
+    for parts in (0, 300):
+        out, lse, _ = run_gpu(w, num_parts=parts)
+        compare(out, lse, *ref, what=f"maxb h{H} {kvd} P={parts}", kv_dtype=kvd)
+
+
 @pytest.mark.parametrize("kvd", ["bf16", "fp8", "q4_0h"])
 def test_forced_part_counts_agree(kvd):
     w = wl.make_workload("parts", 4, 1, 128, [2000, 1, 4096, 777], seed=5, table="permuted",
