@@ -135,6 +135,21 @@ def test_maximum_batch_all_rows(H, kvd, hi_len):
         compare(out, lse, *ref, what=f"maxb h{H} {kvd} P={parts}", kv_dtype=kvd)
 
 
+@pytest.mark.parametrize("kvd", ["bf16", "q8_0", "fp8"])
+def test_maximum_rows_all_rows(kvd):
+    """The most query rows a sequence may have (MLA_MAX_ROWS = 32 new tokens x
+    128 heads: 32 row tiles per part), causal visibility across the tiles,
+    on every row."""
+    w = wl.make_workload(f"maxr_{kvd}", 2, 32, 128, [100, 700], seed=93, table="permuted",
+                         kv_dtype=kvd)
+    assert w.s_q * w.H == mla.MAX_ROWS
+    log(f"max rows {kvd}: {w.rows} rows")
+    ref = oracle_rows(w)
+    for parts in (0, 5):
+        out, lse, _ = run_gpu(w, num_parts=parts)
+        compare(out, lse, *ref, what=f"maxr {kvd} P={parts}", kv_dtype=kvd)
+
+
 @pytest.mark.parametrize("kvd", ["bf16", "fp8", "q4_0h"])
 def test_forced_part_counts_agree(kvd):
     w = wl.make_workload("parts", 4, 1, 128, [2000, 1, 4096, 777], seed=5, table="permuted",
