@@ -78,6 +78,8 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((__vector_size__(8 * sizeof(uint32_t))));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // Eight OCP E4M3 codes (byte i = element i) to bf16, exactly: every finite
 // E4M3 value, subnormals included, is a bf16 value.
@@ -1854,6 +1856,67 @@ __device__ __forceinline__ void mfma_score_valu_a(f32x16& acc, const bf16x8& a, 
   else
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b), "v"(other));
 }
+// The same chain on the fp8 matrix core: 32 tokens x 32 rows x 64 columns of
+// E4M3 operands per instruction, 8 VGPRs (32 codes) of A and of B per lane.
+// A lane's 32 codes are consecutive columns of one token (A) or one query
+// row (B), taken by both operands in the same byte order, so the
+// contraction is over the same 64 columns whatever order the matrix core
+// sums them in. The E4M3 pairs are the default operand type (cbsz = blgp = 0).
+__device__ __forceinline__ void mfma_score8(f32x16& acc, const u32x8& a, const u32x8& b, bool first) {
+  if (first)
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// XDL write (16 passes) -> VALU read of the same VGPRs
+__device__ __forceinline__ void mfma8_vgpr_drain(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+// Query row value x (bf16, already in the score operand layout) as two E4M3
+// codes with x * 2^e = hi + lo: hi = E4M3(x 2^e) rounded to nearest even and
+// lo = E4M3(x 2^e - hi). x 2^e has at most 8 significant bits and hi takes the
+// top 4 (rounded), so the remainder has at most 4 and is exact in E4M3 as
+// long as it is a multiple of 2^-9 (|x 2^e| >= 1/4); with 2^e chosen per row
+// so that the row's largest |x 2^e| lies in [128, 256), only values below
+// 2^-9 of the row maximum lose bits of their lo part. Four bf16 (two words)
+// in, one word of hi codes and one of lo codes out, byte i = value i.
+// sd = 2^-e: the scaled conversions divide by their scale on the way to
+// E4M3 and multiply by it on the way back, so hi comes straight from the
+// bf16 pair and returns as hi 2^-e; h - x is one dot2 (x times -1 plus h,
+// exact), converted with the same scale and its E4M3 sign bits flipped.
+__device__ __forceinline__ void bf16x4_to_fp8_hilo(uint32_t w0, uint32_t w1, float sd, const DotSel& sel,
+                                                    uint32_t& h, uint32_t& l) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef short v2i16 __attribute__((ext_vector_type(2)));
+  // hi through the builtins: their inputs come from lane swaps, whose
+  // hazards the compiler resolves only for instructions it can see
+  v2i16 hh = {0, 0};
+  hh = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hh, __builtin_bit_cast(bf16x2v, w0), sd, false);
+  hh = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hh, __builtin_bit_cast(bf16x2v, w1), sd, true);
+  h = __builtin_bit_cast(uint32_t, hh);
+  const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sd, false);   // hi 2^-e, values 0, 1
+  const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(h, sd, true);    // values 2, 3
+  const bf16x2v x0 = __builtin_bit_cast(bf16x2v, w0), x1 = __builtin_bit_cast(bf16x2v, w1);
+  const bf16x2v slo = __builtin_bit_cast(bf16x2v, sel.lo), shi = __builtin_bit_cast(bf16x2v, sel.hi);
+  const float r0 = __builtin_amdgcn_fdot2_f32_bf16(x0, slo, b0[0], false);
+  const float r1 = __builtin_amdgcn_fdot2_f32_bf16(x0, shi, b0[1], false);
+  const float r2 = __builtin_amdgcn_fdot2_f32_bf16(x1, slo, b1[0], false);
+  const float r3 = __builtin_amdgcn_fdot2_f32_bf16(x1, shi, b1[1], false);
+  // lo in one asm block: its two halves are written by the two conversions,
+  // so no prior contents are copied in. A scaled conversion needs a wait
+  // state after the VALU write of a register it reads (the dot2 results, and
+  // the second half-write reads the first's register), and its result one
+  // before the next instruction reads it: the compiler cannot see into asm,
+  // so the s_nops are written out
+  uint32_t ll;
+  asm("s_nop 1\n\t"
+      "v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %5\n\t"
+      "s_nop 0\n\t"
+      "v_cvt_scalef32_pk_fp8_f32 %0, %3, %4, %5 op_sel:[0,0,0,1]\n\t"
+      "s_nop 0"
+      : "=&v"(ll) : "v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(sd));
+  l = ll ^ 0x80808080u;
+}
 // max of three floats in one v_max3_f32; the asm also pins the result where
 // it stands (no sinking into later conditional code).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -1891,19 +1954,21 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
   constexpr int MT = 128;
   constexpr int NST = 4;                  // ring stages
   constexpr int LPW = 36 / NW;            // 1 KiB LDS-DMA loads per wave per tile (bf16)
-  // score operands in flight (fp8: each is converted one step before its
-  // MFMA, so one more is read ahead)
-  constexpr int KPF = FP8 ? 4 : 3;
+  // score operands in flight (fp8: two 16-byte reads each)
+  constexpr int KPF = FP8 ? 2 : 3;
+  constexpr int KLG = FP8 ? 2 * KPF : KPF;   // LDS reads of those operands
   // fp8: the E4M3 tiles (18 KiB of codes + 128 B of scales) stream into
-  // 19 KiB stages and are read as MFMA operands directly, converted to bf16
-  // in registers (exact: every E4M3 value is a bf16 value), which halves the
-  // LDS traffic of both products
+  // 19 KiB stages and are read as MFMA operands directly: the scores on the
+  // fp8 matrix core against the query split into two E4M3 parts (hi + lo, one
+  // power-of-two scale per row), the value product converted to bf16 in
+  // registers (exact: every E4M3 value is a bf16 value); this halves the LDS
+  // traffic of both products
   constexpr int STB = FP8 ? kFp8StageBytes : kTileBytes;   // bytes per ring stage
   // 4 x 36 KiB: the bf16 stages; the query rows pass through the upper half
   // (18 KiB a wave) before the third tile is issued, for both cache types
   constexpr int RING = 4 * kTileBytes;
   static_assert(NST * STB <= RING, "ring stages");
-  using KOp = std::conditional_t<FP8, u32x2, bf16x8>;       // score operand as read
+  using KOp = std::conditional_t<FP8, u32x8, bf16x8>;       // score operand as read
   // LDS-DMA copy of one block (NT: non-temporal, when no other workgroup
   // reads the same tiles)
   auto copy = [](const void* src, uint32_t off, uint32_t dst) {
@@ -1985,8 +2050,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     // the bank window. LDS-DMA copy m fills chunks 2m, 2m+1: lane l takes
     // chunk 2m + (l >> 5) of token (l & 31) ^ 4 (l >> 5).
     const uint32_t doff8 = (uint32_t)(kDK * ((lane & 31) ^ (4 * hi)) + 16 * hi);
-    const int kofs8_0 = 16 * l32 + 8 * hi;
-    const int kofs8_1 = 16 * (l32 ^ 4) + 8 * hi;
+    // fp8 score operand of k-step k (columns 64 k + 32 hi .. + 31 of token
+    // l32): chunks 4 k + 2 hi (slot l32) and 4 k + 2 hi + 1 (slot l32 ^ 4),
+    // byte 2048 k + kofs8_{0,1}
+    const int kofs8_0 = 1024 * hi + 16 * l32;
+    const int kofs8_1 = 1024 * hi + 512 + 16 * (l32 ^ 4);
     // value read: group g16 covers columns 16 (g16 & 1) + 0..15 of the column
     // block (chunk 8 w + 2 cb + (g16 & 1)); lane i16 = 2 s + h points at
     // codes 8h..8h+7 of the chunk for token 4 vh + (s & 3) + 8 (s >> 2) and
@@ -2130,6 +2198,11 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     // prologue took about 1.4K cycles longer.)
     load_ids();
     bf16x8 qf[36];
+    // fp8: the query rows as E4M3 hi and lo parts (score k-step k: columns
+    // 64 k + 32 hi .. + 31 of row l32) and this row's score factor, the
+    // softmax scale times 2^-e of the row's power-of-two scale
+    u32x8 q8h[FP8 ? 9 : 1], q8l[FP8 ? 9 : 1];
+    float c_row = a.scale_mag_log2;
     if (n_run > 0) {
       wait_vmcnt<0>();
       check_ids();
@@ -2176,6 +2249,57 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
           qf[s2] = __builtin_bit_cast(bf16x8, (z ^ sg) & keep);
         }
       }
+      if constexpr (FP8) {
+        // row maximum of |x| (bf16 bits, NaN above every number) over the
+        // lane's half of the row and its partner lane's
+        u16x2 mx = {0, 0};
+#pragma unroll
+        for (int k = 0; k < 36; ++k) {
+          const u32x4 w = __builtin_bit_cast(u32x4, qf[k]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
+        }
+        int m16 = max((int)mx[0], (int)mx[1]);
+        m16 = max(m16, __shfl_xor(m16, 32, 64));
+        // largest |x| 2^e in [128, 256); e clamped so that 2^e and 2^-e stay
+        // normal fp32 (a row whose maximum is below 2^-93 or above 2^107 keeps
+        // fewer exact bits in its small values)
+        const int e = min(100, max(-100, 134 - ((m16 >> 7) & 0xff)));
+        const float sd = __builtin_amdgcn_ldexpf(1.f, -e);
+        c_row = a.scale_mag_log2 * sd;
+        const DotSel sel;
+        // lane (row, hi) holds chunks 2 k + hi of the row (8 columns each);
+        // k-step k8 needs chunks 8 k8 + 4 hi + 0..3: swap halves with the
+        // partner lane (the same row) before splitting
+#pragma unroll
+        for (int k8 = 0; k8 < 9; ++k8) {
+          const u32x4 a0 = __builtin_bit_cast(u32x4, qf[4 * k8]);      // chunk 8k8 + hi
+          const u32x4 a1 = __builtin_bit_cast(u32x4, qf[4 * k8 + 1]);  // 8k8 + 2 + hi
+          const u32x4 b0 = __builtin_bit_cast(u32x4, qf[4 * k8 + 2]);  // 8k8 + 4 + hi
+          const u32x4 b1 = __builtin_bit_cast(u32x4, qf[4 * k8 + 3]);  // 8k8 + 6 + hi
+          u32x4 c[4];   // chunks 4 hi + 0..3
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const auto s0 = __builtin_amdgcn_permlane32_swap(a0[i], b0[i], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(a1[i], b1[i], false, false);
+            c[0][i] = s0[0];
+            c[1][i] = s0[1];
+            c[2][i] = s1[0];
+            c[3][i] = s1[1];
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint32_t h0, l0, h1, l1;
+            bf16x4_to_fp8_hilo(c[j][0], c[j][1], sd, sel, h0, l0);
+            bf16x4_to_fp8_hilo(c[j][2], c[j][3], sd, sel, h1, l1);
+            q8h[k8][2 * j] = h0;
+            q8h[k8][2 * j + 1] = h1;
+            q8l[k8][2 * j] = l0;
+            q8l[k8][2 * j + 1] = l1;
+          }
+        }
+      }
       lds_barrier();   // every wave holds its query rows; stages 2 and 3 are free
       // "tile -1" (value product before the first tile) reads the last
       // stage with P = 0: both are zero-filled so that it adds exact zeros
@@ -2189,6 +2313,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       check_ids();
 #pragma unroll
       for (int s = 0; s < 36; ++s) qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      if constexpr (FP8) {
+#pragma unroll
+        for (int k8 = 0; k8 < 9; ++k8) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q8h[k8][i] = q8l[k8][i] = 0u;
+        }
+      }
     }
 
     // Iteration it: scores and softmax of tile it (it < n_run), value product
@@ -2197,10 +2328,15 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
     // it-1, before the barrier that publishes P(it-1), so that their LDS
     // latency is not exposed at the start of the score chain.
     KOp kf[KPF];
+    auto rd_fp8 = [&](const LDS_AS uint8_t* st, int k) {
+      const u32x4 c0 = __builtin_bit_cast(u32x4, lds_read_b128(st + 2048 * k + kofs8_0));
+      const u32x4 c1 = __builtin_bit_cast(u32x4, lds_read_b128(st + 2048 * k + kofs8_1));
+      return u32x8{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    };
     auto rd_at = [&](int t, int k) {
       const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage(t % NST);
       if constexpr (FP8)
-        return *reinterpret_cast<const LDS_AS u32x2*>(st + 512 * k + ((k & 1) ? kofs8_1 : kofs8_0));
+        return rd_fp8(st, k);
       else
         return lds_read_b128(st + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0));
     };
@@ -2221,7 +2357,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       // P(it-1), alpha and flags of every wave are visible: their writes were
       // issued before the KPF score reads now in flight, and LDS operations
       // of a wave complete in order
-      if (it > 0) asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KPF) : "memory");
+      if (it > 0) asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(KLG) : "memory");
       const bool has_s = it < n_run;
       const LDS_AS uint8_t* st = (const LDS_AS uint8_t*)s_stage(it % NST);
       const LDS_AS uint8_t* sp = (const LDS_AS uint8_t*)s_stage((it + NST - 1) % NST);
@@ -2244,7 +2380,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       f32x16 s;
       auto rd = [&](int k) -> KOp {
         if constexpr (FP8)
-          return *reinterpret_cast<const LDS_AS u32x2*>(st + 512 * k + ((k & 1) ? kofs8_1 : kofs8_0));
+          return rd_fp8(st, k);
         else
           return lds_read_b128(st + kstep_ofs(k) + ((k & 1) ? kofs1 : kofs0));
       };
@@ -2290,36 +2426,37 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       // ---- phase A: the dependent score chain of tile it (36 MFMAs) and the
       // copy of tile it+2; in its last third the first value operands of
       // tile it-1 are read
-      // fp8: converted score operands, alternating: step k reads kb[k & 1]
-      // while the operand of step k+1 is converted into kb[(k + 1) & 1]
-      bf16x8 kb[2];
       if constexpr (FP8) {
-        kb[0] = fp8x8_to_bf16(kf[0]);
-        kb[1] = kb[0];
-      }
-      unroll<36>([&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        if constexpr (FP8) {
-          mfma_score_valu_a(s, kb[k & 1], qf[k], k == 0, kb[(k + 1) & 1]);
-          if constexpr (k + 1 < 36) kb[(k + 1) & 1] = fp8x8_to_bf16(kf[(k + 1) % KPF]);
-        } else {
+        // 9 k-steps of 64 columns, each operand read once and multiplied by
+        // the hi and then the lo part of the query (one chain of 18 MFMAs)
+        unroll<18>([&](auto jc) {
+          constexpr int j = decltype(jc)::value, k = j >> 1;
+          if constexpr (j & 1)
+            mfma_score8(s, kf[k % KPF], q8l[k], false);
+          else
+            mfma_score8(s, kf[k % KPF], q8h[k], j == 0);
+          if constexpr ((j & 1) && k + KPF < 9) kf[k % KPF] = rd(k + KPF);
+          if constexpr (j >= 12 && j < 16) pf[j - 12] = __builtin_bit_cast(bf16x8, s_p[j - 12][0][lane]);
+          if constexpr (j == 14) va[0] = vread(0, 0);
+          if constexpr (j == 15) va[1] = vread(0, 1);
+          if constexpr (j == 17) vb = fp8x8_to_bf16(va[0]);
+          if constexpr ((j & 3) == 0) copy8(nsrc, nssrc, ndst, j >> 2);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        mfma8_vgpr_drain(s);
+      } else {
+        unroll<36>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
           mfma_score(s, kf[k % KPF], qf[k], k == 0);
-        }
-        if constexpr (k + KPF < 36) kf[k % KPF] = rd(k + KPF);
-        if constexpr (k >= 24 && k < 28) pf[k - 24] = __builtin_bit_cast(bf16x8, s_p[k - 24][0][lane]);
-        if constexpr (k == 29) va[0] = vread(0, 0);
-        if constexpr (k == 31) va[1] = vread(0, 1);
-        if constexpr (FP8) {
-          if constexpr (k == 34) vb = fp8x8_to_bf16(va[0]);
-        }
-        if constexpr (FP8) {
-          if constexpr ((k & 7) == 1) copy8(nsrc, nssrc, ndst, k >> 3);
-        } else {
+          if constexpr (k + KPF < 36) kf[k % KPF] = rd(k + KPF);
+          if constexpr (k >= 24 && k < 28) pf[k - 24] = __builtin_bit_cast(bf16x8, s_p[k - 24][0][lane]);
+          if constexpr (k == 29) va[0] = vread(0, 0);
+          if constexpr (k == 31) va[1] = vread(0, 1);
           if constexpr ((k & 3) == 1) copy(nsrc + 128 * (k >> 2), ndoff, ndst + 4096 * (k >> 2));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      mfma_vgpr_drain(s);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        mfma_vgpr_drain(s);
+      }
 
       // a row's reference maximum moved at tile it-1: rescale its
       // accumulators (which then hold tiles up to it-2) in every wave before
@@ -2346,7 +2483,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       // the commit below. The row maximum pairs the two lane halves with a
       // lane swap; the reference maximum moves only when it is exceeded by
       // more than the threshold.
-      const float c = a.scale_mag_log2;
+      const float c = FP8 ? c_row : a.scale_mag_log2;
       float x[16];
       f32x4 tsc4[4];   // fp8: per-token scales of the lane's tokens 8 g + 4 hi + (0..3)
       const LDS_AS float* tscp = reinterpret_cast<const LDS_AS float*>(st + kFp8TileBytes) + 4 * hi;
