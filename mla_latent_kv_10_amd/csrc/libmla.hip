@@ -1943,7 +1943,12 @@ __device__ __forceinline__ void mfma_vgpr_drain(f32x16& acc) {
 // copies of tile i+2 and the first V reads of tile i-1 in its shadow), then
 // the value product of tile i-1 with the online softmax of tile i cut into
 // short VALU steps between its MFMAs (phase B). A 4-stage ring keeps tile
-// i-1 resident while tile i is scored and tiles i+1, i+2 stream in. The reference maximum of the online softmax moves rarely;
+// i-1 resident while tile i is scored and tiles i+1, i+2 stream in. Over an
+// fp8 (E4M3) cache the scores run on the fp8 matrix core against the query
+// split once per sequence into two E4M3 parts (hi + lo under a power-of-two
+// row scale, exact down to 2^-10 of the row maximum), the values on bf16
+// MFMAs over codes converted exactly. The reference maximum of the online
+// softmax moves rarely;
 // when a row's does, its owner publishes the factor and every wave rescales
 // that row's accumulators. The plan prefix and the epilogue's scratch live in
 // ring space that is idle at those times, which keeps LDS under 160 KiB.
@@ -2423,9 +2428,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_pipe_kernel(DecodeParams a)
       const int limx = masked ? n_vis - t0 - 4 * hi : kTile;
       __builtin_amdgcn_sched_barrier(0);
 
-      // ---- phase A: the dependent score chain of tile it (36 MFMAs) and the
-      // copy of tile it+2; in its last third the first value operands of
-      // tile it-1 are read
+      // ---- phase A: the dependent score chain of tile it (36 bf16 MFMAs;
+      // fp8: 18 fp8 MFMAs against the query's hi and lo parts) and the copy
+      // of tile it+2; in its last third the first value operands of tile it-1
+      // are read
       if constexpr (FP8) {
         // 9 k-steps of 64 columns, each operand read once and multiplied by
         // the hi and then the lo part of the query (one chain of 18 MFMAs)
